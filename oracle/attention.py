@@ -1,0 +1,278 @@
+"""Plain fp64 CPU definition of the attention forward and backward pass.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).  Everything is computed
+in float64 with torch CPU ops; S, P and dS are materialised explicitly.
+
+What is computed, and where the pages define it:
+
+* Forward, per sequence b and head n (FlashAttentionVarLenScore API doc,
+  "计算公式"; aclnnFlashAttentionUnpaddingScoreGradV2 explainer, section 2.2),
+  with no pse, no dropout (keep_prob = 1) and no explicit mask tensor:
+      S = scale * Q K^T, masked entries set to -inf
+      P = softmax(S) row-wise,   out = P V
+* Saved statistics (PyPTO-Gym FlashAttentionScoreGrad article, "前向公式" and
+  "反向公式"): softmax_max = row max of the scaled, masked scores;
+  softmax_sum = sum_j exp(S_ij - softmax_max_i), so that
+  P = exp(S - softmax_max) / softmax_sum.
+* Backward (PyPTO-Gym FlashAttentionScoreGrad article, "反向公式";
+  UnpaddingScoreGradV2 explainer, section 2.3):
+      P  = exp(scale Q K^T - softmax_max) / softmax_sum   (caller's statistics)
+      Dv = rowsum(dY * O)                                  (caller's O)
+      dP = dY V^T,  dS = P * (dP - Dv)
+      dV = P^T dY,  dQ = scale dS K,  dK = scale dS^T Q
+* Masks (op-plugin sliding-window blog, section 1.3 "SparseMode说明"; API doc,
+  preTokensOptional / nextTokensOptional): sparse_mode 0 = no mask;
+  sparse_mode 4 (BAND) keeps key j for query i iff
+  -pre_tokens <= j - i <= next_tokens, with sequence-local indices.
+* Varlen TND packing (API doc, "算子功能" and inputLayout; explainer 4.2, 6.4):
+  tokens of each batch are packed back to back; cumulative ends are inclusive,
+  one per batch; trailing zeros mark batches that do not participate.
+
+Readings where the pages are silent: empty rows (every key masked) give
+out = 0, softmax_max = -inf, softmax_sum = 0 and dq = 0; keys no query attends
+get dk = dv = 0; tokens after the last participating end get zeros; mode 0
+ignores pre/next.
+
+Row chunking (``chunk``) evaluates the same definition a block of rows at a
+time over the columns the band can reach in that block; the dropped columns are
+masked for every row of the block and contribute exactly zero.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+INT_MAX = 2147483647
+F64 = torch.float64
+
+
+def sequences(cu_seqlens):
+    """Return [(start, length)] for each participating batch.
+
+    ``cu_seqlens`` holds inclusive cumulative ends, one per batch.  A zero that
+    follows a positive entry starts the trailing run of non-participating
+    batches (explainer section 6.4: ``[2, 5, 9, 0, 0]``).
+    """
+    out = []
+    prev = 0
+    for c in cu_seqlens:
+        c = int(c)
+        if c == 0 and prev > 0:
+            break
+        if c < prev:
+            raise ValueError("cumulative sequence ends must be non-decreasing")
+        out.append((prev, c - prev))
+        prev = c
+    return out
+
+
+def allowed_mask(rows, cols, sparse_mode, pre_tokens, next_tokens):
+    """Boolean [len(rows), len(cols)]: True where query i may attend key j."""
+    i = torch.as_tensor(rows, dtype=torch.int64)[:, None]
+    j = torch.as_tensor(cols, dtype=torch.int64)[None, :]
+    if sparse_mode == 0:
+        return torch.ones(i.shape[0], j.shape[1], dtype=torch.bool)
+    if sparse_mode == 4:
+        d = j - i
+        return (d >= -int(pre_tokens)) & (d <= int(next_tokens))
+    raise ValueError(f"The sparse_mode value should be 0 or 4, but got {sparse_mode}")
+
+
+def _col_window(r0, r1, skv, sparse_mode, pre, nxt, chunked):
+    """Columns that rows [r0, r1) can reach; all columns unless chunked."""
+    if sparse_mode == 0 or not chunked:
+        return 0, skv
+    lo = max(0, r0 - int(pre))
+    hi = min(skv, r1 - 1 + int(nxt) + 1)
+    return lo, max(lo, hi)
+
+
+def _scores(Q, K, rows, c0, c1, scale, sparse_mode, pre, nxt):
+    """Scaled, masked scores for rows x columns [c0, c1) (masked = -inf)."""
+    S = scale * (Q[rows] @ K[c0:c1].T)
+    M = allowed_mask(torch.as_tensor(rows), torch.arange(c0, c1), sparse_mode, pre, nxt)
+    return S.masked_fill(~M, -math.inf), M
+
+
+def _softmax_stats(S):
+    """Row max, exp(S - max) and row sum; empty rows give -inf, 0, 0."""
+    m = S.max(dim=1).values if S.shape[1] else torch.full((S.shape[0],), -math.inf, dtype=F64)
+    finite = torch.isfinite(m)
+    E = torch.where(finite[:, None], torch.exp(S - torch.where(finite, m, 0.0)[:, None]),
+                    torch.zeros((), dtype=F64))
+    E = torch.nan_to_num(E, nan=0.0)
+    l = E.sum(dim=1)
+    return m, E, l
+
+
+def _seq_head_forward(Q, K, V, scale, sparse_mode, pre, nxt, rows, chunked):
+    r0, r1 = int(rows[0]), int(rows[-1]) + 1
+    c0, c1 = _col_window(r0, r1, K.shape[0], sparse_mode, pre, nxt, chunked)
+    S, _ = _scores(Q, K, rows, c0, c1, scale, sparse_mode, pre, nxt)
+    m, E, l = _softmax_stats(S)
+    P = torch.where(l[:, None] > 0, E / torch.where(l > 0, l, 1.0)[:, None],
+                    torch.zeros((), dtype=F64))
+    O = P @ V[c0:c1]
+    return O, m, l
+
+
+def _row_chunks(n, chunk):
+    if n == 0:
+        return []
+    if not chunk:
+        return [torch.arange(0, n)]
+    return [torch.arange(r, min(n, r + chunk)) for r in range(0, n, chunk)]
+
+
+def _as64(x):
+    return x.detach().to("cpu").to(F64)
+
+
+def forward(q, k, v, cu_seqlens_q, cu_seqlens_kv, scale, pre_tokens=INT_MAX,
+            next_tokens=INT_MAX, sparse_mode=0, chunk=None, heads=None):
+    """Attention forward over a TND batch.
+
+    Returns (out [Tq, N, D], softmax_max [Tq, N], softmax_sum [Tq, N]) in fp64.
+    ``chunk`` (rows per block) only changes evaluation order, not the result.
+    """
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    Tq, N, D = q.shape
+    out = torch.zeros(Tq, N, v.shape[2], dtype=F64)
+    smax = torch.full((Tq, N), -math.inf, dtype=F64)
+    ssum = torch.zeros((Tq, N), dtype=F64)
+    sq_list, skv_list = sequences(cu_seqlens_q), sequences(cu_seqlens_kv)
+    if len(sq_list) != len(skv_list):
+        raise ValueError("query and key/value batches disagree")
+    for (q0, sq), (k0, skv) in zip(sq_list, skv_list):
+        for n in (range(N) if heads is None else heads):
+            Q, K, V = q[q0:q0 + sq, n], k[k0:k0 + skv, n], v[k0:k0 + skv, n]
+            for rows in _row_chunks(sq, chunk):
+                O, m, l = _seq_head_forward(Q, K, V, scale, sparse_mode, pre_tokens,
+                                            next_tokens, rows, chunk is not None)
+                out[q0 + rows, n] = O
+                smax[q0 + rows, n] = m
+                ssum[q0 + rows, n] = l
+    return out, smax, ssum
+
+
+def _recompute_p(Q, K, rows, c0, c1, scale, sparse_mode, pre, nxt, m_rows, l_rows):
+    """P = exp(S - softmax_max) / softmax_sum from the given statistics."""
+    S, M = _scores(Q, K, rows, c0, c1, scale, sparse_mode, pre, nxt)
+    ok = (l_rows > 0) & torch.isfinite(m_rows)
+    mm = torch.where(ok, m_rows, 0.0)
+    ll = torch.where(ok, l_rows, 1.0)
+    P = torch.exp(S - mm[:, None]) / ll[:, None]
+    P = torch.where(M & ok[:, None], P, torch.zeros((), dtype=F64))
+    return P
+
+
+def backward(q, k, v, dy, out, softmax_max, softmax_sum, cu_seqlens_q, cu_seqlens_kv, scale,
+             pre_tokens=INT_MAX, next_tokens=INT_MAX, sparse_mode=0, chunk=None, heads=None):
+    """Attention backward; uses the caller's out and statistics verbatim.
+
+    ``softmax_max``/``softmax_sum`` may be [T, N] or [T, N, 8] (column 0 is
+    read, as the stored statistics keep the value in column 0).
+    Returns (dq, dk, dv) in fp64.
+    """
+    q, k, v, dy, out = _as64(q), _as64(k), _as64(v), _as64(dy), _as64(out)
+    sm, ss = _as64(softmax_max), _as64(softmax_sum)
+    if sm.dim() == 3:
+        sm, ss = sm[..., 0], ss[..., 0]
+    Tq, N, D = q.shape
+    dq = torch.zeros_like(q)
+    dk = torch.zeros_like(k)
+    dv = torch.zeros(v.shape, dtype=F64)
+    for (q0, sq), (k0, skv) in zip(sequences(cu_seqlens_q), sequences(cu_seqlens_kv)):
+        for n in (range(N) if heads is None else heads):
+            Q, K, V = q[q0:q0 + sq, n], k[k0:k0 + skv, n], v[k0:k0 + skv, n]
+            dY, O = dy[q0:q0 + sq, n], out[q0:q0 + sq, n]
+            for rows in _row_chunks(sq, chunk):
+                c0, c1 = _col_window(int(rows[0]), int(rows[-1]) + 1, skv, sparse_mode,
+                                     pre_tokens, next_tokens, chunk is not None)
+                P = _recompute_p(Q, K, rows, c0, c1, scale, sparse_mode, pre_tokens,
+                                 next_tokens, sm[q0 + rows, n], ss[q0 + rows, n])
+                Dv = (dY[rows] * O[rows]).sum(dim=1)
+                dP = dY[rows] @ V[c0:c1].T
+                dS = P * (dP - Dv[:, None])
+                dv[k0 + c0:k0 + c1, n] += P.T @ dY[rows]
+                dq[q0 + rows, n] = scale * (dS @ K[c0:c1])
+                dk[k0 + c0:k0 + c1, n] += scale * (dS.T @ Q[rows])
+    return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# Restrictions of the same definition to a few rows or keys of one
+# (sequence, head).  They let tests check sampled outputs of problems too large
+# to evaluate in full.  Inputs are the sequence-local [S, D] slices.
+# ---------------------------------------------------------------------------
+
+def forward_rows(Q, K, V, rows, scale, sparse_mode=0, pre_tokens=INT_MAX,
+                 next_tokens=INT_MAX, chunk=128):
+    """out, softmax_max, softmax_sum of the given query rows (fp64).
+
+    Rows are evaluated in groups of consecutive indices, ``chunk`` at a time.
+    """
+    Q, K, V = _as64(Q), _as64(K), _as64(V)
+    rows = torch.as_tensor(rows, dtype=torch.int64).reshape(-1)
+    O = torch.zeros(len(rows), V.shape[1], dtype=F64)
+    m = torch.full((len(rows),), -math.inf, dtype=F64)
+    l = torch.zeros(len(rows), dtype=F64)
+    start = 0
+    while start < len(rows):
+        end = start + 1
+        while (end < len(rows) and end - start < chunk
+               and int(rows[end]) == int(rows[end - 1]) + 1):
+            end += 1
+        o, mm, ll = _seq_head_forward(Q, K, V, scale, sparse_mode, pre_tokens, next_tokens,
+                                      rows[start:end], True)
+        O[start:end], m[start:end], l[start:end] = o, mm, ll
+        start = end
+    return O, m, l
+
+
+def backward_rows(Q, K, V, dY, rows, scale, sparse_mode=0, pre_tokens=INT_MAX,
+                  next_tokens=INT_MAX):
+    """dq of the given query rows, end to end (statistics and O from forward_rows)."""
+    Q, K, V, dY = _as64(Q), _as64(K), _as64(V), _as64(dY)
+    rows = torch.as_tensor(rows, dtype=torch.int64)
+    O, m, l = forward_rows(Q, K, V, rows, scale, sparse_mode, pre_tokens, next_tokens)
+    dq = torch.zeros(len(rows), Q.shape[1], dtype=F64)
+    for idx, r in enumerate(rows.tolist()):
+        c0, c1 = _col_window(r, r + 1, K.shape[0], sparse_mode, pre_tokens, next_tokens, True)
+        rr = torch.tensor([r])
+        P = _recompute_p(Q, K, rr, c0, c1, scale, sparse_mode, pre_tokens, next_tokens,
+                         m[idx:idx + 1], l[idx:idx + 1])
+        Dv = (dY[rr] * O[idx:idx + 1]).sum(dim=1)
+        dS = P * (dY[rr] @ V[c0:c1].T - Dv[:, None])
+        dq[idx] = scale * (dS @ K[c0:c1])[0]
+    return dq
+
+
+def backward_keys(Q, K, V, dY, key_lo, key_hi, scale, sparse_mode=0, pre_tokens=INT_MAX,
+                  next_tokens=INT_MAX):
+    """dk, dv of keys [key_lo, key_hi), end to end.
+
+    Every query row that can attend one of these keys is evaluated in full
+    (its statistics and O come from forward_rows over its whole band).
+    """
+    Q, K, V, dY = _as64(Q), _as64(K), _as64(V), _as64(dY)
+    sq = Q.shape[0]
+    if sparse_mode == 4:
+        r0 = max(0, key_lo - int(next_tokens))
+        r1 = min(sq, key_hi - 1 + int(pre_tokens) + 1)
+    else:
+        r0, r1 = 0, sq
+    dk = torch.zeros(key_hi - key_lo, K.shape[1], dtype=F64)
+    dv = torch.zeros(key_hi - key_lo, V.shape[1], dtype=F64)
+    if r1 <= r0:
+        return dk, dv
+    rows = torch.arange(r0, r1)
+    O, m, l = forward_rows(Q, K, V, rows, scale, sparse_mode, pre_tokens, next_tokens)
+    P = _recompute_p(Q, K, rows, key_lo, key_hi, scale, sparse_mode, pre_tokens, next_tokens,
+                     m, l)
+    Dv = (dY[rows] * O).sum(dim=1)
+    dS = P * (dY[rows] @ V[key_lo:key_hi].T - Dv[:, None])
+    dv = P.T @ dY[rows]
+    dk = scale * (dS.T @ Q[rows])
+    return dk, dv
