@@ -1,0 +1,157 @@
+/*
+ * swa.h - C ABI of the MI355X (gfx950) sliding-window FlashAttention library.
+ *
+ * Operation (forward): for every participating batch b and head n of a TND
+ * packed batch,
+ *     out = softmax(mask(scale * Q K^T)) V
+ * with the saved row statistics softmax_max (row max of the scaled, masked
+ * scores) and softmax_sum (sum of exp(score - softmax_max)).
+ *   - formula: FlashAttentionVarLenScore API doc, "计算公式" (no pse, no
+ *     dropout, keep_prob = 1, no explicit atten_mask tensor);
+ *   - statistics: PyPTO-Gym FlashAttentionScoreGrad article, "前向公式" and
+ *     "反向公式" (P = exp(QK^T*scale - softmax_max) / softmax_sum);
+ *   - TND packing with cumulative per-batch ends: API doc, "算子功能" and
+ *     parameters actualSeqQLenOptional / actualSeqKvLenOptional;
+ *   - masks: op-plugin sliding-window blog, section 1.3 "SparseMode说明":
+ *     sparse_mode 0 = no mask; sparse_mode 4 (BAND) keeps key j for query i
+ *     iff -pre_tokens <= j - i <= next_tokens (sequence-local indices).
+ *
+ * Operation (backward): aclnnFlashAttentionUnpaddingScoreGradV2 explainer,
+ * sections 2.3 and 4.2, and the PyPTO-Gym article, "反向公式":
+ *     P  = exp(scale Q K^T - softmax_max) / softmax_sum   (caller's stats)
+ *     D  = rowsum(dY * out)                                (caller's out)
+ *     dP = dY V^T,  dS = P * (dP - D)
+ *     dV = P^T dY,  dQ = scale dS K,  dK = scale dS^T Q
+ *
+ * Call pattern: query the workspace size, let the caller allocate it on the
+ * device, then call the operation on a stream (the two-phase pattern of the
+ * aclnn APIs, explainer section 3).
+ *
+ * Layouts (all row-major, contiguous, device memory unless stated):
+ *   q, out, dy, dq     [t_q,  num_heads, head_dim]   element type `dtype`
+ *   k, v, dk, dv       [t_kv, num_heads, head_dim]   element type `dtype`
+ *   softmax_max/_sum   [t_q,  num_heads, 8] float32; all 8 entries of a row
+ *                      hold the same value (TND statistics layout of the
+ *                      explainer, section 4.2; column 0 is the one read).
+ *   cu_seqlens_q/_kv   HOST int64 arrays of num_seqs inclusive cumulative
+ *                      ends, no leading zero (e.g. {256}; {2, 5, 9, 0, 0}:
+ *                      a zero after a positive entry starts a trailing run of
+ *                      non-participating batches, explainer section 6.4).
+ *
+ * Conventions that the pages leave open:
+ *   - a query row with no allowed key gets out = 0, softmax_max = -inf,
+ *     softmax_sum = 0 and dq = 0; a key no query attends gets dk = dv = 0;
+ *   - tokens after the last participating end get out = 0, softmax_max =
+ *     -inf, softmax_sum = 0, dq = dk = dv = 0;
+ *   - sparse_mode 0 ignores pre_tokens / next_tokens.
+ *
+ * Ownership: every device buffer, the workspace included, belongs to the
+ * caller; the library never allocates or frees caller memory.  Host arrays
+ * are read during the call only.  All device work is enqueued on `stream`
+ * (a hipStream_t; NULL = the default stream) and the calls return without
+ * waiting for it; the caller keeps the buffers alive until the stream has
+ * finished.  Calls on one stream are ordered; distinct calls that share a
+ * workspace must not overlap in time.
+ *
+ * Errors: all validation runs on the host before anything is enqueued; on a
+ * non-OK status nothing is written.  swa_last_error() returns a message for
+ * the last non-OK status of the calling thread.
+ */
+#ifndef SWA_H_
+#define SWA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum swa_status {
+  SWA_OK = 0,
+  /* a required pointer is NULL (the pages' ACLNN_ERR_PARAM_NULLPTR, 161001) */
+  SWA_ERR_NULLPTR = 1,
+  /* an argument is out of range: sparse_mode not 0/4, sizes, inconsistent or
+   * decreasing cumulative ends, pre_tokens + next_tokens < 0, non-finite
+   * scale (the pages' ACLNN_ERR_PARAM_INVALID, 161002) */
+  SWA_ERR_INVALID = 2,
+  /* valid on the pages but not provided by this library: head_dim other than
+   * 64 or 128, fp16, and sparse_mode 4 with a batch whose query and key
+   * lengths differ */
+  SWA_ERR_UNSUPPORTED = 3,
+  /* workspace_bytes is smaller than the size query returned */
+  SWA_ERR_WORKSPACE = 4,
+  /* a HIP runtime call failed; the message carries hipGetErrorString */
+  SWA_ERR_HIP = 5
+} swa_status;
+
+typedef enum swa_dtype {
+  SWA_DTYPE_FP32 = 0,
+  SWA_DTYPE_BF16 = 1,
+  SWA_DTYPE_FP16 = 2 /* listed by the pages; returns SWA_ERR_UNSUPPORTED */
+} swa_dtype;
+
+/* Device workspace bytes that swa_forward needs for a batch of num_seqs
+ * sequences (bounds only depend on the sizes, not on the lengths). */
+swa_status swa_forward_workspace_size(int64_t num_seqs, int64_t t_q, int64_t t_kv,
+                                      int64_t num_heads, int64_t head_dim, int32_t dtype,
+                                      size_t* bytes);
+
+/* Device workspace bytes that swa_backward needs: the tile schedule, the
+ * row terms D = rowsum(dY * out) and the fp32 dq accumulator
+ * [t_q, num_heads, head_dim]. */
+swa_status swa_backward_workspace_size(int64_t num_seqs, int64_t t_q, int64_t t_kv,
+                                       int64_t num_heads, int64_t head_dim, int32_t dtype,
+                                       size_t* bytes);
+
+/* Forward pass.  Writes out, softmax_max, softmax_sum.  `scale` is the
+ * multiplier of Q K^T (usually head_dim^-0.5, API doc, scaleValueOptional).
+ * Valid ranges: num_seqs 1..2048, t_q and t_kv 1..2^20, num_heads 1..256,
+ * head_dim 1..768 (64 and 128 supported). */
+swa_status swa_forward(const void* q, const void* k, const void* v,
+                       const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,
+                       int64_t num_seqs, int64_t t_q, int64_t t_kv, int64_t num_heads,
+                       int64_t head_dim, int32_t dtype, double scale, int64_t pre_tokens,
+                       int64_t next_tokens, int64_t sparse_mode, void* out, float* softmax_max,
+                       float* softmax_sum, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* Backward pass.  Takes the forward's out and statistics verbatim (it does
+ * not recompute them) and writes dq, dk, dv.  The sequence, shape and scalar
+ * arguments must be those of the forward call that produced out and the
+ * statistics; the library cannot check this.  dq is accumulated with fp32
+ * atomics, so its last bits may differ from run to run (the pages' backward
+ * is non-deterministic by default, explainer section 6.1). */
+swa_status swa_backward(const void* q, const void* k, const void* v, const void* dy,
+                        const void* out, const float* softmax_max, const float* softmax_sum,
+                        const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,
+                        int64_t num_seqs, int64_t t_q, int64_t t_kv, int64_t num_heads,
+                        int64_t head_dim, int32_t dtype, double scale, int64_t pre_tokens,
+                        int64_t next_tokens, int64_t sparse_mode, void* dq, void* dk, void* dv,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none).
+ * The pointer stays valid until the next call on the same thread. */
+const char* swa_last_error(void);
+
+/* Host-only: the tile schedule the kernels would run, for checking the
+ * skip pattern.  direction 0 = forward (items are query blocks, tiles are
+ * key blocks), 1 = backward (items are key blocks, tiles are query blocks).
+ * Writes rows of 4 int32 {sequence, item block, tile, kind} in schedule
+ * order, kind 1 = partial (element mask applied), 2 = full (no mask); an
+ * item with no visited tile contributes one row {sequence, block, -1, 0}.
+ * rows_out may be NULL to query the count; *n_rows receives the number of
+ * rows (at most `capacity` are written).  *block_item / *block_tile receive
+ * the block sizes used. */
+swa_status swa_debug_tile_schedule(const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,
+                                   int64_t num_seqs, int64_t t_q, int64_t t_kv,
+                                   int64_t head_dim, int32_t dtype, int64_t pre_tokens,
+                                   int64_t next_tokens, int64_t sparse_mode, int32_t direction,
+                                   int32_t* rows_out, int64_t capacity, int64_t* n_rows,
+                                   int32_t* block_item, int32_t* block_tile);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWA_H_ */

@@ -1,0 +1,110 @@
+"""Shared helpers for the GPU parity tests: run the HIP path, run the oracle,
+compare with the tolerances of the method's precision contract.
+
+Tolerances (per output tensor):
+  fp32 inputs : max |g - o| / max |o| <= 1e-4 (out, dq, dk, dv); the
+                statistics use the same relative bound.
+  bf16 inputs : max |g - o| <= 2e-2 and mean |g - o| <= 5e-3 (out, dq, dk, dv,
+                fp32 accumulation); softmax_max abs <= 1e-3 and softmax_sum
+                rel <= 1e-3.
+"""
+from __future__ import annotations
+
+import sys
+
+import torch
+
+import oracle
+import transformer_attention_tnd_amd as swa
+
+TOL_FP32_REL = 1e-4
+TOL_BF16_MAX = 2e-2
+TOL_BF16_MEAN = 5e-3
+TOL_STAT_MAX_ABS = 1e-3
+TOL_STAT_SUM_REL = 1e-3
+
+
+def note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def require_gpu():
+    assert torch.cuda.is_available(), "GPU test run without a GPU"
+    swa.load_library()
+    return torch.device("cuda:0")
+
+
+def run_hip(p, device, with_backward=True):
+    """Forward (+ backward) of problem p through the C ABI; host copies."""
+    q, k, v, dy = (x.to(device) for x in (p.q, p.k, p.v, p.dy))
+    out, smax, ssum = swa.forward(q, k, v, p.cu_seqlens_q, p.cu_seqlens_kv, p.scale,
+                                  p.pre_tokens, p.next_tokens, p.sparse_mode)
+    res = {"out": out, "smax": smax, "ssum": ssum}
+    if with_backward:
+        dq, dk, dv = swa.backward(q, k, v, dy, out, smax, ssum, p.cu_seqlens_q,
+                                  p.cu_seqlens_kv, p.scale, p.pre_tokens, p.next_tokens,
+                                  p.sparse_mode)
+        res.update(dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    return {k_: v_.cpu() for k_, v_ in res.items()}
+
+
+def run_oracle(p, chunk=256):
+    out, sm, ss = oracle.forward(p.q, p.k, p.v, p.cu_seqlens_q, p.cu_seqlens_kv, p.scale,
+                                 p.pre_tokens, p.next_tokens, p.sparse_mode, chunk=chunk)
+    dq, dk, dv = oracle.backward(p.q, p.k, p.v, p.dy, out, sm, ss, p.cu_seqlens_q,
+                                 p.cu_seqlens_kv, p.scale, p.pre_tokens, p.next_tokens,
+                                 p.sparse_mode, chunk=chunk)
+    return {"out": out, "smax": sm, "ssum": ss, "dq": dq, "dk": dk, "dv": dv}
+
+
+def err_stats(g, o):
+    g = g.double()
+    o = o.double()
+    d = (g - o).abs()
+    return float(d.max()), float(d.mean()), float(o.abs().max())
+
+
+def assert_close(name, g, o, dtype):
+    mx, mean, ref = err_stats(g, o)
+    if dtype == torch.float32:
+        rel = mx / max(ref, 1e-30)
+        note(f"  {name}: max_abs={mx:.3e} max_rel={rel:.3e} (|ref|max={ref:.3e})")
+        assert rel <= TOL_FP32_REL, f"{name}: max relative error {rel:.3e} > {TOL_FP32_REL}"
+    else:
+        note(f"  {name}: max_abs={mx:.3e} mean_abs={mean:.3e} (|ref|max={ref:.3e})")
+        assert mx <= TOL_BF16_MAX, f"{name}: max abs error {mx:.3e} > {TOL_BF16_MAX}"
+        assert mean <= TOL_BF16_MEAN, f"{name}: mean abs error {mean:.3e} > {TOL_BF16_MEAN}"
+
+
+def assert_stats(smax_g, ssum_g, smax_o, ssum_o, dtype):
+    """Statistics [.., 8] from the GPU against oracle [..]; all 8 copies equal."""
+    assert torch.equal(smax_g, smax_g[..., :1].expand_as(smax_g)), "softmax_max copies differ"
+    assert torch.equal(ssum_g, ssum_g[..., :1].expand_as(ssum_g)), "softmax_sum copies differ"
+    gm, gs = smax_g[..., 0].double(), ssum_g[..., 0].double()
+    om, os_ = smax_o.double(), ssum_o.double()
+    inf_g, inf_o = torch.isinf(gm), torch.isinf(om)
+    assert torch.equal(inf_g, inf_o), "empty-row pattern of softmax_max differs"
+    assert torch.equal(gs == 0, os_ == 0), "empty-row pattern of softmax_sum differs"
+    fin = ~inf_o
+    if fin.any():
+        dm = float((gm[fin] - om[fin]).abs().max())
+        ds = float(((gs[fin] - os_[fin]).abs() / os_[fin].abs()).max())
+        note(f"  softmax_max: max_abs={dm:.3e}  softmax_sum: max_rel={ds:.3e}")
+        if dtype == torch.float32:
+            ref = float(om[fin].abs().max())
+            assert dm <= TOL_FP32_REL * max(ref, 1.0)
+            assert ds <= TOL_FP32_REL
+        else:
+            assert dm <= TOL_STAT_MAX_ABS
+            assert ds <= TOL_STAT_SUM_REL
+
+
+def compare_full(p, g, o):
+    dt = p.dtype
+    assert_close("out", g["out"], o["out"], dt)
+    assert_stats(g["smax"], g["ssum"], o["smax"], o["ssum"], dt)
+    for n in ("dq", "dk", "dv"):
+        if n in g:
+            assert_close(n, g[n], o[n], dt)

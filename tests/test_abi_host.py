@@ -1,0 +1,176 @@
+"""Host-side checks of the C ABI (CPU only: no kernel is launched).
+
+* libswa.so loads and exports every function include/swa.h declares;
+* validation returns the documented status for each bad argument, before
+  anything touches the GPU;
+* the tile schedule (swa_debug_tile_schedule) equals the brute-force
+  enumeration of oracle/tiles.py tile by tile (the skip and mask pattern).
+"""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import oracle
+import transformer_attention_tnd_amd as swa
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+INT_MAX = 2147483647
+
+
+def declared_functions():
+    names = set()
+    for hdr in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(hdr).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(swa_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = swa.load_library()
+    names = declared_functions()
+    assert {"swa_forward", "swa_backward", "swa_forward_workspace_size",
+            "swa_backward_workspace_size", "swa_last_error",
+            "swa_debug_tile_schedule"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    # and nothing is exported under those names that the binding does not wrap
+    for n in names:
+        assert hasattr(swa, n), n
+
+
+def raw_forward(**kw):
+    """Call swa_forward through ctypes with fake (never dereferenced) pointers."""
+    lib = swa.load_library()
+    a = dict(q=1, k=1, v=1, cu_q=[16], cu_kv=[16], t_q=16, t_kv=16, n=2, d=64, dtype=1,
+             scale=0.125, pre=INT_MAX, nxt=INT_MAX, mode=0, out=1, smax=1, ssum=1, ws=1,
+             ws_bytes=1 << 30)
+    a.update(kw)
+    cq = (ctypes.c_int64 * max(1, len(a["cu_q"])))(*a["cu_q"])
+    ck = (ctypes.c_int64 * max(1, len(a["cu_kv"])))(*a["cu_kv"])
+    nseq = a.get("nseq", len(a["cu_q"]))
+    return lib.swa_forward(a["q"], a["k"], a["v"], cq, ck, nseq, a["t_q"], a["t_kv"], a["n"],
+                           a["d"], a["dtype"], a["scale"], a["pre"], a["nxt"], a["mode"],
+                           a["out"], a["smax"], a["ssum"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(q=None), swa.SWA_ERR_NULLPTR, "NULL"),
+    (dict(ws=None), swa.SWA_ERR_NULLPTR, "NULL"),
+    (dict(mode=2), swa.SWA_ERR_INVALID, "The sparse_mode value should be 0 or 4, but got 2"),
+    (dict(mode=1), swa.SWA_ERR_INVALID, "should be 0 or 4"),
+    (dict(nseq=0), swa.SWA_ERR_INVALID, "num_seqs"),
+    (dict(t_q=0), swa.SWA_ERR_INVALID, "t_q"),
+    (dict(t_q=(1 << 20) + 1, cu_q=[16]), swa.SWA_ERR_INVALID, "t_q"),
+    (dict(n=257), swa.SWA_ERR_INVALID, "num_heads"),
+    (dict(d=769), swa.SWA_ERR_INVALID, "head_dim"),
+    (dict(d=96), swa.SWA_ERR_UNSUPPORTED, "head_dim"),
+    (dict(dtype=2), swa.SWA_ERR_UNSUPPORTED, "fp16"),
+    (dict(dtype=7), swa.SWA_ERR_INVALID, "dtype"),
+    (dict(scale=float("nan")), swa.SWA_ERR_INVALID, "scale"),
+    (dict(cu_q=[8, 4], cu_kv=[8, 4]), swa.SWA_ERR_INVALID, "non-decreasing"),
+    (dict(cu_q=[8, 0, 4], cu_kv=[8, 0, 4]), swa.SWA_ERR_INVALID, "trailing"),
+    (dict(cu_q=[8, 16], cu_kv=[8, 0]), swa.SWA_ERR_INVALID, "participate"),
+    (dict(cu_q=[17], cu_kv=[17]), swa.SWA_ERR_INVALID, "exceeds t_q"),
+    (dict(cu_q=[-1], cu_kv=[-1]), swa.SWA_ERR_INVALID, ">= 0"),
+    (dict(mode=4, pre=3, nxt=-4), swa.SWA_ERR_INVALID, "pre_tokens + next_tokens"),
+    (dict(mode=4, cu_q=[8, 16], cu_kv=[10, 16]), swa.SWA_ERR_UNSUPPORTED, "sparse_mode 4"),
+    (dict(ws_bytes=16), swa.SWA_ERR_WORKSPACE, "workspace"),
+])
+def test_forward_validation_statuses(kw, status, needle):
+    assert raw_forward(**kw) == status
+    assert needle in swa.swa_last_error()
+
+
+def test_mode0_accepts_unequal_lengths_and_trailing_batches():
+    # only the schedule is built (host); the dump proves validation passed
+    rows, _, _ = swa.swa_debug_tile_schedule([5, 9, 0, 0], [7, 8, 0, 0], 9, 8, 64, 1,
+                                             INT_MAX, INT_MAX, 0, 0)
+    assert rows
+
+
+def test_workspace_sizes_monotone_and_backward_holds_dq_accumulator():
+    f = swa.swa_forward_workspace_size(1, 16384, 16384, 16, 128, 1)
+    b = swa.swa_backward_workspace_size(1, 16384, 16384, 16, 128, 1)
+    assert f > 0 and b >= 16384 * 16 * 128 * 4 + 2 * 16384 * 16 * 4
+    assert swa.swa_backward_workspace_size(4, 16384, 16384, 16, 128, 1) >= b
+    with pytest.raises(ValueError):
+        swa.swa_forward_workspace_size(1, 16, 16, 2, 80, 1)
+
+
+def compare_schedule(cu_q, cu_kv, mode, pre, nxt, direction):
+    t_q = max([c for c in cu_q] + [1])
+    t_kv = max([c for c in cu_kv] + [1])
+    rows, bi, bt = swa.swa_debug_tile_schedule(cu_q, cu_kv, t_q, t_kv, 128, 1, pre, nxt, mode,
+                                               direction)
+    got = {}
+    order = []
+    for seq, blk, tile, kind in rows:
+        key = (seq, blk)
+        if key not in got:
+            got[key] = []
+            order.append(key)
+        if tile >= 0:
+            got[key].append((tile, kind))
+    # tiles of one item are listed contiguously and in increasing order
+    assert len(order) == len(got)
+    for v in got.values():
+        assert [t for t, _ in v] == sorted(t for t, _ in v)
+    expect = oracle.enumerate_tiles(cu_q, cu_kv, mode, pre, nxt, bi, bt,
+                                    "fwd" if direction == 0 else "bwd")
+    # the oracle keys batches by participating index; map to batch index
+    seqs = oracle.sequences(cu_q)
+    exp = {(b, it): v for (b, it), v in expect.items()}
+    assert got == exp
+    return got
+
+
+SCHEDULE_CASES = [
+    ([128], [128], 0, INT_MAX, INT_MAX),
+    ([1000], [1000], 4, 100, 30),
+    ([1, 130, 257, 700, 701], [1, 130, 257, 700, 701], 4, 64, 0),
+    ([300, 300, 800], [300, 300, 800], 4, 0, 200),
+    ([0, 5, 5, 77], [0, 5, 5, 77], 0, 0, 0),
+    ([200, 450, 0, 0], [130, 700, 0, 0], 0, 5, 5),
+    ([513], [513], 4, 2048, 0),
+    ([1024], [1024], 4, 5, -3),
+    ([640], [640], 4, -64, 64),
+    ([4096], [4096], 4, 127, 1),
+]
+
+
+@pytest.mark.parametrize("direction", [0, 1])
+@pytest.mark.parametrize("case", SCHEDULE_CASES)
+def test_schedule_matches_bruteforce_enumeration(case, direction):
+    compare_schedule(*case, direction)
+
+
+@pytest.mark.parametrize("direction", [0, 1])
+def test_headline_schedule_skip_pattern(direction):
+    p = workloads.make_problem(workloads.HEADLINE)
+    got = compare_schedule(p.cu_seqlens_q, p.cu_seqlens_kv, 4, 2048, 0, direction)
+    vis = sum(len(v) for v in got.values())
+    full = sum(1 for v in got.values() for _, k in v if k == 2)
+    # 128-row query blocks: 112 blocks see 2176 keys = 34 tiles of 64, block
+    # qb < 16 sees 2 (qb + 1) tiles -> 112 * 34 + 272 = 4080 visited of the
+    # 128 * 256 = 32768 tiles (12.45 %); 4 partial tiles per complete-band
+    # block (two at each band edge) -> 480 partial.  The backward (128-key
+    # blocks over 64-row tiles) is the mirror image.
+    assert (vis, full) == (4080, 3600)
+
+
+def test_schedule_orders_longest_item_first():
+    rows, _, _ = swa.swa_debug_tile_schedule([100, 4100], [100, 4100], 4100, 4100, 128, 1,
+                                             INT_MAX, INT_MAX, 0, 0)
+    counts = []
+    last = None
+    for seq, blk, tile, kind in rows:
+        if (seq, blk) != last:
+            counts.append(0)
+            last = (seq, blk)
+        counts[-1] += 1
+    assert counts == sorted(counts, reverse=True)

@@ -1,0 +1,224 @@
+"""GPU parity of the HIP path against the fp64 oracle (needs an MI355X).
+
+Small problems (the two small workloads and hand-made varlen/band cases that
+span several tiles and ragged tails) are compared element by element.  The
+three large workloads run in full on the GPU, in the launch configuration the
+benchmark times, and are compared on sampled rows and keys that the oracle
+evaluates one at a time, plus invariants that hold at any size.
+"""
+import math
+
+import pytest
+import torch
+
+import oracle
+import transformer_attention_tnd_amd as swa
+import workloads
+from parity_utils import (assert_close, assert_stats, compare_full, note, require_gpu,
+                          run_hip, run_oracle)
+
+pytestmark = pytest.mark.gpu
+INT_MAX = 2147483647
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return require_gpu()
+
+
+# ------------------------------------------------------------ small, full parity
+
+@pytest.mark.parametrize("name", ["dense_fp32_b1_n2_s128_d64", "dense_bf16_b1_n8_s512_d64"])
+def test_small_workloads_full_parity(dev, name):
+    p = workloads.make_problem(name)
+    note(f"[parity] {name}")
+    g = run_hip(p, dev)
+    o = run_oracle(p)
+    compare_full(p, g, o)
+
+
+CUSTOM = {
+    "bf16_d128_band_ragged": dict(lengths_q=[1, 130, 257, 700], num_heads=3, head_dim=128,
+                                  sparse_mode=4, pre_tokens=64, next_tokens=0),
+    "bf16_d128_dense_varlen": dict(lengths_q=[200, 513], num_heads=2, head_dim=128),
+    "bf16_d64_band_both_sides": dict(lengths_q=[333, 129], num_heads=2, head_dim=64,
+                                     sparse_mode=4, pre_tokens=100, next_tokens=37),
+    "bf16_d128_dense_unequal_kv": dict(lengths_q=[77, 190], lengths_kv=[50, 260],
+                                       num_heads=2, head_dim=128),
+    "fp32_d128_band": dict(lengths_q=[300, 45], num_heads=2, head_dim=128, sparse_mode=4,
+                           pre_tokens=90, next_tokens=20, dtype=torch.float32),
+    "fp32_d64_dense_unequal_kv": dict(lengths_q=[77, 190], lengths_kv=[50, 260], num_heads=2,
+                                      head_dim=64, dtype=torch.float32),
+    "bf16_trailing_and_extra_tokens": dict(lengths_q=[100, 150], num_heads=2, head_dim=128,
+                                           sparse_mode=4, pre_tokens=40, next_tokens=8,
+                                           trailing=2, extra_tokens=5),
+    "bf16_zero_length_sequences": dict(lengths_q=[0, 64, 0, 100], num_heads=2, head_dim=64),
+    "bf16_empty_rows_negative_next": dict(lengths_q=[150, 90], num_heads=2, head_dim=128,
+                                          sparse_mode=4, pre_tokens=70, next_tokens=-5),
+    "bf16_narrow_band_negative_pre": dict(lengths_q=[260], num_heads=1, head_dim=128,
+                                          sparse_mode=4, pre_tokens=-3, next_tokens=9),
+    "bf16_band_wider_than_sequence": dict(lengths_q=[190, 66], num_heads=2, head_dim=128,
+                                          sparse_mode=4, pre_tokens=65536, next_tokens=65536),
+    "bf16_single_token": dict(lengths_q=[1], num_heads=4, head_dim=128),
+}
+
+
+@pytest.mark.parametrize("case", sorted(CUSTOM))
+def test_custom_cases_full_parity(dev, case):
+    kw = dict(CUSTOM[case])
+    p = workloads.make_custom(name=case, **kw)
+    note(f"[parity] {case} cu_q={p.cu_seqlens_q} cu_kv={p.cu_seqlens_kv}")
+    g = run_hip(p, dev)
+    o = run_oracle(p, chunk=None)
+    compare_full(p, g, o)
+    # tokens past the last participating end: zeros / -inf / 0
+    end = max(p.cu_seqlens_q)
+    if end < p.q.shape[0]:
+        assert g["out"][end:].abs().max() == 0 and g["dq"][end:].abs().max() == 0
+        assert torch.isinf(g["smax"][end:]).all() and (g["ssum"][end:] == 0).all()
+        endk = max(p.cu_seqlens_kv)
+        assert g["dk"][endk:].abs().max() == 0 and g["dv"][endk:].abs().max() == 0
+
+
+# ------------------------------------------------------------ exact cases
+
+def test_query_zero_counts_are_exact(dev):
+    """q = 0 (fp32): every score is 0, so softmax_max = 0 and softmax_sum = the
+    number of allowed keys exactly; with V_j = e_(j mod D), out[i, c] is the
+    fraction of allowed keys j = c (mod D): the mask pattern shows bit-exactly."""
+    lengths = [300, 77, 513]
+    D = 64
+    pre, nxt = 70, 9
+    p = workloads.make_custom(lengths, num_heads=1, head_dim=D, dtype=torch.float32,
+                              sparse_mode=4, pre_tokens=pre, next_tokens=nxt)
+    p.q.zero_()
+    T = p.k.shape[0]
+    p.v.zero_()
+    for s0, L in oracle.sequences(p.cu_seqlens_kv):
+        for j in range(L):
+            p.v[s0 + j, 0, j % D] = 1.0
+    g = run_hip(p, dev, with_backward=False)
+    assert torch.equal(g["smax"], torch.zeros_like(g["smax"]))
+    for s0, L in oracle.sequences(p.cu_seqlens_q):
+        M = oracle.allowed_mask(torch.arange(L), torch.arange(L), 4, pre, nxt)
+        counts = M.sum(1)
+        assert torch.equal(g["ssum"][s0:s0 + L, 0, 0], counts.float())
+        per_c = torch.zeros(L, D)
+        for c in range(D):
+            per_c[:, c] = M[:, c::D].sum(1).float()
+        expect = per_c / counts[:, None].float()
+        out = g["out"][s0:s0 + L, 0]
+        assert torch.equal(out != 0, expect != 0), "mask pattern differs"
+        assert (out - expect).abs().max() <= 1e-6
+
+
+def test_forward_example_constant_inputs(dev):
+    """VarLenScore API doc call example (T=256, N=1, D=128, scale 0.088388,
+    pre/next 65536, mode 0) with q = k = v = 1: out = 1, softmax_max =
+    128 * 0.088388, softmax_sum = 256."""
+    x = torch.ones(256, 1, 128, dtype=torch.float32, device=dev)
+    out, smax, ssum = swa.forward(x, x, x, [256], [256], 0.088388, 65536, 65536, 0)
+    torch.cuda.synchronize()
+    assert (out - 1).abs().max().item() <= 1e-6
+    assert (smax - 128 * 0.088388).abs().max().item() <= 1e-5
+    assert (ssum == 256).all()
+
+
+def test_backward_example_uses_given_statistics(dev):
+    """UnpaddingScoreGradV2 explainer call example: all-ones q/k/v/dy/out with
+    softmax_max = softmax_sum = 3.0: dq = dk = 0 and dv = 256 exp(11.313664 - 3)/3."""
+    x = torch.ones(256, 1, 128, dtype=torch.float32, device=dev)
+    st = torch.full((256, 1, 8), 3.0, dtype=torch.float32, device=dev)
+    dq, dk, dv = swa.backward(x, x, x, x, x, st, st, [256], [256], 0.088388, 65536, 65536, 0)
+    torch.cuda.synchronize()
+    assert dq.abs().max().item() == 0 and dk.abs().max().item() == 0
+    expect = 256 * math.exp(128 * 0.088388 - 3) / 3
+    assert ((dv - expect).abs() / expect).max().item() <= 1e-5
+
+
+def test_varlen_equals_separate_calls(dev):
+    """Tiles align to each sequence's start, so a varlen call reproduces
+    separate per-sequence calls bit for bit (out, statistics, dk, dv); dq is
+    summed with atomics and only agrees within tolerance."""
+    lengths = [130, 64, 257, 1]
+    p = workloads.make_custom(lengths, num_heads=2, head_dim=128, sparse_mode=4,
+                              pre_tokens=50, next_tokens=20)
+    g = run_hip(p, dev)
+    for s0, L in oracle.sequences(p.cu_seqlens_q):
+        sl = slice(s0, s0 + L)
+        sub = workloads.Problem(p.q[sl].clone(), p.k[sl].clone(), p.v[sl].clone(),
+                                p.dy[sl].clone(), [L], [L], p.scale, p.pre_tokens,
+                                p.next_tokens, p.sparse_mode)
+        gs = run_hip(sub, dev)
+        for n in ("out", "smax", "ssum", "dk", "dv"):
+            assert torch.equal(gs[n], g[n][sl]), n
+        assert (gs["dq"].float() - g["dq"][sl].float()).abs().max() <= 2e-2
+
+
+# ------------------------------------------------------------ large workloads
+
+def sampled_check(p, g, samples):
+    """Compare GPU results with the oracle on (batch, head, first row/key) samples."""
+    dt = p.dtype
+    seqs = oracle.sequences(p.cu_seqlens_q)
+    errs = {"out": [], "dq": [], "dk": [], "dv": []}
+    smax_g, ssum_g, smax_o, ssum_o = [], [], [], []
+    for b, n, r0, width in samples:
+        s0, L = seqs[b]
+        r0 = min(r0, L - width)
+        Q, K, V, dY = (x[s0:s0 + L, n] for x in (p.q, p.k, p.v, p.dy))
+        rows = list(range(r0, r0 + width))
+        O, m, l = oracle.forward_rows(Q, K, V, rows, p.scale, p.sparse_mode, p.pre_tokens,
+                                      p.next_tokens)
+        dq = oracle.backward_rows(Q, K, V, dY, rows, p.scale, p.sparse_mode, p.pre_tokens,
+                                  p.next_tokens)
+        dk, dv = oracle.backward_keys(Q, K, V, dY, r0, r0 + width, p.scale, p.sparse_mode,
+                                      p.pre_tokens, p.next_tokens)
+        t = slice(s0 + r0, s0 + r0 + width)
+        errs["out"].append((g["out"][t, n], O))
+        errs["dq"].append((g["dq"][t, n], dq))
+        errs["dk"].append((g["dk"][t, n], dk))
+        errs["dv"].append((g["dv"][t, n], dv))
+        smax_g.append(g["smax"][t, n])
+        ssum_g.append(g["ssum"][t, n])
+        smax_o.append(m)
+        ssum_o.append(l)
+    for name, pairs in errs.items():
+        assert_close(name, torch.cat([a.flatten() for a, _ in pairs]),
+                     torch.cat([b.flatten() for _, b in pairs]), dt)
+    assert_stats(torch.cat(smax_g), torch.cat(ssum_g), torch.cat(smax_o), torch.cat(ssum_o), dt)
+
+
+def invariants_check(p, g):
+    """sum_j dV_j = sum_i dY_i and sum_j dK_j = 0 per (sequence, head)."""
+    for s0, L in oracle.sequences(p.cu_seqlens_q):
+        dv_sum = g["dv"][s0:s0 + L].double().sum(0)
+        dy_sum = p.dy[s0:s0 + L].double().sum(0)
+        dk_sum = g["dk"][s0:s0 + L].double().sum(0)
+        scale_dv = float(g["dv"][s0:s0 + L].double().abs().sum(0).max())
+        scale_dk = float(g["dk"][s0:s0 + L].double().abs().sum(0).max())
+        e1 = float((dv_sum - dy_sum).abs().max()) / scale_dv
+        e2 = float(dk_sum.abs().max()) / scale_dk
+        note(f"  invariants seq@{s0}: |sum dV - sum dY|/sum|dV| = {e1:.2e}, "
+             f"|sum dK|/sum|dK| = {e2:.2e}")
+        assert e1 <= 1e-2 and e2 <= 1e-2
+
+
+LARGE = [
+    ("varlen_bf16_n16_d128_8seq_256to4096", [(0, 0, 0, 64), (3, 7, 1000, 64), (7, 15, 10**9, 48)]),
+    ("swa_bf16_b1_n16_s16384_d128_pre2048_next0",
+     [(0, 0, 0, 64), (0, 5, 2000, 96), (0, 11, 9000, 64), (0, 15, 10**9, 64)]),
+    ("varlen_swa_bf16_n32_d128_4seq_16kto32k_pre4096_next512",
+     [(0, 0, 0, 64), (1, 13, 4500, 64), (2, 31, 20000, 64), (3, 20, 10**9, 64)]),
+]
+
+
+@pytest.mark.parametrize("name,samples", LARGE, ids=[n for n, _ in LARGE])
+def test_large_workloads_sampled_parity(dev, name, samples):
+    p = workloads.make_problem(name)
+    note(f"[parity] {name} T={p.q.shape[0]} cu={p.cu_seqlens_q}")
+    g = run_hip(p, dev)
+    for key in ("out", "dq", "dk", "dv"):
+        assert torch.isfinite(g[key].float()).all(), key
+    sampled_check(p, g, samples)
+    invariants_check(p, g)

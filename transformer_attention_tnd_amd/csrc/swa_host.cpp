@@ -1,0 +1,520 @@
+// Host side of the library: argument validation, the varlen tile schedule and
+// the C ABI entry points declared in include/swa.h.
+//
+// The tile schedule is the host half of skipping masked work: the actual_seq
+// values drive the tiling (aclnnFlashAttentionUnpaddingScoreGradV2 explainer,
+// section 8.1, where the actual_seq inputs are value-dependent), and with
+// sparse_mode 4 every tile outside the band -pre_tokens <= j - i <= next_tokens
+// is never visited (op-plugin sliding-window blog, section 1.3).
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/swa.h"
+#include "swa_internal.hpp"
+
+namespace swa {
+namespace {
+
+thread_local std::string g_err;
+
+swa_status fail(swa_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+struct Seq {
+  int64_t q0, sq, k0, skv;
+  int32_t b;
+};
+
+int64_t floor_div(int64_t a, int64_t b) {
+  int64_t q = a / b;
+  if ((a % b != 0) && ((a < 0) != (b < 0))) --q;
+  return q;
+}
+int64_t ceil_div(int64_t a, int64_t b) { return -floor_div(-a, b); }
+
+constexpr int64_t kMaxT = int64_t(1) << 20;  // explainer 6.3: T in 1..1M
+
+swa_status check_sizes(int64_t num_seqs, int64_t t_q, int64_t t_kv, int64_t num_heads,
+                       int64_t head_dim, int32_t dtype) {
+  if (num_seqs < 1 || num_seqs > 2048)
+    return fail(SWA_ERR_INVALID, "num_seqs must be in 1..2048, got " + std::to_string(num_seqs));
+  if (t_q < 1 || t_q > kMaxT || t_kv < 1 || t_kv > kMaxT)
+    return fail(SWA_ERR_INVALID, "t_q and t_kv must be in 1..1048576, got " +
+                                     std::to_string(t_q) + ", " + std::to_string(t_kv));
+  if (num_heads < 1 || num_heads > 256)
+    return fail(SWA_ERR_INVALID, "num_heads must be in 1..256, got " + std::to_string(num_heads));
+  if (head_dim < 1 || head_dim > 768)
+    return fail(SWA_ERR_INVALID, "head_dim must be in 1..768, got " + std::to_string(head_dim));
+  if (dtype != SWA_DTYPE_FP32 && dtype != SWA_DTYPE_BF16 && dtype != SWA_DTYPE_FP16)
+    return fail(SWA_ERR_INVALID, "dtype must be 0 (fp32), 1 (bf16) or 2 (fp16), got " +
+                                     std::to_string(dtype));
+  if (dtype == SWA_DTYPE_FP16)
+    return fail(SWA_ERR_UNSUPPORTED, "fp16 inputs are not supported (fp32 and bf16 are)");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(SWA_ERR_UNSUPPORTED,
+                "head_dim " + std::to_string(head_dim) + " is not supported (64 and 128 are)");
+  return SWA_OK;
+}
+
+// Parse the cumulative ends into participating sequences.
+swa_status parse_seqs(const Problem& p, std::vector<Seq>& seqs, int64_t* end_q,
+                      int64_t* end_kv) {
+  seqs.clear();
+  int64_t prev_q = 0, prev_kv = 0;
+  bool trail_q = false, trail_kv = false;
+  for (int64_t b = 0; b < p.num_seqs; ++b) {
+    const int64_t cq = p.cu_q[b], ck = p.cu_kv[b];
+    if (cq < 0 || ck < 0) return fail(SWA_ERR_INVALID, "cu_seqlens entries must be >= 0");
+    if (trail_q || trail_kv) {
+      if (cq != 0 || ck != 0)
+        return fail(SWA_ERR_INVALID, "cu_seqlens: nonzero entry after the trailing zero run at "
+                                     "batch " + std::to_string(b));
+      continue;
+    }
+    const bool tq = (cq == 0 && prev_q > 0), tk = (ck == 0 && prev_kv > 0);
+    if (tq != tk)
+      return fail(SWA_ERR_INVALID, "cu_seqlens_q and cu_seqlens_kv disagree on which batches "
+                                   "participate (batch " + std::to_string(b) + ")");
+    if (tq) {
+      trail_q = trail_kv = true;
+      continue;
+    }
+    if (cq < prev_q || ck < prev_kv)
+      return fail(SWA_ERR_INVALID, "cu_seqlens must be non-decreasing (batch " +
+                                       std::to_string(b) + ")");
+    seqs.push_back(Seq{prev_q, cq - prev_q, prev_kv, ck - prev_kv, static_cast<int32_t>(b)});
+    prev_q = cq;
+    prev_kv = ck;
+  }
+  if (prev_q > p.t_q)
+    return fail(SWA_ERR_INVALID, "last cu_seqlens_q end " + std::to_string(prev_q) +
+                                     " exceeds t_q " + std::to_string(p.t_q));
+  if (prev_kv > p.t_kv)
+    return fail(SWA_ERR_INVALID, "last cu_seqlens_kv end " + std::to_string(prev_kv) +
+                                     " exceeds t_kv " + std::to_string(p.t_kv));
+  if (p.sparse_mode == 4) {
+    for (const Seq& s : seqs)
+      if (s.sq != s.skv)
+        return fail(SWA_ERR_UNSUPPORTED,
+                    "sparse_mode 4 needs equal query and key lengths per batch; batch " +
+                        std::to_string(s.b) + " has " + std::to_string(s.sq) + " and " +
+                        std::to_string(s.skv));
+  }
+  *end_q = prev_q;
+  *end_kv = prev_kv;
+  return SWA_OK;
+}
+
+swa_status validate(const Problem& p, std::vector<Seq>& seqs, int64_t* end_q, int64_t* end_kv) {
+  if (!p.cu_q || !p.cu_kv) return fail(SWA_ERR_NULLPTR, "cu_seqlens_q / cu_seqlens_kv is NULL");
+  swa_status s = check_sizes(p.num_seqs, p.t_q, p.t_kv, p.num_heads, p.head_dim, p.dtype);
+  if (s != SWA_OK) return s;
+  if (p.sparse_mode != 0 && p.sparse_mode != 4)
+    return fail(SWA_ERR_INVALID, "The sparse_mode value should be 0 or 4, but got " +
+                                     std::to_string(p.sparse_mode));
+  if (!std::isfinite(p.scale)) return fail(SWA_ERR_INVALID, "scale must be finite");
+  if (p.sparse_mode == 4 && p.pre_tokens + p.next_tokens < 0)
+    return fail(SWA_ERR_INVALID, "pre_tokens + next_tokens must be >= 0 in sparse_mode 4 "
+                                 "(otherwise every row is empty)");
+  return parse_seqs(p, seqs, end_q, end_kv);
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int64_t max_items_fwd(int64_t num_seqs, int64_t t_q) {
+  return ceil_div(t_q, FWD_BM) + num_seqs;
+}
+int64_t max_items_bwd(int64_t num_seqs, int64_t t_kv) {
+  return ceil_div(t_kv, BWD_BN) + num_seqs;
+}
+
+struct BwdLayout {
+  size_t items, drow, lse2, dq_acc, total;
+};
+
+BwdLayout bwd_layout(int64_t num_seqs, int64_t t_q, int64_t t_kv, int64_t n, int64_t d) {
+  BwdLayout l;
+  l.items = 0;
+  l.drow = align256(sizeof(Item) * max_items_bwd(num_seqs, t_kv));
+  l.lse2 = l.drow + align256(sizeof(float) * t_q * n);
+  l.dq_acc = l.lse2 + align256(sizeof(float) * t_q * n);
+  l.total = l.dq_acc + align256(sizeof(float) * t_q * n * d);
+  return l;
+}
+
+// Forward schedule: one item per block of FWD_BM query rows; key tiles of
+// FWD_BN.  A tile is visited iff some (i < Sq, j < Skv) in it is allowed, and
+// is "full" iff the whole FWD_BM x FWD_BN tile lies inside the sequence and
+// inside the band.
+void schedule_forward(const Problem& p, const std::vector<Seq>& seqs, std::vector<Item>& items) {
+  items.clear();
+  const int64_t BM = FWD_BM, BN = FWD_BN;
+  for (const Seq& s : seqs) {
+    if (s.sq == 0) continue;
+    const int64_t nqb = ceil_div(s.sq, BM);
+    for (int64_t qb = 0; qb < nqb; ++qb) {
+      const int64_t r0 = qb * BM, r1 = std::min(r0 + BM, s.sq) - 1;
+      int64_t lo = 1, hi = 0, flo = 1, fhi = 0;
+      if (s.skv > 0) {
+        int64_t jlo = 0, jhi = s.skv - 1;
+        if (p.sparse_mode == 4) {
+          jlo = std::max<int64_t>(0, r0 - p.pre_tokens);
+          jhi = std::min<int64_t>(s.skv - 1, r1 + p.next_tokens);
+        }
+        if (jlo <= jhi) {
+          lo = jlo / BN;
+          hi = jhi / BN;
+          if (r0 + BM <= s.sq) {
+            flo = lo;
+            fhi = std::min(hi, s.skv / BN - 1);
+            if (p.sparse_mode == 4) {
+              flo = std::max(flo, ceil_div(r0 + BM - 1 - p.pre_tokens, BN));
+              fhi = std::min(fhi, floor_div(r0 + p.next_tokens - BN + 1, BN));
+            }
+          }
+        }
+      }
+      Item it;
+      it.q_base = static_cast<int32_t>(s.q0);
+      it.kv_base = static_cast<int32_t>(s.k0);
+      it.sq = static_cast<int32_t>(s.sq);
+      it.skv = static_cast<int32_t>(s.skv);
+      it.block = static_cast<int32_t>(qb);
+      it.tiles = pack_range(lo, hi);
+      it.full = pack_range(flo, fhi);
+      it.seq = s.b;
+      items.push_back(it);
+    }
+  }
+}
+
+// Backward schedule: one item per block of BWD_BN keys; query tiles of BWD_BM.
+void schedule_backward(const Problem& p, const std::vector<Seq>& seqs,
+                       std::vector<Item>& items) {
+  items.clear();
+  const int64_t BN = BWD_BN, BM = BWD_BM;
+  for (const Seq& s : seqs) {
+    if (s.skv == 0) continue;
+    const int64_t nkb = ceil_div(s.skv, BN);
+    for (int64_t kb = 0; kb < nkb; ++kb) {
+      const int64_t k0 = kb * BN, k1 = std::min(k0 + BN, s.skv) - 1;
+      int64_t lo = 1, hi = 0, flo = 1, fhi = 0;
+      if (s.sq > 0) {
+        int64_t ilo = 0, ihi = s.sq - 1;
+        if (p.sparse_mode == 4) {
+          ilo = std::max<int64_t>(0, k0 - p.next_tokens);
+          ihi = std::min<int64_t>(s.sq - 1, k1 + p.pre_tokens);
+        }
+        if (ilo <= ihi) {
+          lo = ilo / BM;
+          hi = ihi / BM;
+          if (k0 + BN <= s.skv) {
+            flo = lo;
+            fhi = std::min(hi, s.sq / BM - 1);
+            if (p.sparse_mode == 4) {
+              flo = std::max(flo, ceil_div(k0 + BN - 1 - p.next_tokens, BM));
+              fhi = std::min(fhi, floor_div(k0 + p.pre_tokens - BM + 1, BM));
+            }
+          }
+        }
+      }
+      Item it;
+      it.q_base = static_cast<int32_t>(s.q0);
+      it.kv_base = static_cast<int32_t>(s.k0);
+      it.sq = static_cast<int32_t>(s.sq);
+      it.skv = static_cast<int32_t>(s.skv);
+      it.block = static_cast<int32_t>(kb);
+      it.tiles = pack_range(lo, hi);
+      it.full = pack_range(flo, fhi);
+      it.seq = s.b;
+      items.push_back(it);
+    }
+  }
+}
+
+int range_lo(int32_t r) { return r & 0xffff; }
+int range_hi(int32_t r) { return (r >> 16) & 0xffff; }
+int64_t cost(const Item& it) {
+  const int lo = range_lo(it.tiles), hi = range_hi(it.tiles);
+  return hi >= lo ? hi - lo + 1 : 0;
+}
+
+// Longest item first (stable, so equal-cost blocks of one sequence stay in
+// order and neighbouring query blocks, which read the same key/value tiles,
+// run close together).
+void order_items(std::vector<Item>& items) {
+  std::stable_sort(items.begin(), items.end(),
+                   [](const Item& a, const Item& b) { return cost(a) > cost(b); });
+}
+
+// Pinned staging buffers for uploading the schedule.  A slot is reused only
+// after the copy recorded behind it has completed.
+struct Staging {
+  std::mutex mu;
+  struct Slot {
+    void* host = nullptr;
+    size_t cap = 0;
+    void* event = nullptr;
+    bool pending = false;
+  } slots[8];
+  unsigned next = 0;
+};
+Staging g_staging;
+
+swa_status upload(const std::vector<Item>& items, void* dst, void* stream) {
+  const size_t bytes = sizeof(Item) * items.size();
+  if (bytes == 0) return SWA_OK;
+  std::lock_guard<std::mutex> lock(g_staging.mu);
+  Staging::Slot& s = g_staging.slots[g_staging.next++ % 8];
+  int e = 0;
+  if (s.pending) {
+    if ((e = hip_event_sync(s.event)) != 0) return fail(SWA_ERR_HIP, hip_error_string(e));
+    s.pending = false;
+  }
+  if (s.cap < bytes) {
+    if (s.host) hip_pinned_free(s.host);
+    s.host = nullptr;
+    s.cap = 0;
+    const size_t cap = std::max<size_t>(bytes, 64 * 1024);
+    if ((e = hip_pinned_alloc(&s.host, cap)) != 0) return fail(SWA_ERR_HIP, hip_error_string(e));
+    s.cap = cap;
+  }
+  if (!s.event && (e = hip_event_create(&s.event)) != 0)
+    return fail(SWA_ERR_HIP, hip_error_string(e));
+  std::memcpy(s.host, items.data(), bytes);
+  if ((e = hip_memcpy_h2d_async(dst, s.host, bytes, stream)) != 0)
+    return fail(SWA_ERR_HIP, hip_error_string(e));
+  if ((e = hip_event_record(s.event, stream)) != 0) return fail(SWA_ERR_HIP, hip_error_string(e));
+  s.pending = true;
+  return SWA_OK;
+}
+
+int32_t clamp_window(int64_t x) {
+  const int64_t lim = int64_t(1) << 30;
+  return static_cast<int32_t>(std::max(-lim, std::min(lim, x)));
+}
+
+Problem make_problem(const int64_t* cu_q, const int64_t* cu_kv, int64_t num_seqs, int64_t t_q,
+                     int64_t t_kv, int64_t n, int64_t d, int32_t dtype, double scale,
+                     int64_t pre, int64_t next, int64_t mode) {
+  Problem p;
+  p.num_seqs = num_seqs;
+  p.t_q = t_q;
+  p.t_kv = t_kv;
+  p.num_heads = n;
+  p.head_dim = d;
+  p.dtype = dtype;
+  p.scale = scale;
+  p.pre_tokens = pre;
+  p.next_tokens = next;
+  p.sparse_mode = mode;
+  p.cu_q = cu_q;
+  p.cu_kv = cu_kv;
+  return p;
+}
+
+size_t elem_bytes(int32_t dtype) { return dtype == SWA_DTYPE_FP32 ? 4 : 2; }
+
+}  // namespace
+}  // namespace swa
+
+using namespace swa;
+
+extern "C" {
+
+const char* swa_last_error(void) { return g_err.c_str(); }
+
+swa_status swa_forward_workspace_size(int64_t num_seqs, int64_t t_q, int64_t t_kv,
+                                      int64_t num_heads, int64_t head_dim, int32_t dtype,
+                                      size_t* bytes) {
+  if (!bytes) return fail(SWA_ERR_NULLPTR, "bytes is NULL");
+  swa_status s = check_sizes(num_seqs, t_q, t_kv, num_heads, head_dim, dtype);
+  if (s != SWA_OK) return s;
+  *bytes = align256(sizeof(Item) * max_items_fwd(num_seqs, t_q));
+  return SWA_OK;
+}
+
+swa_status swa_backward_workspace_size(int64_t num_seqs, int64_t t_q, int64_t t_kv,
+                                       int64_t num_heads, int64_t head_dim, int32_t dtype,
+                                       size_t* bytes) {
+  if (!bytes) return fail(SWA_ERR_NULLPTR, "bytes is NULL");
+  swa_status s = check_sizes(num_seqs, t_q, t_kv, num_heads, head_dim, dtype);
+  if (s != SWA_OK) return s;
+  *bytes = bwd_layout(num_seqs, t_q, t_kv, num_heads, head_dim).total;
+  return SWA_OK;
+}
+
+swa_status swa_forward(const void* q, const void* k, const void* v, const int64_t* cu_seqlens_q,
+                       const int64_t* cu_seqlens_kv, int64_t num_seqs, int64_t t_q,
+                       int64_t t_kv, int64_t num_heads, int64_t head_dim, int32_t dtype,
+                       double scale, int64_t pre_tokens, int64_t next_tokens,
+                       int64_t sparse_mode, void* out, float* softmax_max, float* softmax_sum,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !out || !softmax_max || !softmax_sum || !workspace)
+    return fail(SWA_ERR_NULLPTR, "a required tensor or the workspace is NULL");
+  Problem p = make_problem(cu_seqlens_q, cu_seqlens_kv, num_seqs, t_q, t_kv, num_heads,
+                           head_dim, dtype, scale, pre_tokens, next_tokens, sparse_mode);
+  std::vector<Seq> seqs;
+  int64_t end_q = 0, end_kv = 0;
+  swa_status s = validate(p, seqs, &end_q, &end_kv);
+  if (s != SWA_OK) return s;
+  const size_t need = align256(sizeof(Item) * max_items_fwd(num_seqs, t_q));
+  if (workspace_bytes < need)
+    return fail(SWA_ERR_WORKSPACE, "workspace has " + std::to_string(workspace_bytes) +
+                                       " bytes, needs " + std::to_string(need));
+  std::vector<Item> items;
+  schedule_forward(p, seqs, items);
+  order_items(items);
+  if ((s = upload(items, workspace, stream)) != SWA_OK) return s;
+  int e = 0;
+  if (end_q < t_q) {
+    FillArgs f{out, static_cast<int64_t>(elem_bytes(dtype)), num_heads * head_dim, end_q, t_q,
+               softmax_max, softmax_sum, num_heads * 8};
+    if ((e = launch_fill(f, stream)) != 0) return fail(SWA_ERR_HIP, hip_error_string(e));
+  }
+  if (!items.empty()) {
+    FwdArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    a.smax = softmax_max;
+    a.ssum = softmax_sum;
+    a.items = static_cast<const Item*>(workspace);
+    a.n_items = static_cast<int32_t>(items.size());
+    a.num_heads = static_cast<int32_t>(num_heads);
+    a.scale_log2 = static_cast<float>(scale * 1.4426950408889634);
+    a.mode = static_cast<int32_t>(sparse_mode);
+    a.pre = clamp_window(pre_tokens);
+    a.next = clamp_window(next_tokens);
+    if ((e = launch_forward(a, dtype, static_cast<int>(head_dim), stream)) != 0)
+      return fail(SWA_ERR_HIP, hip_error_string(e));
+  }
+  return SWA_OK;
+}
+
+swa_status swa_backward(const void* q, const void* k, const void* v, const void* dy,
+                        const void* out, const float* softmax_max, const float* softmax_sum,
+                        const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,
+                        int64_t num_seqs, int64_t t_q, int64_t t_kv, int64_t num_heads,
+                        int64_t head_dim, int32_t dtype, double scale, int64_t pre_tokens,
+                        int64_t next_tokens, int64_t sparse_mode, void* dq, void* dk, void* dv,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !dy || !out || !softmax_max || !softmax_sum || !dq || !dk || !dv ||
+      !workspace)
+    return fail(SWA_ERR_NULLPTR, "a required tensor or the workspace is NULL");
+  Problem p = make_problem(cu_seqlens_q, cu_seqlens_kv, num_seqs, t_q, t_kv, num_heads,
+                           head_dim, dtype, scale, pre_tokens, next_tokens, sparse_mode);
+  std::vector<Seq> seqs;
+  int64_t end_q = 0, end_kv = 0;
+  swa_status s = validate(p, seqs, &end_q, &end_kv);
+  if (s != SWA_OK) return s;
+  const BwdLayout L = bwd_layout(num_seqs, t_q, t_kv, num_heads, head_dim);
+  if (workspace_bytes < L.total)
+    return fail(SWA_ERR_WORKSPACE, "workspace has " + std::to_string(workspace_bytes) +
+                                       " bytes, needs " + std::to_string(L.total));
+  std::vector<Item> items;
+  schedule_backward(p, seqs, items);
+  order_items(items);
+  char* ws = static_cast<char*>(workspace);
+  if ((s = upload(items, ws + L.items, stream)) != SWA_OK) return s;
+  float* drow = reinterpret_cast<float*>(ws + L.drow);
+  float* lse2 = reinterpret_cast<float*>(ws + L.lse2);
+  float* dq_acc = reinterpret_cast<float*>(ws + L.dq_acc);
+  int e = 0;
+  BwdPreArgs pa{dy, out, softmax_max, softmax_sum, drow, lse2, dq_acc, t_q * num_heads};
+  if ((e = launch_bwd_pre(pa, dtype, static_cast<int>(head_dim), stream)) != 0)
+    return fail(SWA_ERR_HIP, hip_error_string(e));
+  if (!items.empty()) {
+    BwdArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.dy = dy;
+    a.drow = drow;
+    a.lse2 = lse2;
+    a.dq_acc = dq_acc;
+    a.dk = dk;
+    a.dv = dv;
+    a.items = reinterpret_cast<const Item*>(ws + L.items);
+    a.n_items = static_cast<int32_t>(items.size());
+    a.num_heads = static_cast<int32_t>(num_heads);
+    a.scale = static_cast<float>(scale);
+    a.scale_log2 = static_cast<float>(scale * 1.4426950408889634);
+    a.mode = static_cast<int32_t>(sparse_mode);
+    a.pre = clamp_window(pre_tokens);
+    a.next = clamp_window(next_tokens);
+    if ((e = launch_backward(a, dtype, static_cast<int>(head_dim), stream)) != 0)
+      return fail(SWA_ERR_HIP, hip_error_string(e));
+  }
+  FinalizeArgs fa{dq_acc, dq, static_cast<float>(scale), t_q * num_heads * head_dim};
+  if ((e = launch_dq_finalize(fa, dtype, stream)) != 0)
+    return fail(SWA_ERR_HIP, hip_error_string(e));
+  if (end_kv < t_kv) {
+    FillArgs f{dk, static_cast<int64_t>(elem_bytes(dtype)), num_heads * head_dim, end_kv, t_kv,
+               nullptr, nullptr, 0};
+    if ((e = launch_fill(f, stream)) != 0) return fail(SWA_ERR_HIP, hip_error_string(e));
+    f.x = dv;
+    if ((e = launch_fill(f, stream)) != 0) return fail(SWA_ERR_HIP, hip_error_string(e));
+  }
+  return SWA_OK;
+}
+
+swa_status swa_debug_tile_schedule(const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,
+                                   int64_t num_seqs, int64_t t_q, int64_t t_kv,
+                                   int64_t head_dim, int32_t dtype, int64_t pre_tokens,
+                                   int64_t next_tokens, int64_t sparse_mode, int32_t direction,
+                                   int32_t* rows_out, int64_t capacity, int64_t* n_rows,
+                                   int32_t* block_item, int32_t* block_tile) {
+  if (!n_rows || !block_item || !block_tile)
+    return fail(SWA_ERR_NULLPTR, "n_rows / block_item / block_tile is NULL");
+  if (direction != 0 && direction != 1)
+    return fail(SWA_ERR_INVALID, "direction must be 0 (forward) or 1 (backward)");
+  Problem p = make_problem(cu_seqlens_q, cu_seqlens_kv, num_seqs, t_q, t_kv, 1, head_dim, dtype,
+                           1.0, pre_tokens, next_tokens, sparse_mode);
+  std::vector<Seq> seqs;
+  int64_t end_q = 0, end_kv = 0;
+  swa_status s = validate(p, seqs, &end_q, &end_kv);
+  if (s != SWA_OK) return s;
+  std::vector<Item> items;
+  if (direction == 0) {
+    schedule_forward(p, seqs, items);
+    *block_item = FWD_BM;
+    *block_tile = FWD_BN;
+  } else {
+    schedule_backward(p, seqs, items);
+    *block_item = BWD_BN;
+    *block_tile = BWD_BM;
+  }
+  order_items(items);
+  int64_t n = 0;
+  auto emit = [&](int32_t a, int32_t b, int32_t c, int32_t d) {
+    if (rows_out && n < capacity) {
+      rows_out[4 * n + 0] = a;
+      rows_out[4 * n + 1] = b;
+      rows_out[4 * n + 2] = c;
+      rows_out[4 * n + 3] = d;
+    }
+    ++n;
+  };
+  for (const Item& it : items) {
+    const int lo = range_lo(it.tiles), hi = range_hi(it.tiles);
+    const int flo = range_lo(it.full), fhi = range_hi(it.full);
+    if (hi < lo) {
+      emit(it.seq, it.block, -1, 0);
+      continue;
+    }
+    for (int t = lo; t <= hi; ++t) emit(it.seq, it.block, t, (t >= flo && t <= fhi) ? 2 : 1);
+  }
+  *n_rows = n;
+  return SWA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,129 @@
+// Internal declarations shared by the host side (validation, tile schedule,
+// C ABI) and the HIP kernels.  Nothing here is part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace swa {
+
+// Block sizes.  Forward: a work item is one block of FWD_BM query rows of one
+// sequence (one workgroup per item and head); it walks key tiles of FWD_BN.
+// Backward: an item is one block of BWD_BN keys; it walks query tiles of
+// BWD_BM rows.
+constexpr int FWD_BM = 128;
+constexpr int FWD_BN = 64;
+constexpr int BWD_BN = 128;
+constexpr int BWD_BM = 64;
+
+// One schedule entry (32 bytes, uploaded to the workspace).
+//   tiles = lo | hi << 16 : visited tile range [lo, hi] (empty if lo > hi)
+//   full  = flo | fhi << 16 : tiles in [flo, fhi] need no element mask
+struct Item {
+  int32_t q_base;   // first token of the sequence in the query tensor
+  int32_t kv_base;  // first token of the sequence in the key/value tensors
+  int32_t sq;       // query length of the sequence
+  int32_t skv;      // key/value length of the sequence
+  int32_t block;    // item block index inside the sequence
+  int32_t tiles;
+  int32_t full;
+  int32_t seq;      // batch index (diagnostics only)
+};
+static_assert(sizeof(Item) == 32, "Item layout");
+
+inline int32_t pack_range(int64_t lo, int64_t hi) {
+  if (lo > hi) { lo = 1; hi = 0; }
+  return static_cast<int32_t>((lo & 0xffff) | ((hi & 0xffff) << 16));
+}
+
+struct Problem {
+  int64_t num_seqs, t_q, t_kv, num_heads, head_dim;
+  int32_t dtype;
+  double scale;
+  int64_t pre_tokens, next_tokens, sparse_mode;
+  const int64_t* cu_q;
+  const int64_t* cu_kv;
+};
+
+// Kernel arguments.  Element pointers are typeless; the kernels cast.
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  float* smax;
+  float* ssum;
+  const Item* items;
+  int32_t n_items;
+  int32_t num_heads;
+  float scale_log2;  // scale * log2(e)
+  int32_t mode;
+  int32_t pre;       // clamped to +-2^30
+  int32_t next;
+};
+
+struct BwdPreArgs {
+  const void* dy;
+  const void* out;
+  const float* smax;
+  const float* ssum;
+  float* drow;   // [t_q, N] rowsum(dY * out)
+  float* lse2;   // [t_q, N] softmax_max*log2(e) + log2(softmax_sum), +inf if empty
+  float* dq_acc; // [t_q, N, D] zeroed here
+  int64_t rows;  // t_q * N
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dy;
+  const float* drow;
+  const float* lse2;
+  float* dq_acc;
+  void* dk;
+  void* dv;
+  const Item* items;
+  int32_t n_items;
+  int32_t num_heads;
+  float scale;
+  float scale_log2;
+  int32_t mode;
+  int32_t pre;
+  int32_t next;
+};
+
+struct FinalizeArgs {
+  const float* dq_acc;
+  void* dq;
+  float scale;
+  int64_t n;  // elements
+};
+
+// Zero-fill of rows [row0, row1) of a [rows, N, D] tensor and, if smax is
+// given, softmax_max = -inf / softmax_sum = 0 for those rows.
+struct FillArgs {
+  void* x;
+  int64_t elem_bytes;
+  int64_t row_elems;  // N * D
+  int64_t row0, row1;
+  float* smax;
+  float* ssum;
+  int64_t stat_row;   // N * 8
+};
+
+// Launchers (defined in the .hip files).  They return a hipError_t as int.
+int launch_forward(const FwdArgs& a, int dtype, int head_dim, void* stream);
+int launch_bwd_pre(const BwdPreArgs& a, int dtype, int head_dim, void* stream);
+int launch_backward(const BwdArgs& a, int dtype, int head_dim, void* stream);
+int launch_dq_finalize(const FinalizeArgs& a, int dtype, void* stream);
+int launch_fill(const FillArgs& a, void* stream);
+const char* hip_error_string(int err);
+int hip_memcpy_h2d_async(void* dst, const void* src, size_t bytes, void* stream);
+int hip_pinned_alloc(void** p, size_t bytes);
+int hip_pinned_free(void* p);
+int hip_event_create(void** ev);
+int hip_event_record(void* ev, void* stream);
+int hip_event_sync(void* ev);
+
+}  // namespace swa
