@@ -150,6 +150,16 @@ swa_status swa_debug_tile_schedule(const int64_t* cu_seqlens_q, const int64_t* c
                                    int32_t* rows_out, int64_t capacity, int64_t* n_rows,
                                    int32_t* block_item, int32_t* block_tile);
 
+/* Kernel timing (instrumentation for benchmarks).  While enabled, every
+ * kernel the library launches is bracketed by two HIP events recorded on its
+ * stream.  swa_profile_read waits for the recorded launches of one kernel
+ * kind, returns their summed duration (ms) and count, and forgets them.
+ * Kernel kinds: 0 forward, 1 backward preprocess, 2 backward main,
+ * 3 dq finalize, 4 zero fill.  Not thread-safe across concurrent streams
+ * (launches from all threads are pooled). */
+swa_status swa_profile_enable(int32_t enable);
+swa_status swa_profile_read(int32_t kernel, double* total_ms, int64_t* launches);
+
 #ifdef __cplusplus
 }
 #endif

@@ -18,6 +18,7 @@ __all__ = [
     "INT_MAX", "SwaError", "load_library", "library_path",
     "swa_forward_workspace_size", "swa_backward_workspace_size",
     "swa_forward", "swa_backward", "swa_last_error", "swa_debug_tile_schedule",
+    "swa_profile_enable", "swa_profile_read",
     "forward", "backward", "DTYPE_FP32", "DTYPE_BF16", "DTYPE_FP16",
 ]
 
@@ -48,7 +49,11 @@ _SIGNATURES = {
     "swa_last_error": [],
     "swa_debug_tile_schedule": [_i64p, _i64p, _i64, _i64, _i64, _i64, _i32, _i64, _i64, _i64,
                                 _i32, _i32p, _i64, _i64p, _i32p, _i32p],
+    "swa_profile_enable": [_i32],
+    "swa_profile_read": [_i32, ctypes.POINTER(ctypes.c_double), _i64p],
 }
+
+KERNEL_KINDS = {"forward": 0, "bwd_pre": 1, "backward": 2, "dq_finalize": 3, "fill": 4}
 
 
 class SwaError(RuntimeError):
@@ -214,6 +219,19 @@ def swa_debug_tile_schedule(cu_seqlens_q, cu_seqlens_kv, t_q, t_kv, head_dim, dt
                                        ctypes.byref(bt)))
     rows = [tuple(buf[4 * i:4 * i + 4]) for i in range(n.value)]
     return rows, bi.value, bt.value
+
+
+def swa_profile_enable(enable=True):
+    _check(load_library().swa_profile_enable(1 if enable else 0))
+
+
+def swa_profile_read(kernel):
+    """(total_ms, launches) of completed launches of one kernel kind (name or id)."""
+    kid = KERNEL_KINDS[kernel] if isinstance(kernel, str) else int(kernel)
+    ms = ctypes.c_double(0)
+    n = ctypes.c_int64(0)
+    _check(load_library().swa_profile_read(kid, ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
 
 
 def _workspace(nbytes, device):

@@ -28,6 +28,8 @@ def common_flags():
         "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
         # no packed fp32 VALU instructions in device code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # no NaN inputs are assumed: max/min need no NaN-quieting (infinities are kept)
+        "-fno-honor-nans",
         "-Wall", "-Wno-unused-function",
         "-I", os.path.join(ROOT, "include"),
     ]

@@ -13,18 +13,23 @@
 //   lse2 = softmax_max * log2(e) + log2(softmax_sum), so that P = exp2(s*c - lse2)
 //   with c = scale * log2(e); it also zeroes the fp32 dq accumulator.
 // swa_bwd_kernel: one workgroup per (block of 128 keys, head); each of its 4
-//   waves owns 32 keys and keeps K, V (as matrix operands) and its dK, dV
-//   accumulators in registers while it walks the query tiles of the band.
+//   waves owns 32 keys and keeps its dK, dV accumulators in registers while
+//   it walks the query tiles of the band; the K and V blocks stay in LDS.
 //   Scores are formed as S = Q K^T (queries as rows, the wave's keys as
 //   columns), so P and dS come out of the accumulators in the operand layout
-//   of dV^T += dY^T P and dK^T += Q^T dS; Q and dY are staged in LDS both
-//   row-major and transposed.  dS is written to LDS and each wave forms dQ for
-//   one 32-wide head-dim block over all 128 keys, added to the fp32
-//   accumulator with atomics (non-deterministic summation order, as the
-//   explainer section 6.1 describes for the default backward).
+//   of dV^T += dY^T P and dK^T += Q^T dS.  Q and dY tiles go from HBM
+//   straight into swizzled row-major LDS tiles (double-buffered, rows past
+//   the sequence read as zero); the transposed operands Q^T and dY^T come
+//   from them through transposing LDS reads.  dS is written to LDS and each
+//   wave forms dQ for one 32-wide head-dim block over all 128 keys, added to
+//   the fp32 accumulator with atomics
+//   (non-deterministic summation order, as the explainer section 6.1
+//   describes for the default backward).
 // swa_dq_finalize_kernel: dq = scale * dq_acc rounded to the output type.
 
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "swa_common.hpp"
 
@@ -50,45 +55,47 @@ __global__ __launch_bounds__(256) void swa_bwd_pre_kernel(BwdPreArgs a) {
 #pragma unroll
   for (int e = 0; e < EPV; e += 4) *reinterpret_cast<floatx4*>(z + e) = floatx4{0.f, 0.f, 0.f, 0.f};
   if (ch == 0) {
-    a.drow[row] = acc;
+    const int64_t tok = row / a.num_heads, head = row - tok * a.num_heads;
+    const int64_t at = head * a.t_q + tok;  // head-major so that a tile's rows are contiguous
+    a.drow[at] = acc;
     const float mx = a.smax[row * 8], sm = a.ssum[row * 8];
-    a.lse2[row] = (sm > 0.f && mx > -INFINITY) ? mx * 1.4426950408889634f + log2f(sm) : INFINITY;
+    a.lse2[at] = (sm > 0.f && mx > -INFINITY) ? mx * 1.4426950408889634f + log2f(sm) : INFINITY;
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, int BM>
 __global__ __launch_bounds__(256, 1) void swa_bwd_kernel(BwdArgs a) {
   using M = Mfma<T>;
   using op_t = typename M::op_t;
   constexpr int KPL = M::KPL, KSTEP = M::KSTEP;
-  constexpr int BN = BWD_BN, BM = BWD_BM;
-  constexpr int EPV = 16 / sizeof(T);
-  constexpr int CPR = D / EPV;            // 16-byte chunks per row
-  constexpr int QLD = D + EPV;            // row-major Q / dY stage stride
-  constexpr int TLD = BM + EPV;           // transposed Q / dY stage stride
-  constexpr int SLD = BN + EPV;           // dS stage stride
+  constexpr int BN = BWD_BN;
+  constexpr int ES = (int)sizeof(T);
+  constexpr int RB = D * ES;              // Q / dY / K tile row bytes
+  constexpr int QTB = BM * RB;            // Q or dY tile bytes
+  constexpr int KTB = BN * RB;            // K block bytes
+  constexpr int SRB = BN * ES;            // dS tile row bytes
+  constexpr int STB = BM * SRB;           // dS tile bytes
   constexpr int NDB = D / 32;             // head-dim blocks
   constexpr int QB = BM / 32;             // 32-row query blocks per tile
   constexpr int DSTEPS = D / KSTEP;       // contraction steps over d
   constexpr int QSTEPS = 32 / KSTEP;      // contraction steps per 32 query rows
   constexpr int KSTEPS = BN / KSTEP;      // contraction steps over the 128 keys
   constexpr int WPD = 4 / NDB;            // waves sharing one head-dim block in dQ
-  constexpr int TASKS = QB / WPD;         // dQ output blocks per wave
-  constexpr int NV = BM * CPR / 256;      // 16-byte vectors per thread per tensor
-  static_assert(BN == 128 && BM == 64, "kernel assumes 4 waves x 32 keys, 64-row tiles");
-  static_assert(NDB <= 4 && 4 % NDB == 0 && TASKS >= 1, "head-dim split");
-  static_assert(NV >= 1 && BM * CPR % 256 == 0, "tile load mapping");
+  constexpr int TASKS = QB * NDB / 4;     // dQ output blocks per wave
+  static_assert(BN == 128 && (BM == 64 || BM == 32), "4 waves x 32 keys; 32/64-row tiles");
+  static_assert(NDB <= 4 && 4 % NDB == 0 && TASKS >= 1 && QB * NDB % 4 == 0, "dQ split");
 
-  __shared__ __attribute__((aligned(16))) T Qs[BM * QLD];
-  __shared__ __attribute__((aligned(16))) T dYs[BM * QLD];
-  // bf16 also stages Q and dY transposed (8 consecutive query slots per
-  // lane); fp32 reads one element per lane and step from the row-major copy.
-  constexpr bool kTr = sizeof(T) == 2;
-  __shared__ __attribute__((aligned(16))) T Qt[kTr ? D * TLD : 1];
-  __shared__ __attribute__((aligned(16))) T dYt[kTr ? D * TLD : 1];
-  __shared__ __attribute__((aligned(16))) T dSs[BM * SLD];
-  __shared__ __attribute__((aligned(16))) float lse_s[BM];
-  __shared__ __attribute__((aligned(16))) float drow_s[BM];
+  // bf16 reads the B operands of S and dP (K and V rows) from LDS; fp32
+  // (one element per lane and step) keeps them in registers instead.
+  constexpr bool kKVlds = sizeof(T) == 2;
+  __shared__ __attribute__((aligned(1024))) char lds[4 * QTB + (kKVlds ? 2 : 1) * KTB + STB];
+  __shared__ __attribute__((aligned(16))) float lse_s[2][BM];
+  __shared__ __attribute__((aligned(16))) float drow_s[2][BM];
+  char* const qbuf = lds;               // Q tiles [2]
+  char* const ybuf = lds + 2 * QTB;     // dY tiles [2]
+  char* const kblk = lds + 4 * QTB;     // K block (operand of S and of dQ)
+  char* const vblk = kblk + KTB;        // V block (operand of dP)
+  char* const sbuf = kKVlds ? vblk + KTB : vblk;  // dS tile
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, h = lane >> 5, c = lane & 31;
@@ -101,43 +108,26 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kernel(BwdArgs a) {
   const T* dyg = static_cast<const T*>(a.dy) + (int64_t)it.q_base * ld + head * D;
   const T* kg = static_cast<const T*>(a.k) + (int64_t)it.kv_base * ld + head * D;
   const T* vg = static_cast<const T*>(a.v) + (int64_t)it.kv_base * ld + head * D;
+  const float* lse_g = a.lse2 + (int64_t)head * a.t_q + it.q_base;
+  const float* drow_g = a.drow + (int64_t)head * a.t_q + it.q_base;
   const int kb0 = it.block * BN;          // first key of the block (sequence-local)
   const int kw = kb0 + 32 * w + c;        // this lane's key
   const int lo = it.tiles & 0xffff, hi = (it.tiles >> 16) & 0xffff;
   const int flo = it.full & 0xffff, fhi = (it.full >> 16) & 0xffff;
   const float c2 = a.scale_log2;
+  const int wd = w % NDB;                 // head-dim block of this wave's dQ
+  const int ld4 = (int)(ld * 4);          // dq_acc row stride in bytes
+  const int dq_lane_off = (4 * h * (int)ld + 32 * wd + c) * 4;
 
-  // K, V fragments: B operands of S = Q K^T and dP = dY V^T,
-  // lane (column kw) holds K[kw][KSTEP*t + KPL*h + e].
-  op_t kf[DSTEPS], vf[DSTEPS];
-  {
+  // fp32: K, V fragments in registers, lane (column kw) holds K[kw][KSTEP*t + h].
+  op_t kf[kKVlds ? 1 : DSTEPS], vf[kKVlds ? 1 : DSTEPS];
+  if constexpr (!kKVlds) {
     const bool ok = kw < it.skv;
     const int64_t off = (int64_t)(ok ? kw : 0) * ld;
 #pragma unroll
     for (int t = 0; t < DSTEPS; ++t) {
-      kf[t] = M::load(kg + off + KSTEP * t + KPL * h);
-      vf[t] = M::load(vg + off + KSTEP * t + KPL * h);
-      if (!ok) {
-        kf[t] = op_t{};
-        vf[t] = op_t{};
-      }
-    }
-  }
-  // K^T fragments for dQ = dS K: B[k = key slot][j = d], lane (column d of
-  // head-dim block wd) holds K[kb0 + KSTEP*t + KPL*h + e][32*wd + c].
-  const int wd = w % NDB;
-  op_t ktf[KSTEPS];
-#pragma unroll
-  for (int t = 0; t < KSTEPS; ++t) {
-    if constexpr (KPL == 1) {
-      const int key = kb0 + KSTEP * t + h;
-      ktf[t] = key < it.skv ? kg[(int64_t)key * ld + 32 * wd + c] : 0.f;
-    } else {
-#pragma unroll
-      for (int e = 0; e < KPL; ++e) {
-        const int key = kb0 + KSTEP * t + KPL * h + e;
-        ktf[t][e] = key < it.skv ? kg[(int64_t)key * ld + 32 * wd + c] : static_cast<T>(0.f);
-      }
+      kf[t] = ok ? M::load(kg + off + KSTEP * t + KPL * h) : op_t{};
+      vf[t] = ok ? M::load(vg + off + KSTEP * t + KPL * h) : op_t{};
     }
   }
 
@@ -148,83 +138,64 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kernel(BwdArgs a) {
     dv[db] = floatx16{};
   }
 
-  Vec16 qreg[NV], yreg[NV];
+  // Q / dY tiles straight to LDS; lse2 / D rows through registers.
   float sreg = 0.f;
-  auto load_qtile = [&](int tile) {
-#pragma unroll
-    for (int p = 0; p < NV; ++p) {
-      const int vi = tid + 256 * p, row = vi / CPR, ch = vi % CPR;
-      const int i = tile * BM + row;
-      if (i < it.sq) {
-        qreg[p] = load16(qg + (int64_t)i * ld + ch * EPV);
-        yreg[p] = load16(dyg + (int64_t)i * ld + ch * EPV);
-      } else {
-        qreg[p] = zero16();
-        yreg[p] = zero16();
-      }
-    }
+  auto load_qtile = [&](int tile, int b) {
+    const int nvalid = it.sq - tile * BM;
+    tile_load_lds<T, D, BM>(qg + (int64_t)tile * BM * ld, ld, nvalid, qbuf + b * QTB, tid);
+    tile_load_lds<T, D, BM>(dyg + (int64_t)tile * BM * ld, ld, nvalid, ybuf + b * QTB, tid);
     if (tid < 2 * BM) {
       const int row = tid & (BM - 1), i = tile * BM + row;
-      const int64_t idx = ((int64_t)it.q_base + i) * N + head;
       if (tid < BM)
-        sreg = i < it.sq ? a.lse2[idx] : INFINITY;
+        sreg = i < it.sq ? lse_g[i] : INFINITY;
       else
-        sreg = i < it.sq ? a.drow[idx] : 0.f;
+        sreg = i < it.sq ? drow_g[i] : 0.f;
     }
   };
-  auto store_qtile = [&]() {
-#pragma unroll
-    for (int p = 0; p < NV; ++p) {
-      const int vi = tid + 256 * p, row = vi / CPR, ch = vi % CPR;
-      *reinterpret_cast<Vec16*>(&Qs[row * QLD + ch * EPV]) = qreg[p];
-      *reinterpret_cast<Vec16*>(&dYs[row * QLD + ch * EPV]) = yreg[p];
-      if constexpr (kTr) {
-        const int pos = slot_of_row<T>(row);
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) {
-          const int d = ch * EPV + e;
-          Qt[d * TLD + swz(d, pos)] = vec_elem<T>(qreg[p], e);
-          dYt[d * TLD + swz(d, pos)] = vec_elem<T>(yreg[p], e);
-        }
-      }
-    }
+  auto store_rows = [&](int b) {
     if (tid < BM)
-      lse_s[tid] = sreg;
+      lse_s[b][tid] = sreg;
     else if (tid < 2 * BM)
-      drow_s[tid - BM] = sreg;
+      drow_s[b][tid - BM] = sreg;
   };
 
-  if (lo <= hi) {
-    load_qtile(lo);
-    store_qtile();
-  }
-  __syncthreads();
-  for (int tile = lo; tile <= hi; ++tile) {
-    if (tile < hi) load_qtile(tile + 1);
-    const bool need_mask = tile < flo || tile > fhi;
-
-#pragma unroll
+  // Phase A for one query tile: P, dS, dV^T += dY^T P, dK^T += Q^T dS, dS -> LDS.
+  auto phase_a = [&](auto mask_tag, int tile, int b) {
+    constexpr bool kMask = decltype(mask_tag)::value;
+    const char* qt = qbuf + b * QTB;
+    const char* yt = ybuf + b * QTB;
+#pragma unroll 1
     for (int qb = 0; qb < QB; ++qb) {
       floatx16 s = floatx16{}, dp = floatx16{};
 #pragma unroll
       for (int t = 0; t < DSTEPS; ++t) {
-        const op_t qa = M::load(&Qs[(32 * qb + c) * QLD + KSTEP * t + KPL * h]);
-        s = M::mma(qa, kf[t], s);
-        const op_t ya = M::load(&dYs[(32 * qb + c) * QLD + KSTEP * t + KPL * h]);
-        dp = M::mma(ya, vf[t], dp);
+        // A: query rows of Q / dY; B: this lane's key row of K / V (all in LDS)
+        const int off = tile_off<RB>(32 * qb + c, (KSTEP * t + KPL * h) * ES);
+        op_t kb, vb;
+        if constexpr (kKVlds) {
+          const int koff = tile_off<RB>(32 * w + c, (KSTEP * t + KPL * h) * ES);
+          kb = M::load(reinterpret_cast<const T*>(kblk + koff));
+          vb = M::load(reinterpret_cast<const T*>(vblk + koff));
+        } else {
+          kb = kf[t];
+          vb = vf[t];
+        }
+        s = M::mma(M::load(reinterpret_cast<const T*>(qt + off)), kb, s);
+        dp = M::mma(M::load(reinterpret_cast<const T*>(yt + off)), vb, dp);
       }
+      if constexpr (kKVlds) interleave_lds_mfma<2 * DSTEPS, 2, 2>();
       // rows of this lane: 32*qb + c_row(r, h); P = exp2(s*c - lse2), dS = P (dP - D)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int rb = 32 * qb + 8 * g + 4 * h;
-        const floatx4 l4 = *reinterpret_cast<const floatx4*>(&lse_s[rb]);
-        const floatx4 d4 = *reinterpret_cast<const floatx4*>(&drow_s[rb]);
+        const floatx4 l4 = *reinterpret_cast<const floatx4*>(&lse_s[b][rb]);
+        const floatx4 d4 = *reinterpret_cast<const floatx4*>(&drow_s[b][rb]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g + e;
-          float p = __builtin_amdgcn_exp2f(s[r] * c2 - l4[e]);
-          if (need_mask && !allowed(tile * BM + rb + e, kw, it.sq, it.skv, a.mode, a.pre, a.next))
-            p = 0.f;
+          float p = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -l4[e]));
+          if constexpr (kMask)
+            p = allowed(tile * BM + rb + e, kw, it.sq, it.skv, a.mode, a.pre, a.next) ? p : 0.f;
           s[r] = p;
           dp[r] = p * (dp[r] - d4[e]);
         }
@@ -236,45 +207,94 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kernel(BwdArgs a) {
         const op_t sb = M::pack(dp, t2);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const int d = 32 * db + c;
-          const int slot = 32 * qb + KSTEP * t2 + KPL * h;
           op_t ya, qa;
-          if constexpr (kTr) {
-            ya = M::load(&dYt[d * TLD + swz(d, slot)]);
-            qa = M::load(&Qt[d * TLD + swz(d, slot)]);
+          if constexpr (sizeof(T) == 2) {
+            ya = tr_operand<RB, true>(yt, 32 * qb + KSTEP * t2, db, lane);
+            qa = tr_operand<RB, true>(qt, 32 * qb + KSTEP * t2, db, lane);
           } else {
-            ya = M::load(&dYs[row_of_slot<T>(slot) * QLD + d]);
-            qa = M::load(&Qs[row_of_slot<T>(slot) * QLD + d]);
+            const int row = 32 * qb + row_of_slot<T>(KSTEP * t2 + KPL * h);
+            const int off = tile_off<RB>(row, (32 * db + c) * ES);
+            ya = *reinterpret_cast<const T*>(yt + off);
+            qa = *reinterpret_cast<const T*>(qt + off);
           }
           dv[db] = M::mma(ya, pb, dv[db]);
           dk[db] = M::mma(qa, sb, dk[db]);
         }
       }
       // dS (rounded to the input type) for the dQ product
+      if constexpr (sizeof(T) == 2) {
+        // Adjacent lanes hold adjacent keys of the same rows: swap one value
+        // with the neighbour lane so that each lane stores a pair of keys of
+        // one row as a single 32-bit word (even lanes rows r, odd lanes r+1).
+        const bool odd = c & 1;
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        dSs[(32 * qb + c_row(r, h)) * SLD + 32 * w + c] = static_cast<T>(dp[r]);
+        for (int r = 0; r < 16; r += 2) {
+          const uint32_t mine_r = __builtin_bit_cast(uint16_t, static_cast<T>(dp[r]));
+          const uint32_t mine_r1 = __builtin_bit_cast(uint16_t, static_cast<T>(dp[r + 1]));
+          const uint32_t give = odd ? mine_r : mine_r1;
+          const uint32_t got = __builtin_amdgcn_mov_dpp((int)give, 0xB1, 0xF, 0xF, false);
+          const uint32_t word = odd ? (got | (mine_r1 << 16)) : (mine_r | (got << 16));
+          const int row = 32 * qb + c_row(odd ? r + 1 : r, h);
+          *reinterpret_cast<uint32_t*>(sbuf + tile_off<SRB>(row, (32 * w + (c & ~1)) * ES)) = word;
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          *reinterpret_cast<T*>(sbuf + tile_off<SRB>(32 * qb + c_row(r, h), (32 * w + c) * ES)) =
+              static_cast<T>(dp[r]);
+      }
     }
+  };
+
+  if (lo <= hi) {
+    tile_load_lds<T, D, BN>(kg + (int64_t)kb0 * ld, ld, it.skv - kb0, kblk, tid);
+    if constexpr (kKVlds) tile_load_lds<T, D, BN>(vg + (int64_t)kb0 * ld, ld, it.skv - kb0, vblk, tid);
+    load_qtile(lo, 0);
+    store_rows(0);
+    wait_vmem();
+    __syncthreads();
+  }
+  for (int tile = lo; tile <= hi; ++tile) {
+    const int b = (tile - lo) & 1;
+    if (tile < hi) load_qtile(tile + 1, b ^ 1);
+    if (tile < flo || tile > fhi)
+      phase_a(std::true_type{}, tile, b);
+    else
+      phase_a(std::false_type{}, tile, b);
     __syncthreads();
 
     // dQ[32 rows x 32 d] = dS[rows, 128 keys] K[128 keys, d-block wd]
+    const int nrows = it.sq - tile * BM < BM ? it.sq - tile * BM : BM;
+    const bool full_rows = nrows == BM;
+    const __amdgpu_buffer_rsrc_t dq_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        a.dq_acc + ((int64_t)it.q_base + tile * BM) * ld + head * D, (short)0,
+        (int)(((int64_t)(nrows - 1) * ld + D) * 4), 0x00020000);
 #pragma unroll
     for (int k = 0; k < TASKS; ++k) {
       const int qb = w / NDB + k * WPD;
       floatx16 acc = floatx16{};
 #pragma unroll
       for (int t = 0; t < KSTEPS; ++t) {
-        const op_t sa = M::load(&dSs[(32 * qb + c) * SLD + KSTEP * t + KPL * h]);
-        acc = M::mma(sa, ktf[t], acc);
+        const op_t sa = M::load(reinterpret_cast<const T*>(
+            sbuf + tile_off<SRB>(32 * qb + c, (KSTEP * t + KPL * h) * ES)));
+        op_t kb;
+        if constexpr (sizeof(T) == 2)
+          kb = tr_operand<RB, false>(kblk, KSTEP * t, wd, lane);
+        else
+          kb = *reinterpret_cast<const T*>(kblk + tile_off<RB>(KSTEP * t + h, (32 * wd + c) * ES));
+        acc = M::mma(sa, kb, acc);
       }
+      // buffer atomics: wave-uniform row offset in an SGPR, one lane offset
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int i = tile * BM + 32 * qb + c_row(r, h);
-        if (i < it.sq)
-          unsafeAtomicAdd(a.dq_acc + ((int64_t)it.q_base + i) * ld + head * D + 32 * wd + c, acc[r]);
+        const int soff = (32 * qb + 8 * (r >> 2) + (r & 3)) * ld4;
+        if (full_rows || i < it.sq)
+          __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[r], dq_rsrc, dq_lane_off, soff, 0);
       }
     }
-    if (tile < hi) store_qtile();
+    if (tile < hi) store_rows(b ^ 1);
+    wait_vmem();
     __syncthreads();
   }
 
@@ -369,7 +389,8 @@ int launch_bwd_pre(const BwdPreArgs& a, int dtype, int head_dim, void* stream) {
 template <typename T, int D>
 static int launch_bwd_t(const BwdArgs& a, void* stream) {
   const int64_t nwg = (int64_t)a.n_items * a.num_heads;
-  hipLaunchKernelGGL((swa_bwd_kernel<T, D>), dim3((unsigned)nwg), dim3(256), 0,
+  constexpr int BM = bwd_block_q(sizeof(T) == 2 ? 1 : 0, D);
+  hipLaunchKernelGGL((swa_bwd_kernel<T, D, BM>), dim3((unsigned)nwg), dim3(256), 0,
                      static_cast<hipStream_t>(stream), a);
   return (int)hipGetLastError();
 }
@@ -418,5 +439,12 @@ int hip_event_record(void* ev, void* stream) {
   return (int)hipEventRecord(static_cast<hipEvent_t>(ev), static_cast<hipStream_t>(stream));
 }
 int hip_event_sync(void* ev) { return (int)hipEventSynchronize(static_cast<hipEvent_t>(ev)); }
+int hip_event_create_timed(void** ev) {
+  return (int)hipEventCreate(reinterpret_cast<hipEvent_t*>(ev));
+}
+int hip_event_elapsed_ms(float* ms, void* start, void* stop) {
+  return (int)hipEventElapsedTime(ms, static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(stop));
+}
+int hip_event_destroy(void* ev) { return (int)hipEventDestroy(static_cast<hipEvent_t>(ev)); }
 
 }  // namespace swa

@@ -86,6 +86,125 @@ __device__ __host__ constexpr inline int row_of_slot(int p) {
 // the transposing writes of consecutive 8-wide d chunks over distinct banks.
 __device__ inline int swz(int d, int pos) { return pos ^ (((d >> 3) & 7) << 3); }
 
+// Swizzled row-major LDS tiles.  Rows are stored back to back with no
+// padding; the 16-byte chunk c of row r sits at chunk c ^ tile_swz(r).  The
+// permutation keeps 8 consecutive rows reading one logical chunk (a 128-bit
+// operand read) on 8 distinct bank groups, and 4 consecutive rows reading one
+// aligned 32-byte pair (a transposing 64-bit read) on 4 distinct bank groups.
+__device__ __host__ constexpr inline int tile_swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+template <int RB>
+__device__ __host__ constexpr inline int tile_off(int r, int byte) {
+  return r * RB + ((((byte >> 4) ^ tile_swz(r)) << 4) | (byte & 15));
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor (stride 0, byte range nbytes) for the bounds-checked
+// direct global->LDS loads; reads past nbytes return zeros.
+__device__ inline u32x4 buffer_rsrc(const void* base, uint32_t nbytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  u32x4 r = {(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, nbytes, 0x00020000u};
+  r.x = __builtin_amdgcn_readfirstlane(r.x);
+  r.y = __builtin_amdgcn_readfirstlane(r.y);
+  r.z = __builtin_amdgcn_readfirstlane(r.z);
+  r.w = __builtin_amdgcn_readfirstlane(r.w);
+  return r;
+}
+
+__device__ inline uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)((const lds_void*)(p));
+}
+
+// 16 bytes per lane from rsrc + voff into LDS at lds_base + 16 * lane.  The
+// copy is issued as inline assembly so that the compiler does not treat it
+// as an LDS store (it would otherwise wait for it before every later LDS
+// read, even of other buffers); the caller waits with wait_vmem() and
+// synchronises before the destination is read.
+__device__ inline void dma16(u32x4 rsrc, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_base), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
+// Copy rows [0, ROWS) of a row-major [rows, ld] slice starting at `base`
+// into a swizzled LDS tile (no registers involved).  Rows >= nvalid read as
+// zero.  All 256 threads of the workgroup take part.
+template <typename T, int D, int ROWS>
+__device__ inline void tile_load_lds(const T* base, int64_t ld, int nvalid, char* tile, int tid) {
+  constexpr int RB = D * (int)sizeof(T);
+  constexpr int CPR = RB / 16;
+  constexpr int SLOTS = ROWS * CPR;
+  static_assert(SLOTS % 256 == 0, "tile load mapping");
+  const int64_t row_bytes = ld * (int64_t)sizeof(T);
+  nvalid = nvalid < ROWS ? nvalid : ROWS;
+  const uint32_t nrec = nvalid > 0 ? (uint32_t)((nvalid - 1) * row_bytes + RB) : 0u;
+  const u32x4 rsrc = buffer_rsrc(base, nrec);
+  const uint32_t tbase = lds_addr(tile);
+#pragma unroll
+  for (int p = 0; p < SLOTS / 256; ++p) {
+    const int sl = p * 256 + tid;
+    const int row = sl / CPR, pc = sl % CPR;
+    const uint32_t voff = (uint32_t)(row * row_bytes) + (uint32_t)((pc ^ tile_swz(row)) << 4);
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(tbase + (p * 256 + (tid & ~63)) * 16);
+    dma16(rsrc, voff, dst);
+  }
+}
+
+// Contiguous copy of `bytes` (a multiple of 16, at most 1024) into LDS by the
+// first bytes/16 lanes of wave 0; bytes past `valid_bytes` read as zero.
+__device__ inline void span_load_lds(const void* base, uint32_t valid_bytes, int bytes, char* dst,
+                                     int tid) {
+  if (tid < bytes / 16) {
+    const u32x4 rsrc = buffer_rsrc(base, valid_bytes);
+    dma16(rsrc, tid * 16, __builtin_amdgcn_readfirstlane(lds_addr(dst)));
+  }
+}
+
+// Wait for this wave's outstanding vector-memory operations (vmcnt = 0).
+__device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Transposing 64-bit LDS read (ds_read_b64_tr_b16): within each group of 16
+// lanes, lane j receives element (j & 3) of the 4-element chunks addressed by
+// lanes (j >> 2), 4 + (j >> 2), 8 + (j >> 2), 12 + (j >> 2).
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+__device__ inline shortx4 lds_read_tr16(const char* p) {
+  typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(p));
+}
+
+// bf16 operand (8 values) of lane l read from a swizzled row-major [rows, D]
+// bf16 tile at column 32*db + (l & 31).  Element e (contraction slot
+// 8*(l>>5) + e of the step starting at row0) is the tile row
+//   kRho:  row0 + 8*(e>>2) + 4*(l>>5) + (e&3)   (accumulator row order)
+//   else:  row0 + 8*(l>>5) + e                  (natural order)
+template <int RB, bool kRho>
+__device__ inline bf16x8 tr_operand(const char* tile, int row0, int db, int lane) {
+  const int s = lane & 15, h = lane >> 5;
+  const int col = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (s & 3);
+  const int r = row0 + (kRho ? 4 : 8) * h + (s >> 2);
+  const int r2 = r + (kRho ? 8 : 4);
+  const shortx4 lo = lds_read_tr16(tile + tile_off<RB>(r, 2 * col));
+  const shortx4 hi = lds_read_tr16(tile + tile_off<RB>(r2, 2 * col));
+  typedef short shortx8 __attribute__((ext_vector_type(8)));
+  const shortx8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Scheduling hints: ask the machine scheduler to interleave LDS reads with
+// matrix instructions so that operands are fetched `ahead` instructions
+// before their use (masks: 0x008 MFMA, 0x100 LDS read, 0x002 VALU).
+template <int NMFMA, int READS_PER, int AHEAD>
+__device__ inline void interleave_lds_mfma() {
+  __builtin_amdgcn_sched_group_barrier(0x100, READS_PER * AHEAD, 0);
+#pragma unroll
+  for (int i = 0; i < NMFMA; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (i + AHEAD < NMFMA) __builtin_amdgcn_sched_group_barrier(0x100, READS_PER, 0);
+  }
+}
+
 // 16-byte vector of elements.
 struct alignas(16) Vec16 {
   uint32_t w[4];

@@ -4,48 +4,60 @@
 // Math (FlashAttentionVarLenScore API doc, "计算公式"; PyPTO-Gym
 // FlashAttentionScoreGrad article, "前向公式"): out = softmax(mask(scale Q K^T)) V,
 // with softmax_max / softmax_sum saved per row.  The blockwise (online)
-// softmax keeps a running max m and running sum l per row and rescales the
-// output accumulator when m grows, so the full score matrix never exists.
+// softmax keeps a running max and running sum per row, so the full score
+// matrix never exists.
 //
 // Workgroup: 4 wavefronts x 32 query rows.  Each wave keeps its Q rows in
 // registers and computes the transposed score block S^T = K Q^T (keys as
 // rows, its 32 queries as columns), so that a lane owns one query row: the
 // row max and row sum are in-lane reductions plus one swap of lane halves.
-// The probabilities P^T are rounded to the input type and reused directly
-// from the accumulator registers as the B operand of O^T += V^T P^T; V is
-// staged transposed in LDS with its keys at the matching slot positions.
-// K (row-major) and V^T tiles are double-buffered in LDS; the next tile's
-// global loads are issued before the current tile's math.
+// The probabilities are rounded to the input type and fed straight from the
+// accumulator registers as the B operand of O^T += V^T P^T.
+//
+// Data movement: K and V tiles of 64 keys go from HBM straight into
+// swizzled row-major LDS tiles (buffer loads with the LDS destination, rows
+// past the sequence read as zero), double-buffered.  V^T operands come from
+// the row-major V tile through transposing LDS reads.  The copies of the
+// next tiles are in flight while the current one is computed.
+//
+// Rescaling: the exponent reference of a row is only moved when the running
+// max exceeds it by more than 2^8 (in exp2 units); exp values then stay below
+// 256, and the true max is tracked separately for softmax_max, with
+// softmax_sum converted to it at the end.  The result is the same softmax.
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "swa_common.hpp"
+
+// 1: the score block of tile t+1 is formed before the softmax of tile t, so
+// each wave has independent matrix work during its softmax (one wave per
+// SIMD, up to 512 registers); 0: plain double buffering, two waves per SIMD.
+#ifndef SWA_FWD_PIPELINE
+#define SWA_FWD_PIPELINE 0
+#endif
 
 namespace swa {
 
-template <typename T, int D>
-__global__ __launch_bounds__(256, 2) void swa_fwd_kernel(FwdArgs a) {
+template <typename T, int D, bool kPos>
+__global__ __launch_bounds__(256, SWA_FWD_PIPELINE ? 1 : 2) void swa_fwd_kernel(FwdArgs a) {
   using M = Mfma<T>;
   using op_t = typename M::op_t;
   constexpr int KPL = M::KPL, KSTEP = M::KSTEP;
   constexpr int BM = FWD_BM, BN = FWD_BN;
-  constexpr int EPV = 16 / sizeof(T);     // elements per 16-byte vector
-  constexpr int CPR = D / EPV;            // 16-byte chunks per row
-  constexpr int KLD = D + EPV;            // K tile row stride (16-byte pad)
-  constexpr int VLD = BN + EPV;           // V^T tile row stride
+  constexpr int RB = D * (int)sizeof(T);  // tile row bytes
+  constexpr int TB = BN * RB;             // tile bytes
   constexpr int NDB = D / 32;             // 32-wide head-dim blocks
   constexpr int NJB = BN / 32;            // 32-key blocks per tile
   constexpr int QSTEPS = D / KSTEP;       // contraction steps over d
   constexpr int PSTEPS = 32 / KSTEP;      // contraction steps per 32 keys
-  constexpr int NV = BN * CPR / 256;      // 16-byte vectors per thread per tensor
+  constexpr float kRescale = 8.f;         // exp2-domain slack before moving the reference
   static_assert(BM == 128 && BN == 64, "kernel assumes 4 waves x 32 rows and 64-key tiles");
-  static_assert(NV >= 1 && BN * CPR % 256 == 0, "tile load mapping");
 
-  // bf16 stages V transposed (each lane reads 8 consecutive keys); fp32 reads
-  // one element per lane and step, so it keeps V row-major.
-  constexpr bool kVt = sizeof(T) == 2;
-  __shared__ __attribute__((aligned(16))) T Ks[2][BN * KLD];
-  __shared__ __attribute__((aligned(16))) T Vt[2][kVt ? D * VLD : BN * KLD];
+  __shared__ __attribute__((aligned(1024))) char lds[4 * TB];  // K0 K1 V0 V1
+  char* const kbuf0 = lds;
+  char* const vbuf0 = lds + 2 * TB;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, h = lane >> 5, c = lane & 31;
@@ -59,7 +71,7 @@ __global__ __launch_bounds__(256, 2) void swa_fwd_kernel(FwdArgs a) {
   const int qrow = it.block * BM + 32 * w + c;  // this lane's query row (sequence-local)
   const int lo = it.tiles & 0xffff, hi = (it.tiles >> 16) & 0xffff;
   const int flo = it.full & 0xffff, fhi = (it.full >> 16) & 0xffff;
-  const float c2 = a.scale_log2;
+  const float cs = kPos ? a.scale_log2 : 1.f;  // raw score -> exp2 units
 
   // Q fragments: B operand of S^T = K Q^T, lane (column qrow) holds
   // Q[qrow][KSTEP*t + KPL*h + e].
@@ -74,35 +86,22 @@ __global__ __launch_bounds__(256, 2) void swa_fwd_kernel(FwdArgs a) {
     }
   }
 
-  Vec16 kreg[NV], vreg[NV];
-  auto load_tile = [&](int tile) {
-#pragma unroll
-    for (int p = 0; p < NV; ++p) {
-      const int vi = tid + 256 * p, key = vi / CPR, ch = vi % CPR;
-      const int j = tile * BN + key;
-      if (j < it.skv) {
-        kreg[p] = load16(kg + (int64_t)j * ld + ch * EPV);
-        vreg[p] = load16(vg + (int64_t)j * ld + ch * EPV);
-      } else {
-        kreg[p] = zero16();
-        vreg[p] = zero16();
-      }
-    }
+  auto load_k = [&](int tile, int b) {
+    tile_load_lds<T, D, BN>(kg + (int64_t)tile * BN * ld, ld, it.skv - tile * BN, kbuf0 + b * TB, tid);
   };
-  auto store_tile = [&](int buf) {
+  auto load_v = [&](int tile, int b) {
+    tile_load_lds<T, D, BN>(vg + (int64_t)tile * BN * ld, ld, it.skv - tile * BN, vbuf0 + b * TB, tid);
+  };
+  // S^T block jb: rows = keys 32*jb + c_row(r, h), column = this lane's query
+  auto scores = [&](const char* kt, floatx16* s) {
 #pragma unroll
-    for (int p = 0; p < NV; ++p) {
-      const int vi = tid + 256 * p, key = vi / CPR, ch = vi % CPR;
-      *reinterpret_cast<Vec16*>(&Ks[buf][key * KLD + ch * EPV]) = kreg[p];
-      if constexpr (kVt) {
-        const int pos = slot_of_row<T>(key);
+    for (int jb = 0; jb < NJB; ++jb) {
+      s[jb] = floatx16{};
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) {
-          const int d = ch * EPV + e;
-          Vt[buf][d * VLD + swz(d, pos)] = vec_elem<T>(vreg[p], e);
-        }
-      } else {
-        *reinterpret_cast<Vec16*>(&Vt[buf][key * KLD + ch * EPV]) = vreg[p];
+      for (int t = 0; t < QSTEPS; ++t) {
+        const op_t ka = M::load(reinterpret_cast<const T*>(
+            kt + tile_off<RB>(32 * jb + c, (KSTEP * t + KPL * h) * (int)sizeof(T))));
+        s[jb] = M::mma(ka, qf[t], s[jb]);
       }
     }
   };
@@ -110,94 +109,129 @@ __global__ __launch_bounds__(256, 2) void swa_fwd_kernel(FwdArgs a) {
   floatx16 o[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) o[db] = floatx16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_true = -INFINITY;  // running max of the raw (masked) scores
+  float m_ref = -INFINITY;   // exponent reference, raw units
+  float l_run = 0.f;         // running sum relative to m_ref (this lane's half)
+
+  // Softmax of one tile (in place: scores -> probabilities) and P V.
+  auto tile_math = [&](auto mask_tag, int tile, floatx16* s, const char* vt) {
+    constexpr bool kMask = decltype(mask_tag)::value;
+    if constexpr (!kPos) {  // non-positive scale: work on scaled scores (scale before masking)
+#pragma unroll
+      for (int jb = 0; jb < NJB; ++jb) s[jb] *= a.scale_log2;
+    }
+    if constexpr (kMask) {
+#pragma unroll
+      for (int jb = 0; jb < NJB; ++jb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = tile * BN + 32 * jb + c_row(r, h);
+          s[jb][r] = allowed(qrow, j, it.sq, it.skv, a.mode, a.pre, a.next) ? s[jb][r] : -INFINITY;
+        }
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int jb = 0; jb < NJB; ++jb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[jb][r]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    m_true = fmaxf(m_true, mx);
+    if (__ballot((m_true - m_ref) * cs > kRescale)) {
+      const float alpha = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_ref - m_true) * cs);
+      m_ref = m_true;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+    }
+    const float moff = m_ref == -INFINITY ? 0.f : -m_ref * cs;
+    float lsum = 0.f;
+#pragma unroll
+    for (int jb = 0; jb < NJB; ++jb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[jb][r], cs, moff));
+        s[jb][r] = p;
+        lsum += p;
+      }
+    }
+    l_run += lsum;
+    // O^T[db] += V^T P^T
+#pragma unroll
+    for (int jb = 0; jb < NJB; ++jb) {
+#pragma unroll
+      for (int t2 = 0; t2 < PSTEPS; ++t2) {
+        const op_t pb = M::pack(s[jb], t2);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          op_t va;
+          if constexpr (sizeof(T) == 2) {
+            va = tr_operand<RB, true>(vt, 32 * jb + KSTEP * t2, db, lane);
+          } else {
+            const int row = 32 * jb + row_of_slot<T>(KSTEP * t2 + KPL * h);
+            va = *reinterpret_cast<const T*>(vt + tile_off<RB>(row, (32 * db + c) * (int)sizeof(T)));
+          }
+          o[db] = M::mma(va, pb, o[db]);
+        }
+      }
+    }
+  };
 
   if (lo <= hi) {
-    load_tile(lo);
-    store_tile(0);
+#if SWA_FWD_PIPELINE
+    load_k(lo, 0);
+    load_v(lo, 0);
+    if (lo < hi) load_k(lo + 1, 1);
+    wait_vmem();
+    __syncthreads();
+    floatx16 s_cur[NJB];
+    scores(kbuf0, s_cur);
+    __syncthreads();  // every wave has read K(lo) before K(lo + 2) overwrites it
+    for (int tile = lo; tile <= hi; ++tile) {
+      const int b = (tile - lo) & 1;
+      // K(tile + 1) is in kbuf[b ^ 1], V(tile) in vbuf[b]; refill the others
+      if (tile + 1 <= hi) load_v(tile + 1, b ^ 1);
+      if (tile + 2 <= hi) load_k(tile + 2, b);
+      floatx16 s_nxt[NJB];
+      if (tile < hi) scores(kbuf0 + (b ^ 1) * TB, s_nxt);
+      if (tile < flo || tile > fhi)
+        tile_math(std::true_type{}, tile, s_cur, vbuf0 + b * TB);
+      else
+        tile_math(std::false_type{}, tile, s_cur, vbuf0 + b * TB);
+      wait_vmem();
+      __syncthreads();
+#pragma unroll
+      for (int jb = 0; jb < NJB; ++jb) s_cur[jb] = s_nxt[jb];
+    }
+#else
+    load_k(lo, 0);
+    load_v(lo, 0);
+    wait_vmem();
     __syncthreads();
     for (int tile = lo; tile <= hi; ++tile) {
-      const int buf = (tile - lo) & 1;
-      if (tile < hi) load_tile(tile + 1);
-
-      // S^T block jb: rows = keys 32*jb + c_row(r, h), column = this lane's query
+      const int b = (tile - lo) & 1;
+      // K(tile), V(tile) in buffer b; tile + 1 goes to the other buffer
+      if (tile + 1 <= hi) {
+        load_k(tile + 1, b ^ 1);
+        load_v(tile + 1, b ^ 1);
+      }
       floatx16 s[NJB];
-#pragma unroll
-      for (int jb = 0; jb < NJB; ++jb) {
-        s[jb] = floatx16{};
-#pragma unroll
-        for (int t = 0; t < QSTEPS; ++t) {
-          const op_t ka = M::load(&Ks[buf][(32 * jb + c) * KLD + KSTEP * t + KPL * h]);
-          s[jb] = M::mma(ka, qf[t], s[jb]);
-        }
-      }
-
-      // scale into log2 units, mask partial tiles, running max
-      const bool need_mask = tile < flo || tile > fhi;
-      float mx = -INFINITY;
-#pragma unroll
-      for (int jb = 0; jb < NJB; ++jb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = s[jb][r] * c2;
-          if (need_mask) {
-            const int j = tile * BN + 32 * jb + c_row(r, h);
-            if (!allowed(qrow, j, it.sq, it.skv, a.mode, a.pre, a.next)) x = -INFINITY;
-          }
-          s[jb][r] = x;
-          mx = fmaxf(mx, x);
-        }
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      float lsum = 0.f;
-#pragma unroll
-      for (int jb = 0; jb < NJB; ++jb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(s[jb][r] - m_use);
-          s[jb][r] = p;
-          lsum += p;
-        }
-      }
-      l_run = l_run * alpha + lsum;
-      if (__ballot(alpha != 1.f)) {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) o[db] *= alpha;
-      }
-      m_run = m_new;
-
-      // O^T[db] += V^T P^T
-#pragma unroll
-      for (int jb = 0; jb < NJB; ++jb) {
-#pragma unroll
-        for (int t2 = 0; t2 < PSTEPS; ++t2) {
-          const op_t pb = M::pack(s[jb], t2);
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const int d = 32 * db + c;
-            const int pos = 32 * jb + KSTEP * t2 + KPL * h;
-            op_t va;
-            if constexpr (kVt)
-              va = M::load(&Vt[buf][d * VLD + swz(d, pos)]);
-            else
-              va = M::load(&Vt[buf][row_of_slot<T>(pos) * KLD + d]);
-            o[db] = M::mma(va, pb, o[db]);
-          }
-        }
-      }
-
-      if (tile < hi) store_tile(buf ^ 1);
+      scores(kbuf0 + b * TB, s);
+      if (tile < flo || tile > fhi)
+        tile_math(std::true_type{}, tile, s, vbuf0 + b * TB);
+      else
+        tile_math(std::false_type{}, tile, s, vbuf0 + b * TB);
+      wait_vmem();
       __syncthreads();
     }
+#endif
   }
 
   // epilogue: normalise, store out and the statistics of this lane's row
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_ref = l_run + __shfl_xor(l_run, 32);
   if (qrow < it.sq) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float inv = l_ref > 0.f ? 1.f / l_ref : 0.f;
     const int64_t tok = (int64_t)it.q_base + qrow;
     T* op = static_cast<T*>(a.out) + tok * ld + head * D;
 #pragma unroll
@@ -218,9 +252,12 @@ __global__ __launch_bounds__(256, 2) void swa_fwd_kernel(FwdArgs a) {
         }
       }
     }
-    const float smax = (m_run == -INFINITY) ? -INFINITY : m_run * 0.69314718055994531f;
+    // statistics in natural units relative to the true max
+    const bool empty = m_true == -INFINITY;
+    const float smax = empty ? -INFINITY : m_true * cs * 0.69314718055994531f;
+    const float ssum = empty ? 0.f : l_ref * __builtin_amdgcn_exp2f((m_ref - m_true) * cs);
     const floatx4 mv = {smax, smax, smax, smax};
-    const floatx4 sv = {l_tot, l_tot, l_tot, l_tot};
+    const floatx4 sv = {ssum, ssum, ssum, ssum};
     const int64_t so = (tok * a.num_heads + head) * 8 + 4 * h;
     *reinterpret_cast<floatx4*>(a.smax + so) = mv;
     *reinterpret_cast<floatx4*>(a.ssum + so) = sv;
@@ -230,8 +267,12 @@ __global__ __launch_bounds__(256, 2) void swa_fwd_kernel(FwdArgs a) {
 template <typename T, int D>
 static int launch_fwd_t(const FwdArgs& a, void* stream) {
   const int64_t nwg = (int64_t)a.n_items * a.num_heads;
-  hipLaunchKernelGGL((swa_fwd_kernel<T, D>), dim3((unsigned)nwg), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), a);
+  if (a.scale_log2 > 0.f)
+    hipLaunchKernelGGL((swa_fwd_kernel<T, D, true>), dim3((unsigned)nwg), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), a);
+  else
+    hipLaunchKernelGGL((swa_fwd_kernel<T, D, false>), dim3((unsigned)nwg), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), a);
   return (int)hipGetLastError();
 }
 

@@ -195,11 +195,12 @@ void schedule_forward(const Problem& p, const std::vector<Seq>& seqs, std::vecto
   }
 }
 
-// Backward schedule: one item per block of BWD_BN keys; query tiles of BWD_BM.
+// Backward schedule: one item per block of BWD_BN keys; query tiles of
+// bwd_block_q(dtype, head_dim) rows.
 void schedule_backward(const Problem& p, const std::vector<Seq>& seqs,
                        std::vector<Item>& items) {
   items.clear();
-  const int64_t BN = BWD_BN, BM = BWD_BM;
+  const int64_t BN = BWD_BN, BM = bwd_block_q(p.dtype, static_cast<int>(p.head_dim));
   for (const Seq& s : seqs) {
     if (s.skv == 0) continue;
     const int64_t nkb = ceil_div(s.skv, BN);
@@ -322,6 +323,55 @@ Problem make_problem(const int64_t* cu_q, const int64_t* cu_kv, int64_t num_seqs
 
 size_t elem_bytes(int32_t dtype) { return dtype == SWA_DTYPE_FP32 ? 4 : 2; }
 
+// Optional per-kernel timing with HIP events (swa_profile_enable/read).
+enum KernelKind { K_FWD = 0, K_BWD_PRE = 1, K_BWD = 2, K_DQ_FIN = 3, K_FILL = 4, K_KINDS = 5 };
+struct Profiler {
+  std::mutex mu;
+  bool on = false;
+  struct Rec {
+    int kind;
+    void* start;
+    void* stop;
+  };
+  std::vector<Rec> recs;
+  std::vector<void*> pool;
+};
+Profiler g_prof;
+
+void* prof_event() {
+  void* ev = nullptr;
+  if (!g_prof.pool.empty()) {
+    ev = g_prof.pool.back();
+    g_prof.pool.pop_back();
+  } else if (hip_event_create_timed(&ev) != 0) {
+    ev = nullptr;
+  }
+  return ev;
+}
+
+// Launch `fn` and, if timing is on, bracket it with events on `stream`.
+template <typename F>
+int timed_launch(int kind, void* stream, F&& fn) {
+  bool on;
+  {
+    std::lock_guard<std::mutex> lock(g_prof.mu);
+    on = g_prof.on;
+  }
+  if (!on) return fn();
+  void *a = nullptr, *b = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_prof.mu);
+    a = prof_event();
+    b = prof_event();
+  }
+  if (a) hip_event_record(a, stream);
+  const int e = fn();
+  if (b) hip_event_record(b, stream);
+  std::lock_guard<std::mutex> lock(g_prof.mu);
+  if (a && b) g_prof.recs.push_back(Profiler::Rec{kind, a, b});
+  return e;
+}
+
 }  // namespace
 }  // namespace swa
 
@@ -377,7 +427,8 @@ swa_status swa_forward(const void* q, const void* k, const void* v, const int64_
   if (end_q < t_q) {
     FillArgs f{out, static_cast<int64_t>(elem_bytes(dtype)), num_heads * head_dim, end_q, t_q,
                softmax_max, softmax_sum, num_heads * 8};
-    if ((e = launch_fill(f, stream)) != 0) return fail(SWA_ERR_HIP, hip_error_string(e));
+    if ((e = timed_launch(K_FILL, stream, [&] { return launch_fill(f, stream); })) != 0)
+      return fail(SWA_ERR_HIP, hip_error_string(e));
   }
   if (!items.empty()) {
     FwdArgs a;
@@ -394,7 +445,9 @@ swa_status swa_forward(const void* q, const void* k, const void* v, const int64_
     a.mode = static_cast<int32_t>(sparse_mode);
     a.pre = clamp_window(pre_tokens);
     a.next = clamp_window(next_tokens);
-    if ((e = launch_forward(a, dtype, static_cast<int>(head_dim), stream)) != 0)
+    if ((e = timed_launch(K_FWD, stream, [&] {
+           return launch_forward(a, dtype, static_cast<int>(head_dim), stream);
+         })) != 0)
       return fail(SWA_ERR_HIP, hip_error_string(e));
   }
   return SWA_OK;
@@ -429,8 +482,11 @@ swa_status swa_backward(const void* q, const void* k, const void* v, const void*
   float* lse2 = reinterpret_cast<float*>(ws + L.lse2);
   float* dq_acc = reinterpret_cast<float*>(ws + L.dq_acc);
   int e = 0;
-  BwdPreArgs pa{dy, out, softmax_max, softmax_sum, drow, lse2, dq_acc, t_q * num_heads};
-  if ((e = launch_bwd_pre(pa, dtype, static_cast<int>(head_dim), stream)) != 0)
+  BwdPreArgs pa{dy, out, softmax_max, softmax_sum, drow, lse2, dq_acc, t_q * num_heads,
+                static_cast<int32_t>(num_heads), static_cast<int32_t>(t_q)};
+  if ((e = timed_launch(K_BWD_PRE, stream, [&] {
+         return launch_bwd_pre(pa, dtype, static_cast<int>(head_dim), stream);
+       })) != 0)
     return fail(SWA_ERR_HIP, hip_error_string(e));
   if (!items.empty()) {
     BwdArgs a;
@@ -446,23 +502,28 @@ swa_status swa_backward(const void* q, const void* k, const void* v, const void*
     a.items = reinterpret_cast<const Item*>(ws + L.items);
     a.n_items = static_cast<int32_t>(items.size());
     a.num_heads = static_cast<int32_t>(num_heads);
+    a.t_q = static_cast<int32_t>(t_q);
     a.scale = static_cast<float>(scale);
     a.scale_log2 = static_cast<float>(scale * 1.4426950408889634);
     a.mode = static_cast<int32_t>(sparse_mode);
     a.pre = clamp_window(pre_tokens);
     a.next = clamp_window(next_tokens);
-    if ((e = launch_backward(a, dtype, static_cast<int>(head_dim), stream)) != 0)
+    if ((e = timed_launch(K_BWD, stream, [&] {
+           return launch_backward(a, dtype, static_cast<int>(head_dim), stream);
+         })) != 0)
       return fail(SWA_ERR_HIP, hip_error_string(e));
   }
   FinalizeArgs fa{dq_acc, dq, static_cast<float>(scale), t_q * num_heads * head_dim};
-  if ((e = launch_dq_finalize(fa, dtype, stream)) != 0)
+  if ((e = timed_launch(K_DQ_FIN, stream, [&] { return launch_dq_finalize(fa, dtype, stream); })) != 0)
     return fail(SWA_ERR_HIP, hip_error_string(e));
   if (end_kv < t_kv) {
     FillArgs f{dk, static_cast<int64_t>(elem_bytes(dtype)), num_heads * head_dim, end_kv, t_kv,
                nullptr, nullptr, 0};
-    if ((e = launch_fill(f, stream)) != 0) return fail(SWA_ERR_HIP, hip_error_string(e));
+    if ((e = timed_launch(K_FILL, stream, [&] { return launch_fill(f, stream); })) != 0)
+      return fail(SWA_ERR_HIP, hip_error_string(e));
     f.x = dv;
-    if ((e = launch_fill(f, stream)) != 0) return fail(SWA_ERR_HIP, hip_error_string(e));
+    if ((e = timed_launch(K_FILL, stream, [&] { return launch_fill(f, stream); })) != 0)
+      return fail(SWA_ERR_HIP, hip_error_string(e));
   }
   return SWA_OK;
 }
@@ -491,7 +552,7 @@ swa_status swa_debug_tile_schedule(const int64_t* cu_seqlens_q, const int64_t* c
   } else {
     schedule_backward(p, seqs, items);
     *block_item = BWD_BN;
-    *block_tile = BWD_BM;
+    *block_tile = bwd_block_q(dtype, static_cast<int>(head_dim));
   }
   order_items(items);
   int64_t n = 0;
@@ -514,6 +575,39 @@ swa_status swa_debug_tile_schedule(const int64_t* cu_seqlens_q, const int64_t* c
     for (int t = lo; t <= hi; ++t) emit(it.seq, it.block, t, (t >= flo && t <= fhi) ? 2 : 1);
   }
   *n_rows = n;
+  return SWA_OK;
+}
+
+swa_status swa_profile_enable(int32_t enable) {
+  std::lock_guard<std::mutex> lock(g_prof.mu);
+  g_prof.on = enable != 0;
+  return SWA_OK;
+}
+
+swa_status swa_profile_read(int32_t kernel, double* total_ms, int64_t* launches) {
+  if (!total_ms || !launches) return fail(SWA_ERR_NULLPTR, "total_ms / launches is NULL");
+  if (kernel < 0 || kernel >= K_KINDS) return fail(SWA_ERR_INVALID, "unknown kernel kind");
+  std::lock_guard<std::mutex> lock(g_prof.mu);
+  double sum = 0.0;
+  int64_t n = 0;
+  std::vector<Profiler::Rec> keep;
+  for (const Profiler::Rec& r : g_prof.recs) {
+    if (r.kind != kernel) {
+      keep.push_back(r);
+      continue;
+    }
+    int e = hip_event_sync(r.stop);
+    float ms = 0.f;
+    if (e == 0) e = hip_event_elapsed_ms(&ms, r.start, r.stop);
+    if (e != 0) return fail(SWA_ERR_HIP, hip_error_string(e));
+    sum += ms;
+    ++n;
+    g_prof.pool.push_back(r.start);
+    g_prof.pool.push_back(r.stop);
+  }
+  g_prof.recs.swap(keep);
+  *total_ms = sum;
+  *launches = n;
   return SWA_OK;
 }
 

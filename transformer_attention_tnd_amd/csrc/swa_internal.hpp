@@ -10,11 +10,12 @@ namespace swa {
 // Block sizes.  Forward: a work item is one block of FWD_BM query rows of one
 // sequence (one workgroup per item and head); it walks key tiles of FWD_BN.
 // Backward: an item is one block of BWD_BN keys; it walks query tiles of
-// BWD_BM rows.
+// bwd_block_q rows.
 constexpr int FWD_BM = 128;
 constexpr int FWD_BN = 64;
 constexpr int BWD_BN = 128;
-constexpr int BWD_BM = 64;
+// query rows per backward tile: 64, or 32 for fp32 with head_dim 128 (LDS)
+constexpr int bwd_block_q(int dtype, int head_dim) { return (dtype == 0 && head_dim == 128) ? 32 : 64; }
 
 // One schedule entry (32 bytes, uploaded to the workspace).
 //   tiles = lo | hi << 16 : visited tile range [lo, hi] (empty if lo > hi)
@@ -67,10 +68,12 @@ struct BwdPreArgs {
   const void* out;
   const float* smax;
   const float* ssum;
-  float* drow;   // [t_q, N] rowsum(dY * out)
-  float* lse2;   // [t_q, N] softmax_max*log2(e) + log2(softmax_sum), +inf if empty
+  float* drow;   // [N, t_q] rowsum(dY * out)
+  float* lse2;   // [N, t_q] softmax_max*log2(e) + log2(softmax_sum), +inf if empty
   float* dq_acc; // [t_q, N, D] zeroed here
   int64_t rows;  // t_q * N
+  int32_t num_heads;
+  int32_t t_q;
 };
 
 struct BwdArgs {
@@ -78,14 +81,15 @@ struct BwdArgs {
   const void* k;
   const void* v;
   const void* dy;
-  const float* drow;
-  const float* lse2;
+  const float* drow;  // [N, t_q]
+  const float* lse2;  // [N, t_q]
   float* dq_acc;
   void* dk;
   void* dv;
   const Item* items;
   int32_t n_items;
   int32_t num_heads;
+  int32_t t_q;
   float scale;
   float scale_log2;
   int32_t mode;
@@ -125,5 +129,8 @@ int hip_pinned_free(void* p);
 int hip_event_create(void** ev);
 int hip_event_record(void* ev, void* stream);
 int hip_event_sync(void* ev);
+int hip_event_create_timed(void** ev);
+int hip_event_elapsed_ms(float* ms, void* start, void* stop);
+int hip_event_destroy(void* ev);
 
 }  // namespace swa
