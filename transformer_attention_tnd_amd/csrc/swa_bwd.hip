@@ -112,8 +112,8 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kernel(BwdArgs a) {
   const float* drow_g = a.drow + (int64_t)head * a.t_q + it.q_base;
   const int kb0 = it.block * BN;          // first key of the block (sequence-local)
   const int kw = kb0 + 32 * w + c;        // this lane's key
-  const int lo = it.tiles & 0xffff, hi = (it.tiles >> 16) & 0xffff;
-  const int flo = it.full & 0xffff, fhi = (it.full >> 16) & 0xffff;
+  const int lo = it.tiles[0] & 0xffff, hi = (it.tiles[0] >> 16) & 0xffff;
+  const int flo = it.full[0] & 0xffff, fhi = (it.full[0] >> 16) & 0xffff;
   const float c2 = a.scale_log2;
   const int wd = w % NDB;                 // head-dim block of this wave's dQ
   const int ld4 = (int)(ld * 4);          // dq_acc row stride in bytes

@@ -130,24 +130,24 @@ __device__ inline void dma16(u32x4 rsrc, uint32_t voff, uint32_t lds_base) {
 
 // Copy rows [0, ROWS) of a row-major [rows, ld] slice starting at `base`
 // into a swizzled LDS tile (no registers involved).  Rows >= nvalid read as
-// zero.  All 256 threads of the workgroup take part.
-template <typename T, int D, int ROWS>
+// zero.  All NT threads of the workgroup take part.
+template <typename T, int D, int ROWS, int NT = 256>
 __device__ inline void tile_load_lds(const T* base, int64_t ld, int nvalid, char* tile, int tid) {
   constexpr int RB = D * (int)sizeof(T);
   constexpr int CPR = RB / 16;
   constexpr int SLOTS = ROWS * CPR;
-  static_assert(SLOTS % 256 == 0, "tile load mapping");
+  static_assert(SLOTS % NT == 0, "tile load mapping");
   const int64_t row_bytes = ld * (int64_t)sizeof(T);
   nvalid = nvalid < ROWS ? nvalid : ROWS;
   const uint32_t nrec = nvalid > 0 ? (uint32_t)((nvalid - 1) * row_bytes + RB) : 0u;
   const u32x4 rsrc = buffer_rsrc(base, nrec);
   const uint32_t tbase = lds_addr(tile);
 #pragma unroll
-  for (int p = 0; p < SLOTS / 256; ++p) {
-    const int sl = p * 256 + tid;
+  for (int p = 0; p < SLOTS / NT; ++p) {
+    const int sl = p * NT + tid;
     const int row = sl / CPR, pc = sl % CPR;
     const uint32_t voff = (uint32_t)(row * row_bytes) + (uint32_t)((pc ^ tile_swz(row)) << 4);
-    const uint32_t dst = __builtin_amdgcn_readfirstlane(tbase + (p * 256 + (tid & ~63)) * 16);
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(tbase + (p * NT + (tid & ~63)) * 16);
     dma16(rsrc, voff, dst);
   }
 }

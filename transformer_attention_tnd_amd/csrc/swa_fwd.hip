@@ -1,5 +1,5 @@
 // Forward kernel: online-softmax attention over the visited key tiles of one
-// block of 128 query rows of one (sequence, head).
+// block of 256 query rows of one (sequence, head).
 //
 // Math (FlashAttentionVarLenScore API doc, "计算公式"; PyPTO-Gym
 // FlashAttentionScoreGrad article, "前向公式"): out = softmax(mask(scale Q K^T)) V,
@@ -7,18 +7,27 @@
 // softmax keeps a running max and running sum per row, so the full score
 // matrix never exists.
 //
-// Workgroup: 4 wavefronts x 32 query rows.  Each wave keeps its Q rows in
-// registers and computes the transposed score block S^T = K Q^T (keys as
-// rows, its 32 queries as columns), so that a lane owns one query row: the
-// row max and row sum are in-lane reductions plus one swap of lane halves.
-// The probabilities are rounded to the input type and fed straight from the
-// accumulator registers as the B operand of O^T += V^T P^T.
+// Workgroup: 8 wavefronts in two groups of 4; group g owns rows
+// [128 g, 128 g + 128) of the block, 32 rows per wave.  Each wave keeps its Q
+// rows in registers and computes the transposed score block S^T = K Q^T
+// (keys as rows, its 32 queries as columns), so that a lane owns one query
+// row: row max and row sum are in-lane reductions plus one swap of lane
+// halves.  The probabilities are rounded to the input type and fed from
+// registers as the B operand of O^T += V^T P^T.
+//
+// Ping-pong: per key tile t a wave runs a matrix phase M(t) = {P(t-1) V(t-1),
+// S(t) = K(t) Q^T} and a vector phase V(t) = softmax of S(t).  The two groups
+// are offset by half a tile and separated by workgroup barriers:
+//     half A:  group 0 runs M(t)   while group 1 runs V(t-1)
+//     half B:  group 0 runs V(t)   while group 1 runs M(t)
+// Each SIMD holds one wave of each group, so its matrix core always has one
+// wave feeding it while the other wave's softmax runs on the vector ALUs.
 //
 // Data movement: K and V tiles of 64 keys go from HBM straight into
 // swizzled row-major LDS tiles (buffer loads with the LDS destination, rows
-// past the sequence read as zero), double-buffered.  V^T operands come from
-// the row-major V tile through transposing LDS reads.  The copies of the
-// next tiles are in flight while the current one is computed.
+// past the sequence read as zero), double-buffered and issued one tile
+// ahead.  V^T operands come from the row-major V tile through transposing
+// LDS reads.
 //
 // Rescaling: the exponent reference of a row is only moved when the running
 // max exceeds it by more than 2^8 (in exp2 units); exp values then stay below
@@ -31,21 +40,14 @@
 
 #include "swa_common.hpp"
 
-// 1: the score block of tile t+1 is formed before the softmax of tile t, so
-// each wave has independent matrix work during its softmax (one wave per
-// SIMD, up to 512 registers); 0: plain double buffering, two waves per SIMD.
-#ifndef SWA_FWD_PIPELINE
-#define SWA_FWD_PIPELINE 0
-#endif
-
 namespace swa {
 
 template <typename T, int D, bool kPos>
-__global__ __launch_bounds__(256, SWA_FWD_PIPELINE ? 1 : 2) void swa_fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
   using M = Mfma<T>;
   using op_t = typename M::op_t;
   constexpr int KPL = M::KPL, KSTEP = M::KSTEP;
-  constexpr int BM = FWD_BM, BN = FWD_BN;
+  constexpr int HALF = FWD_HALF, BN = FWD_BN, NT = 512;
   constexpr int RB = D * (int)sizeof(T);  // tile row bytes
   constexpr int TB = BN * RB;             // tile bytes
   constexpr int NDB = D / 32;             // 32-wide head-dim blocks
@@ -53,14 +55,14 @@ __global__ __launch_bounds__(256, SWA_FWD_PIPELINE ? 1 : 2) void swa_fwd_kernel(
   constexpr int QSTEPS = D / KSTEP;       // contraction steps over d
   constexpr int PSTEPS = 32 / KSTEP;      // contraction steps per 32 keys
   constexpr float kRescale = 8.f;         // exp2-domain slack before moving the reference
-  static_assert(BM == 128 && BN == 64, "kernel assumes 4 waves x 32 rows and 64-key tiles");
+  static_assert(HALF == 128 && BN == 64, "two groups of 4 waves x 32 rows; 64-key tiles");
 
   __shared__ __attribute__((aligned(1024))) char lds[4 * TB];  // K0 K1 V0 V1
   char* const kbuf0 = lds;
   char* const vbuf0 = lds + 2 * TB;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6, h = lane >> 5, c = lane & 31;
+  const int lane = tid & 63, w = tid >> 6, g = w >> 2, h = lane >> 5, c = lane & 31;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   const int head = L / a.n_items;
   const Item it = a.items[L - head * a.n_items];
@@ -68,9 +70,25 @@ __global__ __launch_bounds__(256, SWA_FWD_PIPELINE ? 1 : 2) void swa_fwd_kernel(
   const T* qg = static_cast<const T*>(a.q) + (int64_t)it.q_base * ld + head * D;
   const T* kg = static_cast<const T*>(a.k) + (int64_t)it.kv_base * ld + head * D;
   const T* vg = static_cast<const T*>(a.v) + (int64_t)it.kv_base * ld + head * D;
-  const int qrow = it.block * BM + 32 * w + c;  // this lane's query row (sequence-local)
-  const int lo = it.tiles & 0xffff, hi = (it.tiles >> 16) & 0xffff;
-  const int flo = it.full & 0xffff, fhi = (it.full >> 16) & 0xffff;
+  const int qrow = it.block * 2 * HALF + HALF * g + 32 * (w & 3) + c;  // sequence-local
+  // this group's tile range, and the union over both groups (the loop range)
+  const int mlo = it.tiles[g] & 0xffff, mhi = (it.tiles[g] >> 16) & 0xffff;
+  const int mflo = it.full[g] & 0xffff, mfhi = (it.full[g] >> 16) & 0xffff;
+  int lo, hi;
+  {
+    const int lo0 = it.tiles[0] & 0xffff, hi0 = (it.tiles[0] >> 16) & 0xffff;
+    const int lo1 = it.tiles[1] & 0xffff, hi1 = (it.tiles[1] >> 16) & 0xffff;
+    if (lo0 > hi0) {
+      lo = lo1;
+      hi = hi1;
+    } else if (lo1 > hi1) {
+      lo = lo0;
+      hi = hi0;
+    } else {
+      lo = lo0 < lo1 ? lo0 : lo1;
+      hi = hi0 > hi1 ? hi0 : hi1;
+    }
+  }
   const float cs = kPos ? a.scale_log2 : 1.f;  // raw score -> exp2 units
 
   // Q fragments: B operand of S^T = K Q^T, lane (column qrow) holds
@@ -87,23 +105,12 @@ __global__ __launch_bounds__(256, SWA_FWD_PIPELINE ? 1 : 2) void swa_fwd_kernel(
   }
 
   auto load_k = [&](int tile, int b) {
-    tile_load_lds<T, D, BN>(kg + (int64_t)tile * BN * ld, ld, it.skv - tile * BN, kbuf0 + b * TB, tid);
+    tile_load_lds<T, D, BN, NT>(kg + (int64_t)tile * BN * ld, ld, it.skv - tile * BN,
+                                kbuf0 + b * TB, tid);
   };
   auto load_v = [&](int tile, int b) {
-    tile_load_lds<T, D, BN>(vg + (int64_t)tile * BN * ld, ld, it.skv - tile * BN, vbuf0 + b * TB, tid);
-  };
-  // S^T block jb: rows = keys 32*jb + c_row(r, h), column = this lane's query
-  auto scores = [&](const char* kt, floatx16* s) {
-#pragma unroll
-    for (int jb = 0; jb < NJB; ++jb) {
-      s[jb] = floatx16{};
-#pragma unroll
-      for (int t = 0; t < QSTEPS; ++t) {
-        const op_t ka = M::load(reinterpret_cast<const T*>(
-            kt + tile_off<RB>(32 * jb + c, (KSTEP * t + KPL * h) * (int)sizeof(T))));
-        s[jb] = M::mma(ka, qf[t], s[jb]);
-      }
-    }
+    tile_load_lds<T, D, BN, NT>(vg + (int64_t)tile * BN * ld, ld, it.skv - tile * BN,
+                                vbuf0 + b * TB, tid);
   };
 
   floatx16 o[NDB];
@@ -112,9 +119,46 @@ __global__ __launch_bounds__(256, SWA_FWD_PIPELINE ? 1 : 2) void swa_fwd_kernel(
   float m_true = -INFINITY;  // running max of the raw (masked) scores
   float m_ref = -INFINITY;   // exponent reference, raw units
   float l_run = 0.f;         // running sum relative to m_ref (this lane's half)
+  floatx16 s[NJB];           // scores of the current tile
+  op_t pk[NJB][PSTEPS];      // probabilities of the previous tile, operand layout
 
-  // Softmax of one tile (in place: scores -> probabilities) and P V.
-  auto tile_math = [&](auto mask_tag, int tile, floatx16* s, const char* vt) {
+  // S^T block jb: rows = keys 32*jb + c_row(r, h), column = this lane's query
+  // (the two key blocks alternate so that consecutive MFMAs are independent)
+  auto scores = [&](const char* kt) {
+#pragma unroll
+    for (int jb = 0; jb < NJB; ++jb) s[jb] = floatx16{};
+#pragma unroll
+    for (int t = 0; t < QSTEPS; ++t) {
+#pragma unroll
+      for (int jb = 0; jb < NJB; ++jb) {
+        const op_t ka = M::load(reinterpret_cast<const T*>(
+            kt + tile_off<RB>(32 * jb + c, (KSTEP * t + KPL * h) * (int)sizeof(T))));
+        s[jb] = M::mma(ka, qf[t], s[jb]);
+      }
+    }
+  };
+  // O^T[db] += V^T P^T with the probabilities of the previous tile
+  auto pv = [&](const char* vt) {
+#pragma unroll
+    for (int jb = 0; jb < NJB; ++jb) {
+#pragma unroll
+      for (int t2 = 0; t2 < PSTEPS; ++t2) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          op_t va;
+          if constexpr (sizeof(T) == 2) {
+            va = tr_operand<RB, true>(vt, 32 * jb + KSTEP * t2, db, lane);
+          } else {
+            const int row = 32 * jb + row_of_slot<T>(KSTEP * t2 + KPL * h);
+            va = *reinterpret_cast<const T*>(vt + tile_off<RB>(row, (32 * db + c) * (int)sizeof(T)));
+          }
+          o[db] = M::mma(va, pk[jb][t2], o[db]);
+        }
+      }
+    }
+  };
+  // Softmax of the current tile: scores -> probabilities (packed), running stats.
+  auto softmax = [&](auto mask_tag, int tile) {
     constexpr bool kMask = decltype(mask_tag)::value;
     if constexpr (!kPos) {  // non-positive scale: work on scaled scores (scale before masking)
 #pragma unroll
@@ -155,77 +199,60 @@ __global__ __launch_bounds__(256, SWA_FWD_PIPELINE ? 1 : 2) void swa_fwd_kernel(
         s[jb][r] = p;
         lsum += p;
       }
+#pragma unroll
+      for (int t2 = 0; t2 < PSTEPS; ++t2) pk[jb][t2] = M::pack(s[jb], t2);
     }
     l_run += lsum;
-    // O^T[db] += V^T P^T
-#pragma unroll
-    for (int jb = 0; jb < NJB; ++jb) {
-#pragma unroll
-      for (int t2 = 0; t2 < PSTEPS; ++t2) {
-        const op_t pb = M::pack(s[jb], t2);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          op_t va;
-          if constexpr (sizeof(T) == 2) {
-            va = tr_operand<RB, true>(vt, 32 * jb + KSTEP * t2, db, lane);
-          } else {
-            const int row = 32 * jb + row_of_slot<T>(KSTEP * t2 + KPL * h);
-            va = *reinterpret_cast<const T*>(vt + tile_off<RB>(row, (32 * db + c) * (int)sizeof(T)));
-          }
-          o[db] = M::mma(va, pb, o[db]);
-        }
-      }
+  };
+
+  // matrix phase M(t): P(t-1) V(t-1) and S(t), for the tiles of this group
+  auto m_phase = [&](int t, int k) {
+    const bool do_pv = t - 1 >= mlo && t - 1 <= mhi;
+    const bool do_s = t >= mlo && t <= mhi;
+    const char* kt = kbuf0 + (k & 1) * TB;
+    const char* vt = vbuf0 + ((k + 1) & 1) * TB;  // V(t-1) sits in buffer (k-1) & 1
+    if (do_pv && do_s) {
+      pv(vt);
+      scores(kt);
+    } else if (do_pv) {
+      pv(vt);
+    } else if (do_s) {
+      scores(kt);
     }
+  };
+  // vector phase V(t)
+  auto v_phase = [&](int t) {
+    if (t < mlo || t > mhi) return;
+    if (t < mflo || t > mfhi)
+      softmax(std::true_type{}, t);
+    else
+      softmax(std::false_type{}, t);
   };
 
   if (lo <= hi) {
-#if SWA_FWD_PIPELINE
     load_k(lo, 0);
-    load_v(lo, 0);
-    if (lo < hi) load_k(lo + 1, 1);
     wait_vmem();
     __syncthreads();
-    floatx16 s_cur[NJB];
-    scores(kbuf0, s_cur);
-    __syncthreads();  // every wave has read K(lo) before K(lo + 2) overwrites it
-    for (int tile = lo; tile <= hi; ++tile) {
-      const int b = (tile - lo) & 1;
-      // K(tile + 1) is in kbuf[b ^ 1], V(tile) in vbuf[b]; refill the others
-      if (tile + 1 <= hi) load_v(tile + 1, b ^ 1);
-      if (tile + 2 <= hi) load_k(tile + 2, b);
-      floatx16 s_nxt[NJB];
-      if (tile < hi) scores(kbuf0 + (b ^ 1) * TB, s_nxt);
-      if (tile < flo || tile > fhi)
-        tile_math(std::true_type{}, tile, s_cur, vbuf0 + b * TB);
+    const int nk = hi - lo + 2;
+    for (int k = 0; k < nk; ++k) {
+      const int t = lo + k;
+      // copies for the next pair of half steps: K(t+1) and V(t)
+      if (t + 1 <= hi) load_k(t + 1, (k + 1) & 1);
+      if (t <= hi) load_v(t, k & 1);
+      // half A
+      if (g == 0)
+        m_phase(t, k);
       else
-        tile_math(std::false_type{}, tile, s_cur, vbuf0 + b * TB);
-      wait_vmem();
+        v_phase(t - 1);
       __syncthreads();
-#pragma unroll
-      for (int jb = 0; jb < NJB; ++jb) s_cur[jb] = s_nxt[jb];
-    }
-#else
-    load_k(lo, 0);
-    load_v(lo, 0);
-    wait_vmem();
-    __syncthreads();
-    for (int tile = lo; tile <= hi; ++tile) {
-      const int b = (tile - lo) & 1;
-      // K(tile), V(tile) in buffer b; tile + 1 goes to the other buffer
-      if (tile + 1 <= hi) {
-        load_k(tile + 1, b ^ 1);
-        load_v(tile + 1, b ^ 1);
-      }
-      floatx16 s[NJB];
-      scores(kbuf0 + b * TB, s);
-      if (tile < flo || tile > fhi)
-        tile_math(std::true_type{}, tile, s, vbuf0 + b * TB);
+      // half B
+      if (g == 0)
+        v_phase(t);
       else
-        tile_math(std::false_type{}, tile, s, vbuf0 + b * TB);
+        m_phase(t, k);
       wait_vmem();
       __syncthreads();
     }
-#endif
   }
 
   // epilogue: normalise, store out and the statistics of this lane's row
@@ -237,17 +264,17 @@ __global__ __launch_bounds__(256, SWA_FWD_PIPELINE ? 1 : 2) void swa_fwd_kernel(
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * db + 8 * g + 4 * h;
+      for (int gq = 0; gq < 4; ++gq) {
+        const int d0 = 32 * db + 8 * gq + 4 * h;
         if constexpr (sizeof(T) == 2) {
           bf16x4 v4;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v4[e] = static_cast<bf16>(o[db][4 * g + e] * inv);
+          for (int e = 0; e < 4; ++e) v4[e] = static_cast<bf16>(o[db][4 * gq + e] * inv);
           *reinterpret_cast<bf16x4*>(op + d0) = v4;
         } else {
           floatx4 v4;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v4[e] = o[db][4 * g + e] * inv;
+          for (int e = 0; e < 4; ++e) v4[e] = o[db][4 * gq + e] * inv;
           *reinterpret_cast<floatx4*>(op + d0) = v4;
         }
       }
@@ -268,10 +295,10 @@ template <typename T, int D>
 static int launch_fwd_t(const FwdArgs& a, void* stream) {
   const int64_t nwg = (int64_t)a.n_items * a.num_heads;
   if (a.scale_log2 > 0.f)
-    hipLaunchKernelGGL((swa_fwd_kernel<T, D, true>), dim3((unsigned)nwg), dim3(256), 0,
+    hipLaunchKernelGGL((swa_fwd_kernel<T, D, true>), dim3((unsigned)nwg), dim3(512), 0,
                        static_cast<hipStream_t>(stream), a);
   else
-    hipLaunchKernelGGL((swa_fwd_kernel<T, D, false>), dim3((unsigned)nwg), dim3(256), 0,
+    hipLaunchKernelGGL((swa_fwd_kernel<T, D, false>), dim3((unsigned)nwg), dim3(512), 0,
                        static_cast<hipStream_t>(stream), a);
   return (int)hipGetLastError();
 }

@@ -149,47 +149,54 @@ BwdLayout bwd_layout(int64_t num_seqs, int64_t t_q, int64_t t_kv, int64_t n, int
   return l;
 }
 
-// Forward schedule: one item per block of FWD_BM query rows; key tiles of
-// FWD_BN.  A tile is visited iff some (i < Sq, j < Skv) in it is allowed, and
-// is "full" iff the whole FWD_BM x FWD_BN tile lies inside the sequence and
-// inside the band.
+// Forward schedule: one item per block of FWD_BM query rows, made of two
+// halves of FWD_HALF rows with their own key-tile ranges (tiles of FWD_BN).
+// For a block of rows, a tile is visited iff some (i < Sq, j < Skv) in it is
+// allowed, and is "full" iff the whole block x FWD_BN tile lies inside the
+// sequence and inside the band.
+void forward_range(const Problem& p, const Seq& s, int64_t r0, int64_t* lo, int64_t* hi,
+                   int64_t* flo, int64_t* fhi) {
+  const int64_t BM = FWD_HALF, BN = FWD_BN;
+  *lo = 1, *hi = 0, *flo = 1, *fhi = 0;
+  if (r0 >= s.sq || s.skv == 0) return;
+  const int64_t r1 = std::min(r0 + BM, s.sq) - 1;
+  int64_t jlo = 0, jhi = s.skv - 1;
+  if (p.sparse_mode == 4) {
+    jlo = std::max<int64_t>(0, r0 - p.pre_tokens);
+    jhi = std::min<int64_t>(s.skv - 1, r1 + p.next_tokens);
+  }
+  if (jlo > jhi) return;
+  *lo = jlo / BN;
+  *hi = jhi / BN;
+  if (r0 + BM <= s.sq) {
+    *flo = *lo;
+    *fhi = std::min(*hi, s.skv / BN - 1);
+    if (p.sparse_mode == 4) {
+      *flo = std::max(*flo, ceil_div(r0 + BM - 1 - p.pre_tokens, BN));
+      *fhi = std::min(*fhi, floor_div(r0 + p.next_tokens - BN + 1, BN));
+    }
+  }
+}
+
 void schedule_forward(const Problem& p, const std::vector<Seq>& seqs, std::vector<Item>& items) {
   items.clear();
-  const int64_t BM = FWD_BM, BN = FWD_BN;
   for (const Seq& s : seqs) {
     if (s.sq == 0) continue;
-    const int64_t nqb = ceil_div(s.sq, BM);
+    const int64_t nqb = ceil_div(s.sq, FWD_BM);
     for (int64_t qb = 0; qb < nqb; ++qb) {
-      const int64_t r0 = qb * BM, r1 = std::min(r0 + BM, s.sq) - 1;
-      int64_t lo = 1, hi = 0, flo = 1, fhi = 0;
-      if (s.skv > 0) {
-        int64_t jlo = 0, jhi = s.skv - 1;
-        if (p.sparse_mode == 4) {
-          jlo = std::max<int64_t>(0, r0 - p.pre_tokens);
-          jhi = std::min<int64_t>(s.skv - 1, r1 + p.next_tokens);
-        }
-        if (jlo <= jhi) {
-          lo = jlo / BN;
-          hi = jhi / BN;
-          if (r0 + BM <= s.sq) {
-            flo = lo;
-            fhi = std::min(hi, s.skv / BN - 1);
-            if (p.sparse_mode == 4) {
-              flo = std::max(flo, ceil_div(r0 + BM - 1 - p.pre_tokens, BN));
-              fhi = std::min(fhi, floor_div(r0 + p.next_tokens - BN + 1, BN));
-            }
-          }
-        }
-      }
-      Item it;
+      Item it{};
       it.q_base = static_cast<int32_t>(s.q0);
       it.kv_base = static_cast<int32_t>(s.k0);
       it.sq = static_cast<int32_t>(s.sq);
       it.skv = static_cast<int32_t>(s.skv);
       it.block = static_cast<int32_t>(qb);
-      it.tiles = pack_range(lo, hi);
-      it.full = pack_range(flo, fhi);
       it.seq = s.b;
+      for (int half = 0; half < 2; ++half) {
+        int64_t lo, hi, flo, fhi;
+        forward_range(p, s, qb * FWD_BM + half * FWD_HALF, &lo, &hi, &flo, &fhi);
+        it.tiles[half] = pack_range(lo, hi);
+        it.full[half] = pack_range(flo, fhi);
+      }
       items.push_back(it);
     }
   }
@@ -226,14 +233,16 @@ void schedule_backward(const Problem& p, const std::vector<Seq>& seqs,
           }
         }
       }
-      Item it;
+      Item it{};
       it.q_base = static_cast<int32_t>(s.q0);
       it.kv_base = static_cast<int32_t>(s.k0);
       it.sq = static_cast<int32_t>(s.sq);
       it.skv = static_cast<int32_t>(s.skv);
       it.block = static_cast<int32_t>(kb);
-      it.tiles = pack_range(lo, hi);
-      it.full = pack_range(flo, fhi);
+      it.tiles[0] = pack_range(lo, hi);
+      it.full[0] = pack_range(flo, fhi);
+      it.tiles[1] = pack_range(1, 0);
+      it.full[1] = pack_range(1, 0);
       it.seq = s.b;
       items.push_back(it);
     }
@@ -242,10 +251,13 @@ void schedule_backward(const Problem& p, const std::vector<Seq>& seqs,
 
 int range_lo(int32_t r) { return r & 0xffff; }
 int range_hi(int32_t r) { return (r >> 16) & 0xffff; }
-int64_t cost(const Item& it) {
-  const int lo = range_lo(it.tiles), hi = range_hi(it.tiles);
+int64_t range_len(int32_t r) {
+  const int lo = range_lo(r), hi = range_hi(r);
   return hi >= lo ? hi - lo + 1 : 0;
 }
+// Work of an item: its longer range (the two halves of a forward item run
+// side by side).
+int64_t cost(const Item& it) { return std::max(range_len(it.tiles[0]), range_len(it.tiles[1])); }
 
 // Longest item first (stable, so equal-cost blocks of one sequence stay in
 // order and neighbouring query blocks, which read the same key/value tiles,
@@ -547,7 +559,7 @@ swa_status swa_debug_tile_schedule(const int64_t* cu_seqlens_q, const int64_t* c
   std::vector<Item> items;
   if (direction == 0) {
     schedule_forward(p, seqs, items);
-    *block_item = FWD_BM;
+    *block_item = FWD_HALF;
     *block_tile = FWD_BN;
   } else {
     schedule_backward(p, seqs, items);
@@ -566,13 +578,18 @@ swa_status swa_debug_tile_schedule(const int64_t* cu_seqlens_q, const int64_t* c
     ++n;
   };
   for (const Item& it : items) {
-    const int lo = range_lo(it.tiles), hi = range_hi(it.tiles);
-    const int flo = range_lo(it.full), fhi = range_hi(it.full);
-    if (hi < lo) {
-      emit(it.seq, it.block, -1, 0);
-      continue;
+    const int halves = direction == 0 ? 2 : 1;
+    for (int half = 0; half < halves; ++half) {
+      const int32_t block = direction == 0 ? it.block * 2 + half : it.block;
+      if (direction == 0 && static_cast<int64_t>(block) * FWD_HALF >= it.sq) continue;
+      const int lo = range_lo(it.tiles[half]), hi = range_hi(it.tiles[half]);
+      const int flo = range_lo(it.full[half]), fhi = range_hi(it.full[half]);
+      if (hi < lo) {
+        emit(it.seq, block, -1, 0);
+        continue;
+      }
+      for (int t = lo; t <= hi; ++t) emit(it.seq, block, t, (t >= flo && t <= fhi) ? 2 : 1);
     }
-    for (int t = lo; t <= hi; ++t) emit(it.seq, it.block, t, (t >= flo && t <= fhi) ? 2 : 1);
   }
   *n_rows = n;
   return SWA_OK;

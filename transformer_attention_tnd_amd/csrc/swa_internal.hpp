@@ -7,30 +7,34 @@
 
 namespace swa {
 
-// Block sizes.  Forward: a work item is one block of FWD_BM query rows of one
-// sequence (one workgroup per item and head); it walks key tiles of FWD_BN.
-// Backward: an item is one block of BWD_BN keys; it walks query tiles of
-// bwd_block_q rows.
-constexpr int FWD_BM = 128;
+// Block sizes.  Forward: a work item is one block of FWD_BM = 2 x FWD_HALF
+// query rows of one sequence (one workgroup per item and head, two wave
+// groups of FWD_HALF rows); it walks key tiles of FWD_BN.  Backward: an item
+// is one block of BWD_BN keys; it walks query tiles of bwd_block_q rows.
+constexpr int FWD_HALF = 128;
+constexpr int FWD_BM = 2 * FWD_HALF;
 constexpr int FWD_BN = 64;
 constexpr int BWD_BN = 128;
 // query rows per backward tile: 64, or 32 for fp32 with head_dim 128 (LDS)
 constexpr int bwd_block_q(int dtype, int head_dim) { return (dtype == 0 && head_dim == 128) ? 32 : 64; }
 
-// One schedule entry (32 bytes, uploaded to the workspace).
-//   tiles = lo | hi << 16 : visited tile range [lo, hi] (empty if lo > hi)
-//   full  = flo | fhi << 16 : tiles in [flo, fhi] need no element mask
+// One schedule entry (48 bytes, uploaded to the workspace).
+//   tiles[i] = lo | hi << 16 : visited tile range [lo, hi] (empty if lo > hi)
+//   full[i]  = flo | fhi << 16 : tiles in [flo, fhi] need no element mask
+// Forward items carry one range per FWD_HALF-row half (index 0, 1); backward
+// items use index 0 only.
 struct Item {
   int32_t q_base;   // first token of the sequence in the query tensor
   int32_t kv_base;  // first token of the sequence in the key/value tensors
   int32_t sq;       // query length of the sequence
   int32_t skv;      // key/value length of the sequence
   int32_t block;    // item block index inside the sequence
-  int32_t tiles;
-  int32_t full;
   int32_t seq;      // batch index (diagnostics only)
+  int32_t tiles[2];
+  int32_t full[2];
+  int32_t pad[2];
 };
-static_assert(sizeof(Item) == 32, "Item layout");
+static_assert(sizeof(Item) == 48, "Item layout");
 
 inline int32_t pack_range(int64_t lo, int64_t hi) {
   if (lo > hi) { lo = 1; hi = 0; }
