@@ -12,9 +12,10 @@
 // swa_bwd_pre_kernel: D and the per-row log2-domain normaliser
 //   lse2 = softmax_max * log2(e) + log2(softmax_sum), so that P = exp2(s*c - lse2)
 //   with c = scale * log2(e); it also zeroes the fp32 dq accumulator.
-// swa_bwd_kernel: one workgroup per (block of 128 keys, head); each of its 4
-//   waves owns 32 keys and keeps its dK, dV accumulators in registers while
-//   it walks the query tiles of the band; the K and V blocks stay in LDS.
+// swa_bwd_kernel (fp32 inputs) and swa_bwd_bf16_kernel: one workgroup per
+//   (block of 128 keys, head); each of its 4 waves owns 32 keys and keeps its
+//   dK, dV accumulators in registers while it walks the query tiles of the
+//   band.
 //   Scores are formed as S = Q K^T (queries as rows, the wave's keys as
 //   columns), so P and dS come out of the accumulators in the operand layout
 //   of dV^T += dY^T P and dK^T += Q^T dS.  Q and dY tiles go from HBM
@@ -332,6 +333,320 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kernel(BwdArgs a) {
   }
 }
 
+// bf16 main kernel (head_dim 64 or 128): the math and the work split of
+// swa_bwd_kernel, arranged so that every matrix product reads at most one
+// operand from LDS:
+//   - each wave keeps its 32 K and V rows in registers (B operands of S and
+//     dP), and the K block's columns of its dQ head-dim block (B operand of
+//     dQ = dS K), built once through transposing LDS reads;
+//   - dS tiles are double-buffered, so one barrier per query tile separates
+//     writing dS from reading it, and the dQ product of tile t-1 runs inside
+//     the body of tile t, next to tile t's own products;
+//   - the dQ atomics carry the row in the lane offset: rows past the end of
+//     the sequence fall outside the buffer range and the hardware range check
+//     drops them, so the tile body has no branches.
+template <int D>
+__global__ __launch_bounds__(256, 1) void swa_bwd_bf16_kernel(BwdArgs a) {
+  using M = Mfma<bf16>;
+  using op_t = M::op_t;
+  constexpr int BN = BWD_BN;           // keys per workgroup
+  constexpr int BM = 64;               // query rows per tile
+  constexpr int QB = BM / 32;          // 32-row query blocks per tile
+  constexpr int RB = D * 2;            // Q / dY / K row bytes
+  constexpr int QTB = BM * RB;         // Q or dY tile bytes
+  constexpr int SRB = BN * 2;          // dS row bytes
+  constexpr int STB = BM * SRB;        // dS tile bytes
+  constexpr int NDB = D / 32;          // head-dim blocks
+  constexpr int DSTEPS = D / 16;       // contraction steps over d
+  constexpr int KSTEPS = BN / 16;      // contraction steps over the keys
+  constexpr int WPD = 4 / NDB;         // waves per head-dim block in dQ
+  constexpr int TASKS = QB * NDB / 4;  // 32x32 dQ blocks per wave
+  static_assert(BN == 128 && (D == 64 || D == 128), "4 waves x 32 keys, 64-row tiles");
+  static_assert(BN * RB <= 2 * STB, "the K block is staged in the dS buffers");
+
+  __shared__ __attribute__((aligned(1024))) char lds[4 * QTB + 2 * STB];
+  __shared__ floatx4 lse_s[2][BM / 4];   // lse2 of the tile's rows
+  __shared__ floatx4 drow_s[2][BM / 4];  // D of the tile's rows
+  char* const qbuf = lds;            // Q tiles [2]
+  char* const ybuf = lds + 2 * QTB;  // dY tiles [2]
+  char* const sbuf = lds + 4 * QTB;  // dS tiles [2]; the K block during set-up
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, h = lane >> 5, c = lane & 31;
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int head = L / a.n_items;
+  const Item it = a.items[L - head * a.n_items];
+  const int64_t ld = (int64_t)a.num_heads * D;
+  const bf16* qg = static_cast<const bf16*>(a.q) + (int64_t)it.q_base * ld + head * D;
+  const bf16* dyg = static_cast<const bf16*>(a.dy) + (int64_t)it.q_base * ld + head * D;
+  const bf16* kg = static_cast<const bf16*>(a.k) + (int64_t)it.kv_base * ld + head * D;
+  const bf16* vg = static_cast<const bf16*>(a.v) + (int64_t)it.kv_base * ld + head * D;
+  const float* lse_g = a.lse2 + (int64_t)head * a.t_q + it.q_base;
+  const float* drow_g = a.drow + (int64_t)head * a.t_q + it.q_base;
+  float* const dq_g = a.dq_acc + (int64_t)it.q_base * ld + head * D;
+  const int kb0 = it.block * BN;       // first key of the block (sequence-local)
+  const int kw = kb0 + 32 * w + c;     // this lane's key
+  const int lo = it.tiles[0] & 0xffff, hi = (it.tiles[0] >> 16) & 0xffff;
+  const int flo = it.full[0] & 0xffff, fhi = (it.full[0] >> 16) & 0xffff;
+  const float c2 = a.scale_log2;
+  const int wd = w % NDB;              // head-dim block of this wave's dQ
+  const int ld4 = (int)(ld * 4);       // dq accumulator row stride in bytes
+  const int dq_lane_off = (4 * h * (int)ld + 32 * wd + c) * 4;
+
+  floatx16 dk[NDB], dv[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    dk[db] = floatx16{};
+    dv[db] = floatx16{};
+  }
+  // B operands of S and dP: lane (column kw) holds K[kw][16t + 8h + e], V likewise
+  op_t kr[DSTEPS], vr[DSTEPS];
+  {
+    const bool ok = kw < it.skv;
+    const int64_t off = (int64_t)(ok ? kw : 0) * ld + 8 * h;
+#pragma unroll
+    for (int t = 0; t < DSTEPS; ++t) {
+      kr[t] = ok ? M::load(kg + off + 16 * t) : op_t{};
+      vr[t] = ok ? M::load(vg + off + 16 * t) : op_t{};
+    }
+  }
+  // B operand of dQ: lane (column 32 wd + c) holds K[kb0 + 16t + 8h + e][32 wd + c]
+  op_t kq[KSTEPS];
+
+  float sreg = 0.f;
+  auto load_qtile = [&](int tile, int b) {
+    const int nvalid = it.sq - tile * BM;
+    tile_load_lds<bf16, D, BM>(qg + (int64_t)tile * BM * ld, ld, nvalid, qbuf + b * QTB, tid);
+    tile_load_lds<bf16, D, BM>(dyg + (int64_t)tile * BM * ld, ld, nvalid, ybuf + b * QTB, tid);
+    if (tid < 2 * BM) {
+      const int row = tid & (BM - 1), i = tile * BM + row;
+      if (tid < BM)
+        sreg = i < it.sq ? lse_g[i] : INFINITY;
+      else
+        sreg = i < it.sq ? drow_g[i] : 0.f;
+    }
+  };
+  auto store_rows = [&](int b) {
+    if (tid < BM)
+      reinterpret_cast<float*>(lse_s[b])[tid] = sreg;
+    else if (tid < 2 * BM)
+      reinterpret_cast<float*>(drow_s[b])[tid - BM] = sreg;
+  };
+
+  // S = Q K^T and dP = dY V^T of query block qb (rows 32 qb + c_row(r, h),
+  // column: this lane's key); the two chains alternate.
+  auto sdp = [&](const char* qt, const char* yt, int qb, floatx16& s, floatx16& dp) {
+    s = floatx16{};
+    dp = floatx16{};
+#pragma unroll
+    for (int t = 0; t < DSTEPS; ++t) {
+      const int off = tile_off<RB>(32 * qb + c, (16 * t + 8 * h) * 2);
+      s = M::mma(M::load(reinterpret_cast<const bf16*>(qt + off)), kr[t], s);
+      dp = M::mma(M::load(reinterpret_cast<const bf16*>(yt + off)), vr[t], dp);
+    }
+  };
+  // P = exp2(s c - lse2) and dS = P (dP - D), packed as operands whose
+  // contraction slots follow the accumulator rows.
+  // Rows allowed for this lane's key: i in [i_min, i_max] (empty if the key
+  // is past the sequence), from the band rule -pre <= kw - i <= next.
+  int i_min = 0, i_max = it.sq - 1;
+  if (a.mode == 4) {  // 64-bit: pre / next may be near the int range
+    const int64_t lo64 = (int64_t)kw - a.next, hi64 = (int64_t)kw + a.pre;
+    i_min = lo64 < 0 ? 0 : (lo64 > it.sq ? it.sq : (int)lo64);
+    i_max = hi64 < i_max ? (hi64 < -1 ? -1 : (int)hi64) : i_max;
+  }
+  if (kw >= it.skv) i_max = -1;
+  auto softmax = [&](auto mask_tag, int tile, int b, int qb, floatx16& s, floatx16& dp, op_t* pk,
+                     op_t* sk) {
+    constexpr bool kMask = decltype(mask_tag)::value;
+    // row 32 qb + 8 g + 4 h + e of the tile is allowed iff the tile-relative
+    // constant 32 qb + 8 g + e lies in [rel_lo, rel_hi]
+    int rel_lo = 0, rel_hi = 0;
+    if constexpr (kMask) {
+      rel_lo = i_min - tile * BM - 4 * h;
+      rel_hi = i_max - tile * BM - 4 * h;
+      asm volatile("" : "+v"(rel_lo), "+v"(rel_hi));
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int rb = 32 * qb + 8 * g + 4 * h;
+      const floatx4 l4 = lse_s[b][rb / 4];
+      const floatx4 d4 = drow_s[b][rb / 4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * g + e;
+        float p = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -l4[e]));
+        if constexpr (kMask) {
+          const int rel = 32 * qb + 8 * g + e;
+          p = (rel >= rel_lo && rel <= rel_hi) ? p : 0.f;
+        }
+        s[r] = p;
+        dp[r] = p * (dp[r] - d4[e]);
+      }
+    }
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      pk[t2] = M::pack(s, t2);
+      sk[t2] = M::pack(dp, t2);
+    }
+  };
+  // dS of query block qb to the LDS tile.  Adjacent lanes hold adjacent keys
+  // of the same rows: each lane swaps one packed pair with its neighbour and
+  // stores two keys of one row as one 32-bit word (even lanes the rows of
+  // accumulator registers r, odd lanes those of r + 1).
+  auto store_ds = [&](char* st, int qb, const op_t* sk) {
+    const bool odd = c & 1;
+    const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
+    const int col = (32 * w + (c & ~1)) * 2;
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const u32x4 wv = __builtin_bit_cast(u32x4, sk[t2]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t mine = wv[k];
+        const uint32_t other = (uint32_t)__builtin_amdgcn_mov_dpp((int)mine, 0xB1, 0xF, 0xF, false);
+        const uint32_t word = __builtin_amdgcn_perm(other, mine, sel);
+        const int row = 32 * qb + c_row(8 * t2 + 2 * k, h) + (odd ? 1 : 0);
+        *reinterpret_cast<uint32_t*>(st + tile_off<SRB>(row, col)) = word;
+      }
+    }
+  };
+  // dV^T += dY^T P and dK^T += Q^T dS over the 32 rows of query block qb
+  auto dvdk = [&](const char* qt, const char* yt, int qb, const op_t* pk, const op_t* sk) {
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const op_t ya = tr_operand<RB, true>(yt, 32 * qb + 16 * t2, db, lane);
+        const op_t qa = tr_operand<RB, true>(qt, 32 * qb + 16 * t2, db, lane);
+        dv[db] = M::mma(ya, pk[t2], dv[db]);
+        dk[db] = M::mma(qa, sk[t2], dk[db]);
+      }
+    }
+  };
+  // dQ blocks (rows 32 qb, head-dim block wd) = dS K of one tile
+  auto dq_mma = [&](const char* st, floatx16* acc) {
+#pragma unroll
+    for (int k = 0; k < TASKS; ++k) acc[k] = floatx16{};
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) {
+#pragma unroll
+      for (int k = 0; k < TASKS; ++k) {
+        const int qb = w / NDB + k * WPD;
+        const op_t sa = M::load(
+            reinterpret_cast<const bf16*>(st + tile_off<SRB>(32 * qb + c, (16 * t + 8 * h) * 2)));
+        acc[k] = M::mma(sa, kq[t], acc[k]);
+      }
+    }
+  };
+  // add them to the fp32 accumulator rows of `tile` (nothing when !valid)
+  auto dq_add = [&](int tile, bool valid, const floatx16* acc) {
+    int nrows = it.sq - tile * BM;
+    nrows = nrows < BM ? nrows : BM;
+    const int nbytes = valid && nrows > 0 ? (int)(((int64_t)(nrows - 1) * ld + D) * 4) : 0;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        dq_g + (int64_t)(valid ? tile : lo) * BM * ld, (short)0, nbytes, 0x00020000);
+    // (opaque copy: the 16 offsets per block are formed here, not kept live)
+    int lane_off = dq_lane_off;
+    asm volatile("" : "+v"(lane_off));
+#pragma unroll
+    for (int k = 0; k < TASKS; ++k) {
+      const int qb = w / NDB + k * WPD;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int voff = lane_off + (32 * qb + 8 * (r >> 2) + (r & 3)) * ld4;
+        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[k][r], rsrc, voff, 0, 0);
+      }
+    }
+  };
+
+  // scheduling fence: keeps each phase's operand reads inside the phase
+  auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+  // One query tile: its S, dP, P, dS, dV, dK, plus dQ of the previous tile.
+  auto step = [&](auto mask_tag, int tile, int b) {
+    const char* qt = qbuf + b * QTB;
+    const char* yt = ybuf + b * QTB;
+    char* st = sbuf + b * STB;
+    const char* sp = sbuf + (b ^ 1) * STB;
+    floatx16 s0, dp0, s1, dp1, acc[TASKS];
+    op_t pk0[2], sk0[2], pk1[2], sk1[2];
+    sdp(qt, yt, 0, s0, dp0);
+    fence();
+    dq_mma(sp, acc);
+    fence();
+    dq_add(tile - 1, tile > lo, acc);
+    softmax(mask_tag, tile, b, 0, s0, dp0, pk0, sk0);
+    store_ds(st, 0, sk0);
+    fence();
+    sdp(qt, yt, 1, s1, dp1);
+    fence();
+    dvdk(qt, yt, 0, pk0, sk0);
+    fence();
+    softmax(mask_tag, tile, b, 1, s1, dp1, pk1, sk1);
+    store_ds(st, 1, sk1);
+    fence();
+    dvdk(qt, yt, 1, pk1, sk1);
+    fence();
+  };
+
+  if (lo <= hi) {
+    tile_load_lds<bf16, D, BN>(kg + (int64_t)kb0 * ld, ld, it.skv - kb0, sbuf, tid);
+    load_qtile(lo, 0);
+    wait_vmem();
+    store_rows(0);
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) kq[t] = tr_operand<RB, false>(sbuf, 16 * t, wd, lane);
+    if (lo < hi) load_qtile(lo + 1, 1);
+    __syncthreads();  // the K block is read before dS overwrites it
+  }
+  // tiles [from, to] in order, each body branch-free (masked or not)
+  auto run = [&](auto mask_tag, int from, int to) {
+    for (int tile = from; tile <= to; ++tile) {
+      const int b = (tile - lo) & 1;
+      step(mask_tag, tile, b);
+      if (tile < hi) store_rows(b ^ 1);
+      wait_vmem();
+      __syncthreads();
+      if (tile + 2 <= hi) load_qtile(tile + 2, b);
+    }
+  };
+  if (flo <= fhi) {  // masked tiles before and after the mask-free range
+    run(std::true_type{}, lo, flo - 1);
+    run(std::false_type{}, flo, fhi);
+    run(std::true_type{}, fhi + 1, hi);
+  } else {
+    run(std::true_type{}, lo, hi);
+  }
+  if (lo <= hi) {
+    floatx16 acc[TASKS];
+    dq_mma(sbuf + ((hi - lo) & 1) * STB, acc);
+    dq_add(hi, true, acc);
+  }
+
+  // epilogue: this lane's key column of dK^T / dV^T
+  if (kw < it.skv) {
+    const int64_t tok = (int64_t)it.kv_base + kw;
+    bf16* dkp = static_cast<bf16*>(a.dk) + tok * ld + head * D;
+    bf16* dvp = static_cast<bf16*>(a.dv) + tok * ld + head * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * db + 8 * g + 4 * h;
+        bf16x4 k4, v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          k4[e] = static_cast<bf16>(dk[db][4 * g + e] * a.scale);
+          v4[e] = static_cast<bf16>(dv[db][4 * g + e]);
+        }
+        *reinterpret_cast<bf16x4*>(dkp + d0) = k4;
+        *reinterpret_cast<bf16x4*>(dvp + d0) = v4;
+      }
+    }
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void swa_dq_finalize_kernel(FinalizeArgs a) {
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
@@ -390,8 +705,12 @@ template <typename T, int D>
 static int launch_bwd_t(const BwdArgs& a, void* stream) {
   const int64_t nwg = (int64_t)a.n_items * a.num_heads;
   constexpr int BM = bwd_block_q(sizeof(T) == 2 ? 1 : 0, D);
-  hipLaunchKernelGGL((swa_bwd_kernel<T, D, BM>), dim3((unsigned)nwg), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), a);
+  if constexpr (sizeof(T) == 2)
+    hipLaunchKernelGGL((swa_bwd_bf16_kernel<D>), dim3((unsigned)nwg), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), a);
+  else
+    hipLaunchKernelGGL((swa_bwd_kernel<T, D, BM>), dim3((unsigned)nwg), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), a);
   return (int)hipGetLastError();
 }
 

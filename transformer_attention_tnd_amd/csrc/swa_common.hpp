@@ -81,20 +81,20 @@ __device__ __host__ constexpr inline int row_of_slot(int p) {
                         : ((p & ~31) | (((p >> 3) & 3) << 3) | ((p & 1) << 2) | ((p >> 1) & 3));
 }
 
-// XOR swizzle of transposed LDS tiles (rows = head-dim index d, 64 positions
-// per row): keeps aligned groups of 8 positions contiguous while spreading
-// the transposing writes of consecutive 8-wide d chunks over distinct banks.
-__device__ inline int swz(int d, int pos) { return pos ^ (((d >> 3) & 7) << 3); }
-
 // Swizzled row-major LDS tiles.  Rows are stored back to back with no
-// padding; the 16-byte chunk c of row r sits at chunk c ^ tile_swz(r).  The
-// permutation keeps 8 consecutive rows reading one logical chunk (a 128-bit
-// operand read) on 8 distinct bank groups, and 4 consecutive rows reading one
-// aligned 32-byte pair (a transposing 64-bit read) on 4 distinct bank groups.
-__device__ __host__ constexpr inline int tile_swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+// padding; the 16-byte chunk c of row r sits at chunk c ^ tile_swz<RB>(r).
+// Rows of 256 bytes or more use a 4-bit permutation, so that 16 consecutive
+// rows reading one logical chunk (a 128-bit operand read) land on 16
+// distinct bank groups; 128-byte rows (8 chunks) use a 3-bit one.  Both keep
+// the 4 rows of a transposing 64-bit read (an aligned 32-byte pair per row)
+// on distinct bank groups.
+template <int RB>
+__device__ __host__ constexpr inline int tile_swz(int r) {
+  return RB >= 256 ? (((r & 7) << 1) | ((r >> 3) & 1)) : (((r & 3) << 1) | ((r >> 2) & 1));
+}
 template <int RB>
 __device__ __host__ constexpr inline int tile_off(int r, int byte) {
-  return r * RB + ((((byte >> 4) ^ tile_swz(r)) << 4) | (byte & 15));
+  return r * RB + ((((byte >> 4) ^ tile_swz<RB>(r)) << 4) | (byte & 15));
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -146,7 +146,7 @@ __device__ inline void tile_load_lds(const T* base, int64_t ld, int nvalid, char
   for (int p = 0; p < SLOTS / NT; ++p) {
     const int sl = p * NT + tid;
     const int row = sl / CPR, pc = sl % CPR;
-    const uint32_t voff = (uint32_t)(row * row_bytes) + (uint32_t)((pc ^ tile_swz(row)) << 4);
+    const uint32_t voff = (uint32_t)(row * row_bytes) + (uint32_t)((pc ^ tile_swz<RB>(row)) << 4);
     const uint32_t dst = __builtin_amdgcn_readfirstlane(tbase + (p * NT + (tid & ~63)) * 16);
     dma16(rsrc, voff, dst);
   }
