@@ -7,7 +7,8 @@ pre_tokens 2048, next_tokens 0) with seeded synthetic inputs resident in HBM.
 Metric: effective TFLOP/s of forward + backward counting only unmasked
 (query, key) pairs: 4*D flops per pair forward (Q K^T and P V), 10*D per pair
 backward (the five products S, dP, dV, dK, dQ; recomputing S is part of the
-method).  Also reported: the fraction of the bf16 dense MFMA peak, the
+method; the second recomputation of S and dP by the dQ kernel of the bf16
+two-pass backward is not counted).  Also reported: the fraction of the bf16 dense MFMA peak, the
 roofline position of the dominant kernel (timed with HIP events on the
 launching stream), and the fp64 CPU oracle timed on a bounded sample.
 
@@ -35,9 +36,11 @@ PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = {
     "forward": "transformer_attention_tnd_amd/csrc/swa_fwd.hip",
     "backward": "transformer_attention_tnd_amd/csrc/swa_bwd.hip",
+    "bwd_dq": "transformer_attention_tnd_amd/csrc/swa_bwd.hip",
     "bwd_pre": "transformer_attention_tnd_amd/csrc/swa_bwd.hip",
     "dq_finalize": "transformer_attention_tnd_amd/csrc/swa_bwd.hip",
 }
+BWD_KERNELS = ("bwd_pre", "backward", "bwd_dq", "dq_finalize")
 
 
 def allowed_pairs(cu_q, cu_kv, mode, pre, nxt):
@@ -181,9 +184,10 @@ def main():
     swa.swa_profile_enable(False)
     total_ms = e0.elapsed_time(e1)
     kern = {}
-    for kind in ("forward", "bwd_pre", "backward", "dq_finalize"):
+    for kind in ("forward",) + BWD_KERNELS:
         ms, n = swa.swa_profile_read(kind)
-        kern[kind] = {"avg_ms": ms / max(n, 1), "launches": n}
+        if n:
+            kern[kind] = {"avg_ms": ms / n, "launches": n}
 
     pairs = allowed_pairs(p.cu_seqlens_q, p.cu_seqlens_kv, p.sparse_mode, p.pre_tokens,
                           p.next_tokens)
@@ -192,15 +196,22 @@ def main():
     ms_step = total_ms / args.steps
     value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
     elem = q.element_size()
+    two_pass = "bwd_dq" in kern
     # algorithmic work per launch of each kernel
     algo = {
         "forward": ("mfma", f_fwd / 1e12, "TFLOP/s"),
-        "backward": ("mfma", f_bwd / 1e12, "TFLOP/s"),
-        # per (token, head): read dY, O and two statistics; write D, lse2 and zero dq_acc
-        "bwd_pre": ("hbm", T * N * (2 * D * elem + 8 + 8 + 4 * D) / 1e9, "GB/s"),
+        # two-pass: the dK/dV kernel does S, dP, dV, dK (8*D per pair), the dQ
+        # kernel adds dQ (2*D; its recomputed S and dP are not counted)
+        "backward": ("mfma", (0.8 if two_pass else 1.0) * f_bwd / 1e12, "TFLOP/s"),
+        "bwd_dq": ("mfma", 0.2 * f_bwd / 1e12, "TFLOP/s"),
+        # per (token, head): read dY, O and two statistics; write D and lse2
+        # (and zero the fp32 dq accumulator in the one-pass backward)
+        "bwd_pre": ("hbm", T * N * (2 * D * elem + 8 + 8 + (0 if two_pass else 4 * D)) / 1e9,
+                    "GB/s"),
         # per (token, head): read the fp32 accumulator, write dq
         "dq_finalize": ("hbm", T * N * (4 * D + elem * D) / 1e9, "GB/s"),
     }
+    algo = {kk: vv for kk, vv in algo.items() if kk in kern}
     for kind, (bound, work, unit) in algo.items():
         kern[kind]["achieved"] = work / (kern[kind]["avg_ms"] * 1e-3)
         kern[kind]["unit"] = unit
@@ -220,7 +231,7 @@ def main():
         cpu = cpu_baseline(p, N, pairs)
 
     t_f = kern["forward"]["avg_ms"]
-    t_b = sum(kern[kk]["avg_ms"] for kk in ("bwd_pre", "backward", "dq_finalize"))
+    t_b = sum(kern[kk]["avg_ms"] for kk in BWD_KERNELS if kk in kern)
     line = {
         "metric": "effective TFLOP/s fwd+bwd (unmasked FLOPs) and % of bf16 MFMA peak",
         "value": value,

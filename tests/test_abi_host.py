@@ -120,8 +120,10 @@ def compare_schedule(cu_q, cu_kv, mode, pre, nxt, direction):
     assert len(order) == len(got)
     for v in got.values():
         assert [t for t, _ in v] == sorted(t for t, _ in v)
+    # directions 0 (forward) and 2 (bf16 backward dQ) walk query blocks over
+    # key tiles, direction 1 (backward dK/dV) key blocks over query tiles
     expect = oracle.enumerate_tiles(cu_q, cu_kv, mode, pre, nxt, bi, bt,
-                                    "fwd" if direction == 0 else "bwd")
+                                    "bwd" if direction == 1 else "fwd")
     # the oracle keys batches by participating index; map to batch index
     seqs = oracle.sequences(cu_q)
     exp = {(b, it): v for (b, it), v in expect.items()}
@@ -143,13 +145,13 @@ SCHEDULE_CASES = [
 ]
 
 
-@pytest.mark.parametrize("direction", [0, 1])
+@pytest.mark.parametrize("direction", [0, 1, 2])
 @pytest.mark.parametrize("case", SCHEDULE_CASES)
 def test_schedule_matches_bruteforce_enumeration(case, direction):
     compare_schedule(*case, direction)
 
 
-@pytest.mark.parametrize("direction", [0, 1])
+@pytest.mark.parametrize("direction", [0, 1, 2])
 def test_headline_schedule_skip_pattern(direction):
     p = workloads.make_problem(workloads.HEADLINE)
     got = compare_schedule(p.cu_seqlens_q, p.cu_seqlens_kv, 4, 2048, 0, direction)
@@ -158,8 +160,9 @@ def test_headline_schedule_skip_pattern(direction):
     # 128-row query blocks: 112 blocks see 2176 keys = 34 tiles of 64, block
     # qb < 16 sees 2 (qb + 1) tiles -> 112 * 34 + 272 = 4080 visited of the
     # 128 * 256 = 32768 tiles (12.45 %); 4 partial tiles per complete-band
-    # block (two at each band edge) -> 480 partial.  The backward (128-key
-    # blocks over 64-row tiles) is the mirror image.
+    # block (two at each band edge) -> 480 partial.  The backward dK/dV
+    # schedule (128-key blocks over 64-row tiles) is the mirror image, and the
+    # dQ schedule uses the forward's 128-row blocks.
     assert (vis, full) == (4080, 3600)
 
 

@@ -11,26 +11,26 @@
 //
 // swa_bwd_pre_kernel: D and the per-row log2-domain normaliser
 //   lse2 = softmax_max * log2(e) + log2(softmax_sum), so that P = exp2(s*c - lse2)
-//   with c = scale * log2(e); it also zeroes the fp32 dq accumulator.
-// swa_bwd_kernel (fp32 inputs) and swa_bwd_bf16_kernel: one workgroup per
-//   (block of 128 keys, head); each of its 4 waves owns 32 keys and keeps its
-//   dK, dV accumulators in registers while it walks the query tiles of the
-//   band.
+//   with c = scale * log2(e); for fp32 it also zeroes the dq accumulator.
+// bf16: swa_bwd_kv_kernel (dK, dV) and swa_bwd_dq_kernel (dQ), the two-pass
+//   structure with no atomics (described below).
+// fp32: swa_bwd_kernel, one pass: one workgroup per (block of 128 keys,
+//   head); each of its 4 waves owns 32 keys and keeps its dK, dV
+//   accumulators in registers while it walks the query tiles of the band.
 //   Scores are formed as S = Q K^T (queries as rows, the wave's keys as
 //   columns), so P and dS come out of the accumulators in the operand layout
 //   of dV^T += dY^T P and dK^T += Q^T dS.  Q and dY tiles go from HBM
 //   straight into swizzled row-major LDS tiles (double-buffered, rows past
-//   the sequence read as zero); the transposed operands Q^T and dY^T come
-//   from them through transposing LDS reads.  dS is written to LDS and each
-//   wave forms dQ for one 32-wide head-dim block over all 128 keys, added to
-//   the fp32 accumulator with atomics
-//   (non-deterministic summation order, as the explainer section 6.1
-//   describes for the default backward).
-// swa_dq_finalize_kernel: dq = scale * dq_acc rounded to the output type.
+//   the sequence read as zero).  dS is written to LDS and each wave forms dQ
+//   for one 32-wide head-dim block over all 128 keys, added to the fp32
+//   accumulator with atomics (non-deterministic summation order, as the
+//   explainer section 6.1 describes for the default backward);
+//   swa_dq_finalize_kernel then writes dq = scale * dq_acc in the output type.
 
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "swa_common.hpp"
 
@@ -52,9 +52,11 @@ __global__ __launch_bounds__(256) void swa_bwd_pre_kernel(BwdPreArgs a) {
   for (int e = 0; e < EPV; ++e) acc += to_f32(vec_elem<T>(vy, e)) * to_f32(vec_elem<T>(vo, e));
 #pragma unroll
   for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-  float* z = a.dq_acc + row * D + ch * EPV;
+  if (a.dq_acc) {
+    float* z = a.dq_acc + row * D + ch * EPV;
 #pragma unroll
-  for (int e = 0; e < EPV; e += 4) *reinterpret_cast<floatx4*>(z + e) = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int e = 0; e < EPV; e += 4) *reinterpret_cast<floatx4*>(z + e) = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
   if (ch == 0) {
     const int64_t tok = row / a.num_heads, head = row - tok * a.num_heads;
     const int64_t at = head * a.t_q + tok;  // head-major so that a tile's rows are contiguous
@@ -333,43 +335,79 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kernel(BwdArgs a) {
   }
 }
 
-// bf16 main kernel (head_dim 64 or 128): the math and the work split of
-// swa_bwd_kernel, arranged so that every matrix product reads at most one
-// operand from LDS:
-//   - each wave keeps its 32 K and V rows in registers (B operands of S and
-//     dP), and the K block's columns of its dQ head-dim block (B operand of
-//     dQ = dS K), built once through transposing LDS reads;
-//   - dS tiles are double-buffered, so one barrier per query tile separates
-//     writing dS from reading it, and the dQ product of tile t-1 runs inside
-//     the body of tile t, next to tile t's own products;
-//   - the dQ atomics carry the row in the lane offset: rows past the end of
-//     the sequence fall outside the buffer range and the hardware range check
-//     drops them, so the tile body has no branches.
+// bf16 backward in two kernels, no atomics (deterministic): the two-pass
+// structure of the PyPTO-Gym FlashAttentionScoreGrad article (两趟循环结构),
+// which recomputes P and dS in both passes.
+//   swa_bwd_kv_kernel: one workgroup per (block of 128 keys, head); each of
+//     its 4 waves owns 32 keys, keeps its K and V rows in registers (B
+//     operands of S = Q K^T and dP = dY V^T) and its dK^T, dV^T accumulators,
+//     and walks the query tiles (64 rows) of the band.
+//   swa_bwd_dq_kernel: one workgroup per (block of 128 query rows, head);
+//     each wave owns 32 rows, keeps its Q and dY rows in registers (B operands
+//     of S^T = K Q^T and dP^T = V dY^T) and its dQ^T accumulator, and walks the
+//     key tiles (64 keys) of the band; dQ^T += K^T dS^T takes K^T from the
+//     key tile through transposing LDS reads.  dq is written once, in the
+//     input type.
+// Both are organised for one wave per SIMD.  The products of a tile form one
+// software pipeline in a fixed order; each LDS operand is read a fixed number
+// of products ahead into a small register ring, and the vector work (the
+// softmax elements) is spread over the slots between products, with
+// scheduling fences keeping that order.  LDS holds two slabs (the tiles of
+// query/key tile t and t+1, loaded straight from HBM); the lane offsets into
+// them sit in registers and move to the other slab once per tile.
+#ifndef SWA_BWD_AHEAD
+#define SWA_BWD_AHEAD 5
+#endif
+template <typename F, int... I>
+__device__ inline void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ inline void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Operands of the transposing reads (two 64-bit reads -> one 8 x bf16 operand)
+__device__ inline bf16x8 tr_pair(const char* p0, const char* p1) {
+  const shortx4 x = lds_read_tr16(p0);
+  const shortx4 y = lds_read_tr16(p1);
+  typedef short shortx8 __attribute__((ext_vector_type(8)));
+  const shortx8 v = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Lane offsets of the transposing operand reads of a swizzled [rows, RB]
+// tile (accumulator row order, see tr_operand): rows 4h + l%16/4 and 8 more,
+// head-dim block db.
+template <int RB>
+__device__ inline void tr_offsets(int lane, int db, int& o0, int& o1) {
+  const int s16 = lane & 15, h = lane >> 5;
+  const int col2 = 2 * (32 * db + 16 * ((lane >> 4) & 1) + 4 * (s16 & 3));
+  o0 = tile_off<RB>(4 * h + (s16 >> 2), col2);
+  o1 = tile_off<RB>(4 * h + (s16 >> 2) + 8, col2);
+}
+
 template <int D>
-__global__ __launch_bounds__(256, 1) void swa_bwd_bf16_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
   using M = Mfma<bf16>;
   using op_t = M::op_t;
   constexpr int BN = BWD_BN;           // keys per workgroup
   constexpr int BM = 64;               // query rows per tile
-  constexpr int QB = BM / 32;          // 32-row query blocks per tile
-  constexpr int RB = D * 2;            // Q / dY / K row bytes
+  constexpr int RB = D * 2;            // row bytes
   constexpr int QTB = BM * RB;         // Q or dY tile bytes
-  constexpr int SRB = BN * 2;          // dS row bytes
-  constexpr int STB = BM * SRB;        // dS tile bytes
+  constexpr int SLAB = 2 * QTB;        // Q | dY
   constexpr int NDB = D / 32;          // head-dim blocks
   constexpr int DSTEPS = D / 16;       // contraction steps over d
-  constexpr int KSTEPS = BN / 16;      // contraction steps over the keys
-  constexpr int WPD = 4 / NDB;         // waves per head-dim block in dQ
-  constexpr int TASKS = QB * NDB / 4;  // 32x32 dQ blocks per wave
+  // products of one tile, in issue order: S/dP of rows 0-31, of rows 32-63,
+  // dV/dK of rows 0-31, of rows 32-63
+  constexpr int NS = 2 * DSTEPS, NV = 4 * NDB;
+  constexpr int G_S1 = NS, G_V0 = 2 * NS, G_V1 = G_V0 + NV, NOPS = G_V1 + NV;
+  constexpr int AHEAD = SWA_BWD_AHEAD, RING = AHEAD + 1;
   static_assert(BN == 128 && (D == 64 || D == 128), "4 waves x 32 keys, 64-row tiles");
-  static_assert(BN * RB <= 2 * STB, "the K block is staged in the dS buffers");
 
-  __shared__ __attribute__((aligned(1024))) char lds[4 * QTB + 2 * STB];
+  __shared__ __attribute__((aligned(1024))) char lds[2 * SLAB];
   __shared__ floatx4 lse_s[2][BM / 4];   // lse2 of the tile's rows
   __shared__ floatx4 drow_s[2][BM / 4];  // D of the tile's rows
-  char* const qbuf = lds;            // Q tiles [2]
-  char* const ybuf = lds + 2 * QTB;  // dY tiles [2]
-  char* const sbuf = lds + 4 * QTB;  // dS tiles [2]; the K block during set-up
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, h = lane >> 5, c = lane & 31;
@@ -383,15 +421,10 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_bf16_kernel(BwdArgs a) {
   const bf16* vg = static_cast<const bf16*>(a.v) + (int64_t)it.kv_base * ld + head * D;
   const float* lse_g = a.lse2 + (int64_t)head * a.t_q + it.q_base;
   const float* drow_g = a.drow + (int64_t)head * a.t_q + it.q_base;
-  float* const dq_g = a.dq_acc + (int64_t)it.q_base * ld + head * D;
-  const int kb0 = it.block * BN;       // first key of the block (sequence-local)
-  const int kw = kb0 + 32 * w + c;     // this lane's key
+  const int kw = it.block * BN + 32 * w + c;  // this lane's key (sequence-local)
   const int lo = it.tiles[0] & 0xffff, hi = (it.tiles[0] >> 16) & 0xffff;
   const int flo = it.full[0] & 0xffff, fhi = (it.full[0] >> 16) & 0xffff;
   const float c2 = a.scale_log2;
-  const int wd = w % NDB;              // head-dim block of this wave's dQ
-  const int ld4 = (int)(ld * 4);       // dq accumulator row stride in bytes
-  const int dq_lane_off = (4 * h * (int)ld + 32 * wd + c) * 4;
 
   floatx16 dk[NDB], dv[NDB];
 #pragma unroll
@@ -410,14 +443,32 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_bf16_kernel(BwdArgs a) {
       vr[t] = ok ? M::load(vg + off + 16 * t) : op_t{};
     }
   }
-  // B operand of dQ: lane (column 32 wd + c) holds K[kb0 + 16t + 8h + e][32 wd + c]
-  op_t kq[KSTEPS];
+  // Rows allowed for this lane's key: i in [i_min, i_max] (empty if the key
+  // is past the sequence), from the band rule -pre <= kw - i <= next.
+  int i_min = 0, i_max = it.sq - 1;
+  if (a.mode == 4) {  // 64-bit: pre / next may be near the int range
+    const int64_t lo64 = (int64_t)kw - a.next, hi64 = (int64_t)kw + a.pre;
+    i_min = lo64 < 0 ? 0 : (lo64 > it.sq ? it.sq : (int)lo64);
+    i_max = hi64 < i_max ? (hi64 < -1 ? -1 : (int)hi64) : i_max;
+  }
+  if (kw >= it.skv) i_max = -1;
+
+  // Lane offsets (slab of the current tile).  Rows 16 apart share a swizzle,
+  // so the 32-row block, the 16-row step and Q vs dY are immediate offsets.
+  int oq[DSTEPS];   // 128-bit read of row c, chunk 2t + h
+  int otr[NDB][2];  // transposing reads, head-dim block db
+  int olr = 16 * h; // lse2 / D of rows 4h .. 4h + 3 of each 8
+#pragma unroll
+  for (int t = 0; t < DSTEPS; ++t) oq[t] = tile_off<RB>(c, (16 * t + 8 * h) * 2);
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) tr_offsets<RB>(lane, db, otr[db][0], otr[db][1]);
 
   float sreg = 0.f;
-  auto load_qtile = [&](int tile, int b) {
+  auto load_tile = [&](int tile, int b) {
     const int nvalid = it.sq - tile * BM;
-    tile_load_lds<bf16, D, BM>(qg + (int64_t)tile * BM * ld, ld, nvalid, qbuf + b * QTB, tid);
-    tile_load_lds<bf16, D, BM>(dyg + (int64_t)tile * BM * ld, ld, nvalid, ybuf + b * QTB, tid);
+    char* slab = lds + b * SLAB;
+    tile_load_lds<bf16, D, BM>(qg + (int64_t)tile * BM * ld, ld, nvalid, slab, tid);
+    tile_load_lds<bf16, D, BM>(dyg + (int64_t)tile * BM * ld, ld, nvalid, slab + QTB, tid);
     if (tid < 2 * BM) {
       const int row = tid & (BM - 1), i = tile * BM + row;
       if (tid < BM)
@@ -432,183 +483,140 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_bf16_kernel(BwdArgs a) {
     else if (tid < 2 * BM)
       reinterpret_cast<float*>(drow_s[b])[tid - BM] = sreg;
   };
+  auto rd128 = [&](int off) { return *reinterpret_cast<const op_t*>(lds + off); };
 
-  // S = Q K^T and dP = dY V^T of query block qb (rows 32 qb + c_row(r, h),
-  // column: this lane's key); the two chains alternate.
-  auto sdp = [&](const char* qt, const char* yt, int qb, floatx16& s, floatx16& dp) {
-    s = floatx16{};
-    dp = floatx16{};
-#pragma unroll
-    for (int t = 0; t < DSTEPS; ++t) {
-      const int off = tile_off<RB>(32 * qb + c, (16 * t + 8 * h) * 2);
-      s = M::mma(M::load(reinterpret_cast<const bf16*>(qt + off)), kr[t], s);
-      dp = M::mma(M::load(reinterpret_cast<const bf16*>(yt + off)), vr[t], dp);
-    }
-  };
-  // P = exp2(s c - lse2) and dS = P (dP - D), packed as operands whose
-  // contraction slots follow the accumulator rows.
-  // Rows allowed for this lane's key: i in [i_min, i_max] (empty if the key
-  // is past the sequence), from the band rule -pre <= kw - i <= next.
-  int i_min = 0, i_max = it.sq - 1;
-  if (a.mode == 4) {  // 64-bit: pre / next may be near the int range
-    const int64_t lo64 = (int64_t)kw - a.next, hi64 = (int64_t)kw + a.pre;
-    i_min = lo64 < 0 ? 0 : (lo64 > it.sq ? it.sq : (int)lo64);
-    i_max = hi64 < i_max ? (hi64 < -1 ? -1 : (int)hi64) : i_max;
-  }
-  if (kw >= it.skv) i_max = -1;
-  auto softmax = [&](auto mask_tag, int tile, int b, int qb, floatx16& s, floatx16& dp, op_t* pk,
-                     op_t* sk) {
+  // One query tile: S, dP, P, dS, dV^T += dY^T P, dK^T += Q^T dS.
+  auto step = [&](auto mask_tag, int tile) {
     constexpr bool kMask = decltype(mask_tag)::value;
-    // row 32 qb + 8 g + 4 h + e of the tile is allowed iff the tile-relative
-    // constant 32 qb + 8 g + e lies in [rel_lo, rel_hi]
+    // row 32 qb + 8 g + 4 h + e is allowed iff 32 qb + 8 g + e is in [rel_lo, rel_hi]
     int rel_lo = 0, rel_hi = 0;
     if constexpr (kMask) {
       rel_lo = i_min - tile * BM - 4 * h;
       rel_hi = i_max - tile * BM - 4 * h;
       asm volatile("" : "+v"(rel_lo), "+v"(rel_hi));
     }
+    op_t ring[RING];
+    floatx16 s[2], dp[2];
+    floatx4 lv[2][4], dv4[2][4];
+    op_t pk[2][2], sk[2][2];
+
+    auto read = [&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (i < G_V0) {
+        constexpr int qb = i / NS, t = (i % NS) / 2, isdp = i % 2;
+        ring[i % RING] = rd128(oq[t] + isdp * QTB + 32 * qb * RB);
+      } else {
+        constexpr int j = i - G_V0, qb = j / NV, jj = j % NV;
+        constexpr int t2 = jj / (2 * NDB), db = (jj / 2) % NDB, isdv = 1 - jj % 2;
+        constexpr int imm = isdv * QTB + (32 * qb + 16 * t2) * RB;
+        ring[i % RING] = tr_pair(lds + otr[db][0] + imm, lds + otr[db][1] + imm);
+      }
+    };
+    auto mfma = [&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      const op_t& x = ring[i % RING];
+      if constexpr (i < G_V0) {
+        constexpr int qb = i / NS, t = (i % NS) / 2;
+        if constexpr (i % 2 == 0)
+          s[qb] = M::mma(x, kr[t], t == 0 ? floatx16{} : s[qb]);
+        else
+          dp[qb] = M::mma(x, vr[t], t == 0 ? floatx16{} : dp[qb]);
+      } else {
+        constexpr int j = i - G_V0, qb = j / NV, jj = j % NV;
+        constexpr int t2 = jj / (2 * NDB), db = (jj / 2) % NDB;
+        if constexpr (jj % 2 == 0)
+          dv[db] = M::mma(x, pk[qb][t2], dv[db]);
+        else
+          dk[db] = M::mma(x, sk[qb][t2], dk[db]);
+      }
+    };
+    // P = exp2(s c - lse2), dS = P (dP - D) of accumulator register r of block
+    // qb; each completed pair is rounded into the operands of dV / dK.
+    auto soft = [&](int qb, int r) {
+      const int g = r >> 2, e = r & 3;
+      float p = __builtin_amdgcn_exp2f(fmaf(s[qb][r], c2, -lv[qb][g][e]));
+      if constexpr (kMask) {
+        const int rel = 32 * qb + 8 * g + e;
+        p = (rel >= rel_lo && rel <= rel_hi) ? p : 0.f;
+      }
+      s[qb][r] = p;
+      dp[qb][r] = p * (dp[qb][r] - dv4[qb][g][e]);
+      if (r & 1) {
+        pk[qb][r >> 3][(r & 7) - 1] = static_cast<bf16>(s[qb][r - 1]);
+        pk[qb][r >> 3][r & 7] = static_cast<bf16>(s[qb][r]);
+        sk[qb][r >> 3][(r & 7) - 1] = static_cast<bf16>(dp[qb][r - 1]);
+        sk[qb][r >> 3][r & 7] = static_cast<bf16>(dp[qb][r]);
+      }
+    };
+    auto valu = [&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      // lse2 / D rows of block qb early in its S / dP products
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int rb = 32 * qb + 8 * g + 4 * h;
-      const floatx4 l4 = lse_s[b][rb / 4];
-      const floatx4 d4 = drow_s[b][rb / 4];
+      for (int qb = 0; qb < 2; ++qb) {
+        if (m == qb * NS + 1) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * g + e;
-        float p = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -l4[e]));
-        if constexpr (kMask) {
-          const int rel = 32 * qb + 8 * g + e;
-          p = (rel >= rel_lo && rel <= rel_hi) ? p : 0.f;
+          for (int g = 0; g < 4; ++g) {
+            const int off = olr + (32 * qb + 8 * g) * 4;
+            lv[qb][g] = *reinterpret_cast<const floatx4*>(reinterpret_cast<const char*>(lse_s) + off);
+            dv4[qb][g] = *reinterpret_cast<const floatx4*>(reinterpret_cast<const char*>(drow_s) + off);
+          }
         }
-        s[r] = p;
-        dp[r] = p * (dp[r] - d4[e]);
       }
-    }
-#pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2) {
-      pk[t2] = M::pack(s, t2);
-      sk[t2] = M::pack(dp, t2);
-    }
-  };
-  // dS of query block qb to the LDS tile.  Adjacent lanes hold adjacent keys
-  // of the same rows: each lane swaps one packed pair with its neighbour and
-  // stores two keys of one row as one 32-bit word (even lanes the rows of
-  // accumulator registers r, odd lanes those of r + 1).
-  auto store_ds = [&](char* st, int qb, const op_t* sk) {
-    const bool odd = c & 1;
-    const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
-    const int col = (32 * w + (c & ~1)) * 2;
-#pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2) {
-      const u32x4 wv = __builtin_bit_cast(u32x4, sk[t2]);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t mine = wv[k];
-        const uint32_t other = (uint32_t)__builtin_amdgcn_mov_dpp((int)mine, 0xB1, 0xF, 0xF, false);
-        const uint32_t word = __builtin_amdgcn_perm(other, mine, sel);
-        const int row = 32 * qb + c_row(8 * t2 + 2 * k, h) + (odd ? 1 : 0);
-        *reinterpret_cast<uint32_t*>(st + tile_off<SRB>(row, col)) = word;
-      }
-    }
-  };
-  // dV^T += dY^T P and dK^T += Q^T dS over the 32 rows of query block qb
-  auto dvdk = [&](const char* qt, const char* yt, int qb, const op_t* pk, const op_t* sk) {
-#pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const op_t ya = tr_operand<RB, true>(yt, 32 * qb + 16 * t2, db, lane);
-        const op_t qa = tr_operand<RB, true>(qt, 32 * qb + 16 * t2, db, lane);
-        dv[db] = M::mma(ya, pk[t2], dv[db]);
-        dk[db] = M::mma(qa, sk[t2], dk[db]);
-      }
-    }
-  };
-  // dQ blocks (rows 32 qb, head-dim block wd) = dS K of one tile
-  auto dq_mma = [&](const char* st, floatx16* acc) {
-#pragma unroll
-    for (int k = 0; k < TASKS; ++k) acc[k] = floatx16{};
-#pragma unroll
-    for (int t = 0; t < KSTEPS; ++t) {
-#pragma unroll
-      for (int k = 0; k < TASKS; ++k) {
-        const int qb = w / NDB + k * WPD;
-        const op_t sa = M::load(
-            reinterpret_cast<const bf16*>(st + tile_off<SRB>(32 * qb + c, (16 * t + 8 * h) * 2)));
-        acc[k] = M::mma(sa, kq[t], acc[k]);
-      }
-    }
-  };
-  // add them to the fp32 accumulator rows of `tile` (nothing when !valid)
-  auto dq_add = [&](int tile, bool valid, const floatx16* acc) {
-    int nrows = it.sq - tile * BM;
-    nrows = nrows < BM ? nrows : BM;
-    const int nbytes = valid && nrows > 0 ? (int)(((int64_t)(nrows - 1) * ld + D) * 4) : 0;
-    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        dq_g + (int64_t)(valid ? tile : lo) * BM * ld, (short)0, nbytes, 0x00020000);
-    // (opaque copy: the 16 offsets per block are formed here, not kept live)
-    int lane_off = dq_lane_off;
-    asm volatile("" : "+v"(lane_off));
-#pragma unroll
-    for (int k = 0; k < TASKS; ++k) {
-      const int qb = w / NDB + k * WPD;
+      // softmax of block 0 over the S / dP products of block 1; of block 1:
+      // the first contraction step over the dV / dK products of block 0, the
+      // second over the first half of those of block 1
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int voff = lane_off + (32 * qb + 8 * (r >> 2) + (r & 3)) * ld4;
-        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[k][r], rsrc, voff, 0, 0);
+        if (m == G_S1 + (r * NS) / 16) soft(0, r);
+        if (r < 8 && m == G_V0 + (r * NV) / 8) soft(1, r);
+        if (r >= 8 && m == G_V1 + ((r - 8) * NV) / 16) soft(1, r);
       }
-    }
-  };
+    };
 
-  // scheduling fence: keeps each phase's operand reads inside the phase
-  auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
-  // One query tile: its S, dP, P, dS, dV, dK, plus dQ of the previous tile.
-  auto step = [&](auto mask_tag, int tile, int b) {
-    const char* qt = qbuf + b * QTB;
-    const char* yt = ybuf + b * QTB;
-    char* st = sbuf + b * STB;
-    const char* sp = sbuf + (b ^ 1) * STB;
-    floatx16 s0, dp0, s1, dp1, acc[TASKS];
-    op_t pk0[2], sk0[2], pk1[2], sk1[2];
-    sdp(qt, yt, 0, s0, dp0);
-    fence();
-    dq_mma(sp, acc);
-    fence();
-    dq_add(tile - 1, tile > lo, acc);
-    softmax(mask_tag, tile, b, 0, s0, dp0, pk0, sk0);
-    store_ds(st, 0, sk0);
-    fence();
-    sdp(qt, yt, 1, s1, dp1);
-    fence();
-    dvdk(qt, yt, 0, pk0, sk0);
-    fence();
-    softmax(mask_tag, tile, b, 1, s1, dp1, pk1, sk1);
-    store_ds(st, 1, sk1);
-    fence();
-    dvdk(qt, yt, 1, pk1, sk1);
-    fence();
+    static_for<NOPS + AHEAD>([&](auto sc) {
+      constexpr int sl = decltype(sc)::value;
+      if constexpr (sl < NOPS) read(std::integral_constant<int, sl>{});
+      if constexpr (sl >= AHEAD) {
+        mfma(std::integral_constant<int, sl - AHEAD>{});
+        valu(std::integral_constant<int, sl - AHEAD>{});
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
   };
 
   if (lo <= hi) {
-    tile_load_lds<bf16, D, BN>(kg + (int64_t)kb0 * ld, ld, it.skv - kb0, sbuf, tid);
-    load_qtile(lo, 0);
+    load_tile(lo, 0);
     wait_vmem();
     store_rows(0);
     __syncthreads();
-#pragma unroll
-    for (int t = 0; t < KSTEPS; ++t) kq[t] = tr_operand<RB, false>(sbuf, 16 * t, wd, lane);
-    if (lo < hi) load_qtile(lo + 1, 1);
-    __syncthreads();  // the K block is read before dS overwrites it
+    if (lo < hi) load_tile(lo + 1, 1);
   }
+  auto flip = [&](int b) {  // move the lane offsets to the other slab
+    const int dr = b ? -SLAB : SLAB;
+#pragma unroll
+    for (int t = 0; t < DSTEPS; ++t) {
+      oq[t] += dr;
+      asm volatile("" : "+v"(oq[t]));
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      otr[db][0] += dr;
+      otr[db][1] += dr;
+      asm volatile("" : "+v"(otr[db][0]), "+v"(otr[db][1]));
+    }
+    olr += b ? -(int)sizeof(lse_s[0]) : (int)sizeof(lse_s[0]);
+    asm volatile("" : "+v"(olr));
+  };
   // tiles [from, to] in order, each body branch-free (masked or not)
   auto run = [&](auto mask_tag, int from, int to) {
     for (int tile = from; tile <= to; ++tile) {
       const int b = (tile - lo) & 1;
-      step(mask_tag, tile, b);
+      step(mask_tag, tile);
       if (tile < hi) store_rows(b ^ 1);
       wait_vmem();
       __syncthreads();
-      if (tile + 2 <= hi) load_qtile(tile + 2, b);
+      if (tile + 2 <= hi) load_tile(tile + 2, b);
+      flip(b);
     }
   };
   if (flo <= fhi) {  // masked tiles before and after the mask-free range
@@ -618,13 +626,8 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_bf16_kernel(BwdArgs a) {
   } else {
     run(std::true_type{}, lo, hi);
   }
-  if (lo <= hi) {
-    floatx16 acc[TASKS];
-    dq_mma(sbuf + ((hi - lo) & 1) * STB, acc);
-    dq_add(hi, true, acc);
-  }
 
-  // epilogue: this lane's key column of dK^T / dV^T
+  // this lane's key column of dK^T / dV^T
   if (kw < it.skv) {
     const int64_t tok = (int64_t)it.kv_base + kw;
     bf16* dkp = static_cast<bf16*>(a.dk) + tok * ld + head * D;
@@ -642,6 +645,217 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_bf16_kernel(BwdArgs a) {
         }
         *reinterpret_cast<bf16x4*>(dkp + d0) = k4;
         *reinterpret_cast<bf16x4*>(dvp + d0) = v4;
+      }
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void swa_bwd_dq_kernel(BwdArgs a) {
+  using M = Mfma<bf16>;
+  using op_t = M::op_t;
+  constexpr int BQ = 128;              // query rows per workgroup
+  constexpr int BN = 64;               // keys per tile
+  constexpr int RB = D * 2;            // row bytes
+  constexpr int KTB = BN * RB;         // K or V tile bytes
+  constexpr int SLAB = 2 * KTB;        // K | V
+  constexpr int NDB = D / 32;          // head-dim blocks
+  constexpr int DSTEPS = D / 16;       // contraction steps over d
+  // products of one tile, in issue order: S^T/dP^T of keys 0-31, of keys
+  // 32-63, dQ^T from keys 0-31, from keys 32-63
+  constexpr int NS = 2 * DSTEPS, NQ = 2 * NDB;
+  constexpr int G_S1 = NS, G_Q0 = 2 * NS, G_Q1 = G_Q0 + NQ, NOPS = G_Q1 + NQ;
+  constexpr int AHEAD = SWA_BWD_AHEAD, RING = AHEAD + 1;
+  static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+
+  __shared__ __attribute__((aligned(1024))) char lds[2 * SLAB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, h = lane >> 5, c = lane & 31;
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int head = L / a.n_items;
+  const Item it = a.items[L - head * a.n_items];
+  const int64_t ld = (int64_t)a.num_heads * D;
+  const bf16* qg = static_cast<const bf16*>(a.q) + (int64_t)it.q_base * ld + head * D;
+  const bf16* dyg = static_cast<const bf16*>(a.dy) + (int64_t)it.q_base * ld + head * D;
+  const bf16* kg = static_cast<const bf16*>(a.k) + (int64_t)it.kv_base * ld + head * D;
+  const bf16* vg = static_cast<const bf16*>(a.v) + (int64_t)it.kv_base * ld + head * D;
+  const int qrow = it.block * BQ + 32 * w + c;  // this lane's query row (sequence-local)
+  const int lo = it.tiles[0] & 0xffff, hi = (it.tiles[0] >> 16) & 0xffff;
+  const int flo = it.full[0] & 0xffff, fhi = (it.full[0] >> 16) & 0xffff;
+  const float c2 = a.scale_log2;
+
+  // B operands of S^T and dP^T: lane (column qrow) holds Q[qrow][16t + 8h + e], dY likewise
+  op_t qf[DSTEPS], yf[DSTEPS];
+  float lse = INFINITY, drow = 0.f;  // this row's lse2 and D (rows past the end: P = 0)
+  {
+    const bool ok = qrow < it.sq;
+    const int64_t off = (int64_t)(ok ? qrow : 0) * ld + 8 * h;
+#pragma unroll
+    for (int t = 0; t < DSTEPS; ++t) {
+      qf[t] = ok ? M::load(qg + off + 16 * t) : op_t{};
+      yf[t] = ok ? M::load(dyg + off + 16 * t) : op_t{};
+    }
+    if (ok) {
+      lse = a.lse2[(int64_t)head * a.t_q + it.q_base + qrow];
+      drow = a.drow[(int64_t)head * a.t_q + it.q_base + qrow];
+    }
+  }
+  // Keys allowed for this lane's row: j in [j_min, j_max] (empty past the end)
+  int j_min = 0, j_max = it.skv - 1;
+  if (a.mode == 4) {  // 64-bit: pre / next may be near the int range
+    const int64_t lo64 = (int64_t)qrow - a.pre, hi64 = (int64_t)qrow + a.next;
+    j_min = lo64 < 0 ? 0 : (lo64 > it.skv ? it.skv : (int)lo64);
+    j_max = hi64 < j_max ? (hi64 < -1 ? -1 : (int)hi64) : j_max;
+  }
+  if (qrow >= it.sq) j_max = -1;
+
+  floatx16 acc[NDB];  // dQ^T: rows = head dim 32 db + c_row(r, h), column = this lane's row
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = floatx16{};
+
+  // Lane offsets (slab of the current tile)
+  int ok_[DSTEPS];  // 128-bit read of key row c, chunk 2t + h
+  int otr[NDB][2];  // transposing reads of the K tile, head-dim block db
+#pragma unroll
+  for (int t = 0; t < DSTEPS; ++t) ok_[t] = tile_off<RB>(c, (16 * t + 8 * h) * 2);
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) tr_offsets<RB>(lane, db, otr[db][0], otr[db][1]);
+
+  auto load_tile = [&](int tile, int b) {
+    const int nvalid = it.skv - tile * BN;
+    char* slab = lds + b * SLAB;
+    tile_load_lds<bf16, D, BN>(kg + (int64_t)tile * BN * ld, ld, nvalid, slab, tid);
+    tile_load_lds<bf16, D, BN>(vg + (int64_t)tile * BN * ld, ld, nvalid, slab + KTB, tid);
+  };
+  auto rd128 = [&](int off) { return *reinterpret_cast<const op_t*>(lds + off); };
+
+  // One key tile: S^T, dP^T, P, dS, dQ^T += K^T dS^T.
+  auto step = [&](auto mask_tag, int tile) {
+    constexpr bool kMask = decltype(mask_tag)::value;
+    // key 32 jb + 8 g + 4 h + e of the tile is allowed iff 32 jb + 8 g + e is in [rel_lo, rel_hi]
+    int rel_lo = 0, rel_hi = 0;
+    if constexpr (kMask) {
+      rel_lo = j_min - tile * BN - 4 * h;
+      rel_hi = j_max - tile * BN - 4 * h;
+      asm volatile("" : "+v"(rel_lo), "+v"(rel_hi));
+    }
+    op_t ring[RING];
+    floatx16 s[2], dp[2];
+    op_t sk[2][2];
+
+    auto read = [&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (i < G_Q0) {
+        constexpr int jb = i / NS, t = (i % NS) / 2, isv = i % 2;
+        ring[i % RING] = rd128(ok_[t] + isv * KTB + 32 * jb * RB);
+      } else {
+        constexpr int j = i - G_Q0, jb = j / NQ, t2 = (j % NQ) / NDB, db = j % NDB;
+        constexpr int imm = (32 * jb + 16 * t2) * RB;
+        ring[i % RING] = tr_pair(lds + otr[db][0] + imm, lds + otr[db][1] + imm);
+      }
+    };
+    auto mfma = [&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      const op_t& x = ring[i % RING];
+      if constexpr (i < G_Q0) {
+        constexpr int jb = i / NS, t = (i % NS) / 2;
+        if constexpr (i % 2 == 0)
+          s[jb] = M::mma(x, qf[t], t == 0 ? floatx16{} : s[jb]);
+        else
+          dp[jb] = M::mma(x, yf[t], t == 0 ? floatx16{} : dp[jb]);
+      } else {
+        constexpr int j = i - G_Q0, jb = j / NQ, t2 = (j % NQ) / NDB, db = j % NDB;
+        acc[db] = M::mma(x, sk[jb][t2], acc[db]);
+      }
+    };
+    // P = exp2(s c - lse2), dS = P (dP - D) of accumulator register r of key
+    // block jb; each completed pair is rounded into the operand of dQ^T.
+    auto soft = [&](int jb, int r) {
+      float p = __builtin_amdgcn_exp2f(fmaf(s[jb][r], c2, -lse));
+      if constexpr (kMask) {
+        const int rel = 32 * jb + 8 * (r >> 2) + (r & 3);
+        p = (rel >= rel_lo && rel <= rel_hi) ? p : 0.f;
+      }
+      dp[jb][r] = p * (dp[jb][r] - drow);
+      if (r & 1) {
+        sk[jb][r >> 3][(r & 7) - 1] = static_cast<bf16>(dp[jb][r - 1]);
+        sk[jb][r >> 3][r & 7] = static_cast<bf16>(dp[jb][r]);
+      }
+    };
+    auto valu = [&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      // softmax of key block 0 over the S^T / dP^T products of block 1; of
+      // block 1: the first contraction step over the dQ products of block 0,
+      // the second over the first half of those of block 1
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if (m == G_S1 + (r * NS) / 16) soft(0, r);
+        if (r < 8 && m == G_Q0 + (r * NQ) / 8) soft(1, r);
+        if (r >= 8 && m == G_Q1 + ((r - 8) * NQ) / 16) soft(1, r);
+      }
+    };
+
+    static_for<NOPS + AHEAD>([&](auto sc) {
+      constexpr int sl = decltype(sc)::value;
+      if constexpr (sl < NOPS) read(std::integral_constant<int, sl>{});
+      if constexpr (sl >= AHEAD) {
+        mfma(std::integral_constant<int, sl - AHEAD>{});
+        valu(std::integral_constant<int, sl - AHEAD>{});
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+  if (lo <= hi) {
+    load_tile(lo, 0);
+    wait_vmem();
+    __syncthreads();
+    if (lo < hi) load_tile(lo + 1, 1);
+  }
+  auto flip = [&](int b) {  // move the lane offsets to the other slab
+    const int dr = b ? -SLAB : SLAB;
+#pragma unroll
+    for (int t = 0; t < DSTEPS; ++t) {
+      ok_[t] += dr;
+      asm volatile("" : "+v"(ok_[t]));
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      otr[db][0] += dr;
+      otr[db][1] += dr;
+      asm volatile("" : "+v"(otr[db][0]), "+v"(otr[db][1]));
+    }
+  };
+  auto run = [&](auto mask_tag, int from, int to) {
+    for (int tile = from; tile <= to; ++tile) {
+      const int b = (tile - lo) & 1;
+      step(mask_tag, tile);
+      wait_vmem();
+      __syncthreads();
+      if (tile + 2 <= hi) load_tile(tile + 2, b);
+      flip(b);
+    }
+  };
+  if (flo <= fhi) {  // masked tiles before and after the mask-free range
+    run(std::true_type{}, lo, flo - 1);
+    run(std::false_type{}, flo, fhi);
+    run(std::true_type{}, fhi + 1, hi);
+  } else {
+    run(std::true_type{}, lo, hi);
+  }
+
+  // dq = scale dQ for this lane's row (zero when the row attends no key)
+  if (qrow < it.sq) {
+    bf16* dqp = static_cast<bf16*>(a.dq) + ((int64_t)it.q_base + qrow) * ld + head * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = static_cast<bf16>(acc[db][4 * g + e] * a.scale);
+        *reinterpret_cast<bf16x4*>(dqp + 32 * db + 8 * g + 4 * h) = v4;
       }
     }
   }
@@ -706,7 +920,7 @@ static int launch_bwd_t(const BwdArgs& a, void* stream) {
   const int64_t nwg = (int64_t)a.n_items * a.num_heads;
   constexpr int BM = bwd_block_q(sizeof(T) == 2 ? 1 : 0, D);
   if constexpr (sizeof(T) == 2)
-    hipLaunchKernelGGL((swa_bwd_bf16_kernel<D>), dim3((unsigned)nwg), dim3(256), 0,
+    hipLaunchKernelGGL((swa_bwd_kv_kernel<D>), dim3((unsigned)nwg), dim3(256), 0,
                        static_cast<hipStream_t>(stream), a);
   else
     hipLaunchKernelGGL((swa_bwd_kernel<T, D, BM>), dim3((unsigned)nwg), dim3(256), 0,
@@ -719,6 +933,17 @@ int launch_backward(const BwdArgs& a, int dtype, int head_dim, void* stream) {
                                          : launch_bwd_t<bf16, 64>(a, stream);
   return head_dim == 128 ? launch_bwd_t<float, 128>(a, stream)
                          : launch_bwd_t<float, 64>(a, stream);
+}
+
+int launch_bwd_dq(const BwdArgs& a, int head_dim, void* stream) {
+  const int64_t nwg = (int64_t)a.n_items * a.num_heads;
+  if (head_dim == 128)
+    hipLaunchKernelGGL((swa_bwd_dq_kernel<128>), dim3((unsigned)nwg), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), a);
+  else
+    hipLaunchKernelGGL((swa_bwd_dq_kernel<64>), dim3((unsigned)nwg), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), a);
+  return (int)hipGetLastError();
 }
 
 int launch_dq_finalize(const FinalizeArgs& a, int dtype, void* stream) {

@@ -134,7 +134,11 @@ int64_t max_items_fwd(int64_t num_seqs, int64_t t_q) {
 int64_t max_items_bwd(int64_t num_seqs, int64_t t_kv) {
   return ceil_div(t_kv, BWD_BN) + num_seqs;
 }
+int64_t max_items_dq(int64_t num_seqs, int64_t t_q) {
+  return ceil_div(t_q, DQ_BM) + num_seqs;
+}
 
+// Backward workspace: dK/dV items, then dQ items | D | lse2 | dq accumulator.
 struct BwdLayout {
   size_t items, drow, lse2, dq_acc, total;
 };
@@ -142,7 +146,7 @@ struct BwdLayout {
 BwdLayout bwd_layout(int64_t num_seqs, int64_t t_q, int64_t t_kv, int64_t n, int64_t d) {
   BwdLayout l;
   l.items = 0;
-  l.drow = align256(sizeof(Item) * max_items_bwd(num_seqs, t_kv));
+  l.drow = align256(sizeof(Item) * (max_items_bwd(num_seqs, t_kv) + max_items_dq(num_seqs, t_q)));
   l.lse2 = l.drow + align256(sizeof(float) * t_q * n);
   l.dq_acc = l.lse2 + align256(sizeof(float) * t_q * n);
   l.total = l.dq_acc + align256(sizeof(float) * t_q * n * d);
@@ -249,6 +253,32 @@ void schedule_backward(const Problem& p, const std::vector<Seq>& seqs,
   }
 }
 
+// dQ schedule (bf16 backward): one item per block of DQ_BM query rows, with
+// the key-tile range of forward_range (tiles of FWD_BN).
+void schedule_dq(const Problem& p, const std::vector<Seq>& seqs, std::vector<Item>& items) {
+  items.clear();
+  for (const Seq& s : seqs) {
+    if (s.sq == 0) continue;
+    const int64_t nqb = ceil_div(s.sq, DQ_BM);
+    for (int64_t qb = 0; qb < nqb; ++qb) {
+      int64_t lo, hi, flo, fhi;
+      forward_range(p, s, qb * DQ_BM, &lo, &hi, &flo, &fhi);
+      Item it{};
+      it.q_base = static_cast<int32_t>(s.q0);
+      it.kv_base = static_cast<int32_t>(s.k0);
+      it.sq = static_cast<int32_t>(s.sq);
+      it.skv = static_cast<int32_t>(s.skv);
+      it.block = static_cast<int32_t>(qb);
+      it.tiles[0] = pack_range(lo, hi);
+      it.full[0] = pack_range(flo, fhi);
+      it.tiles[1] = pack_range(1, 0);
+      it.full[1] = pack_range(1, 0);
+      it.seq = s.b;
+      items.push_back(it);
+    }
+  }
+}
+
 int range_lo(int32_t r) { return r & 0xffff; }
 int range_hi(int32_t r) { return (r >> 16) & 0xffff; }
 int64_t range_len(int32_t r) {
@@ -336,7 +366,8 @@ Problem make_problem(const int64_t* cu_q, const int64_t* cu_kv, int64_t num_seqs
 size_t elem_bytes(int32_t dtype) { return dtype == SWA_DTYPE_FP32 ? 4 : 2; }
 
 // Optional per-kernel timing with HIP events (swa_profile_enable/read).
-enum KernelKind { K_FWD = 0, K_BWD_PRE = 1, K_BWD = 2, K_DQ_FIN = 3, K_FILL = 4, K_KINDS = 5 };
+enum KernelKind { K_FWD = 0, K_BWD_PRE = 1, K_BWD = 2, K_DQ_FIN = 3, K_FILL = 4, K_BWD_DQ = 5,
+                  K_KINDS = 6 };
 struct Profiler {
   std::mutex mu;
   bool on = false;
@@ -485,14 +516,22 @@ swa_status swa_backward(const void* q, const void* k, const void* v, const void*
   if (workspace_bytes < L.total)
     return fail(SWA_ERR_WORKSPACE, "workspace has " + std::to_string(workspace_bytes) +
                                        " bytes, needs " + std::to_string(L.total));
-  std::vector<Item> items;
+  // bf16: dK/dV kernel + dQ kernel (no atomics); fp32: one pass with a dq accumulator
+  const bool two_pass = dtype == SWA_DTYPE_BF16;
+  std::vector<Item> items, dq_items;
   schedule_backward(p, seqs, items);
   order_items(items);
+  if (two_pass) {
+    schedule_dq(p, seqs, dq_items);
+    order_items(dq_items);
+  }
+  const size_t n_kv_items = items.size();
+  items.insert(items.end(), dq_items.begin(), dq_items.end());
   char* ws = static_cast<char*>(workspace);
   if ((s = upload(items, ws + L.items, stream)) != SWA_OK) return s;
   float* drow = reinterpret_cast<float*>(ws + L.drow);
   float* lse2 = reinterpret_cast<float*>(ws + L.lse2);
-  float* dq_acc = reinterpret_cast<float*>(ws + L.dq_acc);
+  float* dq_acc = two_pass ? nullptr : reinterpret_cast<float*>(ws + L.dq_acc);
   int e = 0;
   BwdPreArgs pa{dy, out, softmax_max, softmax_sum, drow, lse2, dq_acc, t_q * num_heads,
                 static_cast<int32_t>(num_heads), static_cast<int32_t>(t_q)};
@@ -500,34 +539,53 @@ swa_status swa_backward(const void* q, const void* k, const void* v, const void*
          return launch_bwd_pre(pa, dtype, static_cast<int>(head_dim), stream);
        })) != 0)
     return fail(SWA_ERR_HIP, hip_error_string(e));
-  if (!items.empty()) {
-    BwdArgs a;
-    a.q = q;
-    a.k = k;
-    a.v = v;
-    a.dy = dy;
-    a.drow = drow;
-    a.lse2 = lse2;
-    a.dq_acc = dq_acc;
-    a.dk = dk;
-    a.dv = dv;
-    a.items = reinterpret_cast<const Item*>(ws + L.items);
-    a.n_items = static_cast<int32_t>(items.size());
-    a.num_heads = static_cast<int32_t>(num_heads);
-    a.t_q = static_cast<int32_t>(t_q);
-    a.scale = static_cast<float>(scale);
-    a.scale_log2 = static_cast<float>(scale * 1.4426950408889634);
-    a.mode = static_cast<int32_t>(sparse_mode);
-    a.pre = clamp_window(pre_tokens);
-    a.next = clamp_window(next_tokens);
+  BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dy = dy;
+  a.drow = drow;
+  a.lse2 = lse2;
+  a.dq_acc = dq_acc;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.items = reinterpret_cast<const Item*>(ws + L.items);
+  a.n_items = static_cast<int32_t>(n_kv_items);
+  a.num_heads = static_cast<int32_t>(num_heads);
+  a.t_q = static_cast<int32_t>(t_q);
+  a.scale = static_cast<float>(scale);
+  a.scale_log2 = static_cast<float>(scale * 1.4426950408889634);
+  a.mode = static_cast<int32_t>(sparse_mode);
+  a.pre = clamp_window(pre_tokens);
+  a.next = clamp_window(next_tokens);
+  if (n_kv_items > 0) {
     if ((e = timed_launch(K_BWD, stream, [&] {
            return launch_backward(a, dtype, static_cast<int>(head_dim), stream);
          })) != 0)
       return fail(SWA_ERR_HIP, hip_error_string(e));
   }
-  FinalizeArgs fa{dq_acc, dq, static_cast<float>(scale), t_q * num_heads * head_dim};
-  if ((e = timed_launch(K_DQ_FIN, stream, [&] { return launch_dq_finalize(fa, dtype, stream); })) != 0)
-    return fail(SWA_ERR_HIP, hip_error_string(e));
+  if (two_pass) {
+    if (!dq_items.empty()) {
+      BwdArgs b = a;
+      b.items = reinterpret_cast<const Item*>(ws + L.items) + n_kv_items;
+      b.n_items = static_cast<int32_t>(dq_items.size());
+      if ((e = timed_launch(K_BWD_DQ, stream, [&] {
+             return launch_bwd_dq(b, static_cast<int>(head_dim), stream);
+           })) != 0)
+        return fail(SWA_ERR_HIP, hip_error_string(e));
+    }
+    if (end_q < t_q) {  // tokens after the last sequence
+      FillArgs f{dq, static_cast<int64_t>(elem_bytes(dtype)), num_heads * head_dim, end_q, t_q,
+                 nullptr, nullptr, 0};
+      if ((e = timed_launch(K_FILL, stream, [&] { return launch_fill(f, stream); })) != 0)
+        return fail(SWA_ERR_HIP, hip_error_string(e));
+    }
+  } else {
+    FinalizeArgs fa{dq_acc, dq, static_cast<float>(scale), t_q * num_heads * head_dim};
+    if ((e = timed_launch(K_DQ_FIN, stream, [&] { return launch_dq_finalize(fa, dtype, stream); })) != 0)
+      return fail(SWA_ERR_HIP, hip_error_string(e));
+  }
   if (end_kv < t_kv) {
     FillArgs f{dk, static_cast<int64_t>(elem_bytes(dtype)), num_heads * head_dim, end_kv, t_kv,
                nullptr, nullptr, 0};
@@ -548,8 +606,9 @@ swa_status swa_debug_tile_schedule(const int64_t* cu_seqlens_q, const int64_t* c
                                    int32_t* block_item, int32_t* block_tile) {
   if (!n_rows || !block_item || !block_tile)
     return fail(SWA_ERR_NULLPTR, "n_rows / block_item / block_tile is NULL");
-  if (direction != 0 && direction != 1)
-    return fail(SWA_ERR_INVALID, "direction must be 0 (forward) or 1 (backward)");
+  if (direction < 0 || direction > 2)
+    return fail(SWA_ERR_INVALID,
+                "direction must be 0 (forward), 1 (backward dK/dV) or 2 (backward dQ)");
   Problem p = make_problem(cu_seqlens_q, cu_seqlens_kv, num_seqs, t_q, t_kv, 1, head_dim, dtype,
                            1.0, pre_tokens, next_tokens, sparse_mode);
   std::vector<Seq> seqs;
@@ -561,10 +620,14 @@ swa_status swa_debug_tile_schedule(const int64_t* cu_seqlens_q, const int64_t* c
     schedule_forward(p, seqs, items);
     *block_item = FWD_HALF;
     *block_tile = FWD_BN;
-  } else {
+  } else if (direction == 1) {
     schedule_backward(p, seqs, items);
     *block_item = BWD_BN;
     *block_tile = bwd_block_q(dtype, static_cast<int>(head_dim));
+  } else {
+    schedule_dq(p, seqs, items);
+    *block_item = DQ_BM;
+    *block_tile = FWD_BN;
   }
   order_items(items);
   int64_t n = 0;

@@ -9,12 +9,15 @@ namespace swa {
 
 // Block sizes.  Forward: a work item is one block of FWD_BM = 2 x FWD_HALF
 // query rows of one sequence (one workgroup per item and head, two wave
-// groups of FWD_HALF rows); it walks key tiles of FWD_BN.  Backward: an item
-// is one block of BWD_BN keys; it walks query tiles of bwd_block_q rows.
+// groups of FWD_HALF rows); it walks key tiles of FWD_BN.  Backward dK/dV
+// (and the fp32 one-pass backward): an item is one block of BWD_BN keys; it
+// walks query tiles of bwd_block_q rows.  Backward dQ (bf16): an item is one
+// block of DQ_BM query rows; it walks key tiles of FWD_BN.
 constexpr int FWD_HALF = 128;
 constexpr int FWD_BM = 2 * FWD_HALF;
 constexpr int FWD_BN = 64;
 constexpr int BWD_BN = 128;
+constexpr int DQ_BM = FWD_HALF;
 // query rows per backward tile: 64, or 32 for fp32 with head_dim 128 (LDS)
 constexpr int bwd_block_q(int dtype, int head_dim) { return (dtype == 0 && head_dim == 128) ? 32 : 64; }
 
@@ -22,7 +25,7 @@ constexpr int bwd_block_q(int dtype, int head_dim) { return (dtype == 0 && head_
 //   tiles[i] = lo | hi << 16 : visited tile range [lo, hi] (empty if lo > hi)
 //   full[i]  = flo | fhi << 16 : tiles in [flo, fhi] need no element mask
 // Forward items carry one range per FWD_HALF-row half (index 0, 1); backward
-// items use index 0 only.
+// items (dK/dV and dQ) use index 0 only.
 struct Item {
   int32_t q_base;   // first token of the sequence in the query tensor
   int32_t kv_base;  // first token of the sequence in the key/value tensors
@@ -74,7 +77,7 @@ struct BwdPreArgs {
   const float* ssum;
   float* drow;   // [N, t_q] rowsum(dY * out)
   float* lse2;   // [N, t_q] softmax_max*log2(e) + log2(softmax_sum), +inf if empty
-  float* dq_acc; // [t_q, N, D] zeroed here
+  float* dq_acc; // [t_q, N, D] zeroed here (null: nothing to zero)
   int64_t rows;  // t_q * N
   int32_t num_heads;
   int32_t t_q;
@@ -87,7 +90,8 @@ struct BwdArgs {
   const void* dy;
   const float* drow;  // [N, t_q]
   const float* lse2;  // [N, t_q]
-  float* dq_acc;
+  float* dq_acc;      // fp32 one-pass backward only
+  void* dq;           // bf16 dQ kernel only
   void* dk;
   void* dv;
   const Item* items;
@@ -123,7 +127,10 @@ struct FillArgs {
 // Launchers (defined in the .hip files).  They return a hipError_t as int.
 int launch_forward(const FwdArgs& a, int dtype, int head_dim, void* stream);
 int launch_bwd_pre(const BwdPreArgs& a, int dtype, int head_dim, void* stream);
+// fp32: the one-pass kernel (dK, dV and the dq accumulator); bf16: the dK/dV kernel
 int launch_backward(const BwdArgs& a, int dtype, int head_dim, void* stream);
+// bf16 only: the dQ kernel over the dQ schedule (writes dq)
+int launch_bwd_dq(const BwdArgs& a, int head_dim, void* stream);
 int launch_dq_finalize(const FinalizeArgs& a, int dtype, void* stream);
 int launch_fill(const FillArgs& a, void* stream);
 const char* hip_error_string(int err);
