@@ -404,6 +404,17 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
   constexpr int G_S1 = NS, G_V0 = 2 * NS, G_V1 = G_V0 + NV, NOPS = G_V1 + NV;
   constexpr int AHEAD = SWA_BWD_AHEAD, RING = AHEAD + 1;
   static_assert(BN == 128 && (D == 64 || D == 128), "4 waves x 32 keys, 64-row tiles");
+  // Slot of the first softmax stage of register r of block qb: the 16
+  // registers are spread evenly from the end of the block's S / dP products
+  // to two slots before the dV / dK products that use registers 8..15;
+  // registers 0..7 then finish before the products that use them.
+  constexpr auto kv_soft_slot = [](int qb, int r) {
+    const int rel = qb == 0 ? G_S1 : G_V0, last = (qb == 0 ? G_V0 : G_V1) + NV / 2 - 2;
+    return rel + (r * (last - rel)) / 15;
+  };
+  static_assert(kv_soft_slot(0, 7) + 1 < G_V0 && kv_soft_slot(1, 7) + 1 < G_V1 &&
+                kv_soft_slot(0, 15) + 1 < G_V0 + NV / 2 && kv_soft_slot(1, 15) + 1 < G_V1 + NV / 2,
+                "softmax stages finish before the products that use them");
 
   __shared__ __attribute__((aligned(1024))) char lds[2 * SLAB];
   __shared__ floatx4 lse_s[2][BM / 4];   // lse2 of the tile's rows
@@ -530,9 +541,11 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
           dk[db] = M::mma(x, sk[qb][t2], dk[db]);
       }
     };
-    // P = exp2(s c - lse2), dS = P (dP - D) of accumulator register r of block
-    // qb; each completed pair is rounded into the operands of dV / dK.
-    auto soft = [&](int qb, int r) {
+    // Softmax of accumulator register r of block qb in two stages one slot
+    // apart (so no instruction waits on the one before it):
+    //   A: P = exp2(s c - lse2), masked;   B: dS = P (dP - D), and each
+    //   completed pair of P and dS is rounded into the dV / dK operands.
+    auto soft_a = [&](int qb, int r) {
       const int g = r >> 2, e = r & 3;
       float p = __builtin_amdgcn_exp2f(fmaf(s[qb][r], c2, -lv[qb][g][e]));
       if constexpr (kMask) {
@@ -540,7 +553,9 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
         p = (rel >= rel_lo && rel <= rel_hi) ? p : 0.f;
       }
       s[qb][r] = p;
-      dp[qb][r] = p * (dp[qb][r] - dv4[qb][g][e]);
+    };
+    auto soft_b = [&](int qb, int r) {
+      dp[qb][r] = s[qb][r] * (dp[qb][r] - dv4[qb][r >> 2][r & 3]);
       if (r & 1) {
         pk[qb][r >> 3][(r & 7) - 1] = static_cast<bf16>(s[qb][r - 1]);
         pk[qb][r >> 3][r & 7] = static_cast<bf16>(s[qb][r]);
@@ -562,14 +577,13 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
           }
         }
       }
-      // softmax of block 0 over the S / dP products of block 1; of block 1:
-      // the first contraction step over the dV / dK products of block 0, the
-      // second over the first half of those of block 1
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if (m == G_S1 + (r * NS) / 16) soft(0, r);
-        if (r < 8 && m == G_V0 + (r * NV) / 8) soft(1, r);
-        if (r >= 8 && m == G_V1 + ((r - 8) * NV) / 16) soft(1, r);
+      for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          if (m == kv_soft_slot(qb, r)) soft_a(qb, r);
+          if (m == kv_soft_slot(qb, r) + 1) soft_b(qb, r);
+        }
       }
     };
 
@@ -667,6 +681,15 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_dq_kernel(BwdArgs a) {
   constexpr int G_S1 = NS, G_Q0 = 2 * NS, G_Q1 = G_Q0 + NQ, NOPS = G_Q1 + NQ;
   constexpr int AHEAD = SWA_BWD_AHEAD, RING = AHEAD + 1;
   static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+  // Slot of the first softmax stage of register r of key block jb (spread as
+  // in the dK/dV kernel, before the dQ products that use it).
+  constexpr auto dq_soft_slot = [](int jb, int r) {
+    const int rel = jb == 0 ? G_S1 : G_Q0, last = (jb == 0 ? G_Q0 : G_Q1) + NDB - 2;
+    return rel + (r * (last - rel)) / 15;
+  };
+  static_assert(dq_soft_slot(0, 7) + 1 < G_Q0 && dq_soft_slot(1, 7) + 1 < G_Q1 &&
+                dq_soft_slot(0, 15) + 1 < G_Q0 + NDB && dq_soft_slot(1, 15) + 1 < G_Q1 + NDB,
+                "softmax stages finish before the products that use them");
 
   __shared__ __attribute__((aligned(1024))) char lds[2 * SLAB];
 
@@ -769,15 +792,19 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_dq_kernel(BwdArgs a) {
         acc[db] = M::mma(x, sk[jb][t2], acc[db]);
       }
     };
-    // P = exp2(s c - lse2), dS = P (dP - D) of accumulator register r of key
-    // block jb; each completed pair is rounded into the operand of dQ^T.
-    auto soft = [&](int jb, int r) {
+    // Softmax of accumulator register r of key block jb in two stages one
+    // slot apart: A: P = exp2(s c - lse2), masked;  B: dS = P (dP - D), and
+    // each completed pair of dS is rounded into the operand of dQ^T.
+    auto soft_a = [&](int jb, int r) {
       float p = __builtin_amdgcn_exp2f(fmaf(s[jb][r], c2, -lse));
       if constexpr (kMask) {
         const int rel = 32 * jb + 8 * (r >> 2) + (r & 3);
         p = (rel >= rel_lo && rel <= rel_hi) ? p : 0.f;
       }
-      dp[jb][r] = p * (dp[jb][r] - drow);
+      s[jb][r] = p;
+    };
+    auto soft_b = [&](int jb, int r) {
+      dp[jb][r] = s[jb][r] * (dp[jb][r] - drow);
       if (r & 1) {
         sk[jb][r >> 3][(r & 7) - 1] = static_cast<bf16>(dp[jb][r - 1]);
         sk[jb][r >> 3][r & 7] = static_cast<bf16>(dp[jb][r]);
@@ -785,14 +812,13 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_dq_kernel(BwdArgs a) {
     };
     auto valu = [&](auto mc) {
       constexpr int m = decltype(mc)::value;
-      // softmax of key block 0 over the S^T / dP^T products of block 1; of
-      // block 1: the first contraction step over the dQ products of block 0,
-      // the second over the first half of those of block 1
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if (m == G_S1 + (r * NS) / 16) soft(0, r);
-        if (r < 8 && m == G_Q0 + (r * NQ) / 8) soft(1, r);
-        if (r >= 8 && m == G_Q1 + ((r - 8) * NQ) / 16) soft(1, r);
+      for (int jb = 0; jb < 2; ++jb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          if (m == dq_soft_slot(jb, r)) soft_a(jb, r);
+          if (m == dq_soft_slot(jb, r) + 1) soft_b(jb, r);
+        }
       }
     };
 

@@ -37,10 +37,23 @@
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "swa_common.hpp"
 
 namespace swa {
+
+#ifndef SWA_FWD_AHEAD
+#define SWA_FWD_AHEAD 3
+#endif
+template <typename F, int... I>
+__device__ inline void fwd_static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ inline void static_for(F&& f) {
+  fwd_static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 template <typename T, int D, bool kPos>
 __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
@@ -205,19 +218,91 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
     l_run += lsum;
   };
 
+  // bf16 matrix phase as one software pipeline over its products: first
+  // O^T += V^T P^T of the previous tile (PVN products, the head-dim blocks
+  // innermost so consecutive products use different accumulators), then
+  // S^T = K Q^T (SN products, the two key blocks alternating).  Each LDS
+  // operand is read AHEAD products before use into a small register ring;
+  // scheduling fences keep the order.
+  constexpr int PVN = NJB * PSTEPS * NDB, SN = QSTEPS * NJB;
+  constexpr int AHEAD = SWA_FWD_AHEAD, RING = AHEAD + 1;
+  int ok_[QSTEPS];   // 128-bit read of key row c, chunk 2t + h
+  int otr[NDB][2];   // transposing reads of the V tile, head-dim block db
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int t = 0; t < QSTEPS; ++t) ok_[t] = tile_off<RB>(c, (KSTEP * t + KPL * h) * 2);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int s16 = lane & 15;
+      const int col2 = 2 * (32 * db + 16 * ((lane >> 4) & 1) + 4 * (s16 & 3));
+      otr[db][0] = tile_off<RB>(4 * h + (s16 >> 2), col2);
+      otr[db][1] = tile_off<RB>(4 * h + (s16 >> 2) + 8, col2);
+    }
+  }
+  auto pipeline = [&](auto first_c, auto last_c, const char* kt, const char* vt) {
+    constexpr int FIRST = decltype(first_c)::value, LAST = decltype(last_c)::value;
+    op_t ring[RING];
+    auto read = [&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (sizeof(T) != 2) {
+        // fp32 runs the unpipelined phase
+      } else if constexpr (i < PVN) {
+        constexpr int jb = i / (PSTEPS * NDB), t2 = (i / NDB) % PSTEPS, db = i % NDB;
+        constexpr int imm = (32 * jb + KSTEP * t2) * RB;
+        typedef short shortx8 __attribute__((ext_vector_type(8)));
+        const shortx4 x = lds_read_tr16(vt + otr[db][0] + imm);
+        const shortx4 y = lds_read_tr16(vt + otr[db][1] + imm);
+        const shortx8 v = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+        ring[i % RING] = __builtin_bit_cast(op_t, v);
+      } else {
+        constexpr int j = i - PVN, t = j / NJB, jb = j % NJB;
+        ring[i % RING] = *reinterpret_cast<const op_t*>(kt + ok_[t] + 32 * jb * RB);
+      }
+    };
+    auto mfma = [&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      const op_t& x = ring[i % RING];
+      if constexpr (i < PVN) {
+        constexpr int jb = i / (PSTEPS * NDB), t2 = (i / NDB) % PSTEPS, db = i % NDB;
+        o[db] = M::mma(x, pk[jb][t2], o[db]);
+      } else {
+        constexpr int j = i - PVN, t = j / NJB, jb = j % NJB;
+        s[jb] = M::mma(x, qf[t], t == 0 ? floatx16{} : s[jb]);
+      }
+    };
+    static_for<LAST - FIRST + AHEAD>([&](auto sc) {
+      constexpr int sl = decltype(sc)::value;
+      if constexpr (sl < LAST - FIRST) read(std::integral_constant<int, FIRST + sl>{});
+      if constexpr (sl >= AHEAD) mfma(std::integral_constant<int, FIRST + sl - AHEAD>{});
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
   // matrix phase M(t): P(t-1) V(t-1) and S(t), for the tiles of this group
   auto m_phase = [&](int t, int k) {
     const bool do_pv = t - 1 >= mlo && t - 1 <= mhi;
     const bool do_s = t >= mlo && t <= mhi;
     const char* kt = kbuf0 + (k & 1) * TB;
     const char* vt = vbuf0 + ((k + 1) & 1) * TB;  // V(t-1) sits in buffer (k-1) & 1
-    if (do_pv && do_s) {
-      pv(vt);
-      scores(kt);
-    } else if (do_pv) {
-      pv(vt);
-    } else if (do_s) {
-      scores(kt);
+    if constexpr (sizeof(T) == 2) {
+      using Z = std::integral_constant<int, 0>;
+      using P = std::integral_constant<int, PVN>;
+      using E = std::integral_constant<int, PVN + SN>;
+      if (do_pv && do_s)
+        pipeline(Z{}, E{}, kt, vt);
+      else if (do_pv)
+        pipeline(Z{}, P{}, kt, vt);
+      else if (do_s)
+        pipeline(P{}, E{}, kt, vt);
+    } else {
+      if (do_pv && do_s) {
+        pv(vt);
+        scores(kt);
+      } else if (do_pv) {
+        pv(vt);
+      } else if (do_s) {
+        scores(kt);
+      }
     }
   };
   // vector phase V(t)
