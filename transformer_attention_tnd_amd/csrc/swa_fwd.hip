@@ -70,9 +70,12 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
   constexpr float kRescale = 8.f;         // exp2-domain slack before moving the reference
   static_assert(HALF == 128 && BN == 64, "two groups of 4 waves x 32 rows; 64-key tiles");
 
-  __shared__ __attribute__((aligned(1024))) char lds[4 * TB];  // K0 K1 V0 V1
+  // K and V tiles rotate through NBUF buffers each (three when they fit:
+  // the copy of a tile then lands a full step before its first use)
+  constexpr int NBUF = 6 * TB <= 160 * 1024 ? 3 : 2;
+  __shared__ __attribute__((aligned(1024))) char lds[2 * NBUF * TB];  // K[NBUF] V[NBUF]
   char* const kbuf0 = lds;
-  char* const vbuf0 = lds + 2 * TB;
+  char* const vbuf0 = lds + NBUF * TB;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, g = w >> 2, h = lane >> 5, c = lane & 31;
@@ -85,8 +88,9 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
   const T* vg = static_cast<const T*>(a.v) + (int64_t)it.kv_base * ld + head * D;
   const int qrow = it.block * 2 * HALF + HALF * g + 32 * (w & 3) + c;  // sequence-local
   // this group's tile range, and the union over both groups (the loop range)
-  const int mlo = it.tiles[g] & 0xffff, mhi = (it.tiles[g] >> 16) & 0xffff;
-  const int mflo = it.full[g] & 0xffff, mfhi = (it.full[g] >> 16) & 0xffff;
+  const int32_t mtiles = g ? it.tiles[1] : it.tiles[0], mfull = g ? it.full[1] : it.full[0];
+  const int mlo = mtiles & 0xffff, mhi = (mtiles >> 16) & 0xffff;
+  const int mflo = mfull & 0xffff, mfhi = (mfull >> 16) & 0xffff;
   int lo, hi;
   {
     const int lo0 = it.tiles[0] & 0xffff, hi0 = (it.tiles[0] >> 16) & 0xffff;
@@ -282,8 +286,8 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
   auto m_phase = [&](int t, int k) {
     const bool do_pv = t - 1 >= mlo && t - 1 <= mhi;
     const bool do_s = t >= mlo && t <= mhi;
-    const char* kt = kbuf0 + (k & 1) * TB;
-    const char* vt = vbuf0 + ((k + 1) & 1) * TB;  // V(t-1) sits in buffer (k-1) & 1
+    const char* kt = kbuf0 + (k % NBUF) * TB;                 // K(t)
+    const char* vt = vbuf0 + ((k + NBUF - 1) % NBUF) * TB;    // V(t-1)
     if constexpr (sizeof(T) == 2) {
       using Z = std::integral_constant<int, 0>;
       using P = std::integral_constant<int, PVN>;
@@ -314,16 +318,26 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
       softmax(std::false_type{}, t);
   };
 
+  // copy instructions per thread for one K or V tile
+  constexpr int NC = BN * (RB / 16) / NT;
+  static_assert(2 * NC <= 15, "copy batch fits the wait immediate");
   if (lo <= hi) {
     load_k(lo, 0);
+    if (NBUF == 3) {
+      if (lo + 1 <= hi) load_k(lo + 1, 1);
+      load_v(lo, 0);
+    }
     wait_vmem();
     __syncthreads();
     const int nk = hi - lo + 2;
     for (int k = 0; k < nk; ++k) {
       const int t = lo + k;
-      // copies for the next pair of half steps: K(t+1) and V(t)
-      if (t + 1 <= hi) load_k(t + 1, (k + 1) & 1);
-      if (t <= hi) load_v(t, k & 1);
+      // copies: three buffers: K(t+2), V(t+1) (used two steps on);
+      // two buffers: K(t+1), V(t) (used in the next step)
+      const bool ck = NBUF == 3 ? t + 2 <= hi : t + 1 <= hi;
+      const bool cv = NBUF == 3 ? t + 1 <= hi : t <= hi;
+      if (ck) load_k(NBUF == 3 ? t + 2 : t + 1, (k + (NBUF == 3 ? 2 : 1)) % NBUF);
+      if (cv) load_v(NBUF == 3 ? t + 1 : t, (k + (NBUF == 3 ? 1 : 0)) % NBUF);
       // half A
       if (g == 0)
         m_phase(t, k);
@@ -335,7 +349,14 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
         v_phase(t);
       else
         m_phase(t, k);
-      wait_vmem();
+      // the tiles of the next step have landed (with three buffers, the
+      // copies issued in this step may still be in flight)
+      if (NBUF == 2 || (!ck && !cv))
+        wait_vmem();
+      else if (ck && cv)
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * NC));
+      else
+        __builtin_amdgcn_s_waitcnt(0x0F70 | NC);
       __syncthreads();
     }
   }
