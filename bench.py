@@ -33,12 +33,16 @@ PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
 PEAK_BF16_DERIVED = 2516.6      # 256 CU x 4096 flop/clk x 2.4 GHz
 PEAK_FP32_MATRIX_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
+_CSRC = "transformer_attention_tnd_amd/csrc/"
+_HDRS = tuple(_CSRC + f for f in ("swa_common.hpp", "swa_internal.hpp"))
+# each kernel's source file and the headers it is built from (the traffic
+# record of a kernel is valid only for the exact text of these files)
 KERNEL_SOURCES = {
-    "forward": "transformer_attention_tnd_amd/csrc/swa_fwd.hip",
-    "backward": "transformer_attention_tnd_amd/csrc/swa_bwd.hip",
-    "bwd_dq": "transformer_attention_tnd_amd/csrc/swa_bwd.hip",
-    "bwd_pre": "transformer_attention_tnd_amd/csrc/swa_bwd.hip",
-    "dq_finalize": "transformer_attention_tnd_amd/csrc/swa_bwd.hip",
+    "forward": (_CSRC + "swa_fwd.hip",) + _HDRS,
+    "backward": (_CSRC + "swa_bwd.hip", _CSRC + "swa_pipe.hpp") + _HDRS,
+    "bwd_dq": (_CSRC + "swa_bwd_dq.hip", _CSRC + "swa_pipe.hpp") + _HDRS,
+    "bwd_pre": (_CSRC + "swa_bwd.hip", _CSRC + "swa_pipe.hpp") + _HDRS,
+    "dq_finalize": (_CSRC + "swa_bwd.hip", _CSRC + "swa_pipe.hpp") + _HDRS,
 }
 BWD_KERNELS = ("bwd_pre", "backward", "bwd_dq", "dq_finalize")
 
@@ -63,9 +67,12 @@ def allowed_pairs(cu_q, cu_kv, mode, pre, nxt):
     return total
 
 
-def source_hash(rel):
-    with open(os.path.join(ROOT, rel), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(files):
+    h = hashlib.sha256()
+    for rel in files:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_record(kernel, workload):

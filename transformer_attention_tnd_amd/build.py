@@ -12,7 +12,15 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libswa.so")
-SOURCES = ["swa_host.cpp", "swa_fwd.hip", "swa_bwd.hip"]
+# source -> extra compiler flags
+SOURCES = {
+    "swa_host.cpp": [],
+    "swa_fwd.hip": [],
+    "swa_bwd.hip": [],
+    # matrix-core results in ordinary vector registers: the dQ kernel's
+    # softmax then reads them without accumulator-register copies
+    "swa_bwd_dq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
 ARCH = os.environ.get("SWA_OFFLOAD_ARCH", "gfx950")
 
 
@@ -52,7 +60,7 @@ def build(verbose=True, extra=()):
     """Compile every source and link libswa.so; always rebuilds."""
     os.makedirs(BUILD, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, list(extra)), SOURCES))
+        objs = list(ex.map(lambda s: _compile(s, SOURCES[s] + list(extra)), SOURCES))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)

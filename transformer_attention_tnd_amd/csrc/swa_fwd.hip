@@ -55,6 +55,17 @@ __device__ inline void static_for(F&& f) {
   fwd_static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
+// Maximum / sum of a value over the lane pair (l, l ^ 32): one lane-half
+// swap in registers (v_permlane32_swap), no LDS round trip.
+__device__ inline float pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float pair_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <typename T, int D, bool kPos>
 __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
   using M = Mfma<T>;
@@ -191,13 +202,14 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
         }
       }
     }
-    float mx = -INFINITY;
+    // four independent partial maxima / sums keep the dependency chains short
+    float mp[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
     for (int jb = 0; jb < NJB; ++jb) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[jb][r]);
+      for (int r = 0; r < 16; ++r) mp[r & 3] = fmaxf(mp[r & 3], s[jb][r]);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mx = pair_max(fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3])));
     m_true = fmaxf(m_true, mx);
     if (__ballot((m_true - m_ref) * cs > kRescale)) {
       const float alpha = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_ref - m_true) * cs);
@@ -207,19 +219,19 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
       for (int db = 0; db < NDB; ++db) o[db] *= alpha;
     }
     const float moff = m_ref == -INFINITY ? 0.f : -m_ref * cs;
-    float lsum = 0.f;
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int jb = 0; jb < NJB; ++jb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float p = __builtin_amdgcn_exp2f(fmaf(s[jb][r], cs, moff));
         s[jb][r] = p;
-        lsum += p;
+        ls[r & 3] += p;
       }
 #pragma unroll
       for (int t2 = 0; t2 < PSTEPS; ++t2) pk[jb][t2] = M::pack(s[jb], t2);
     }
-    l_run += lsum;
+    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
   };
 
   // bf16 matrix phase as one software pipeline over its products: first
@@ -362,7 +374,7 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
   }
 
   // epilogue: normalise, store out and the statistics of this lane's row
-  const float l_ref = l_run + __shfl_xor(l_run, 32);
+  const float l_ref = pair_sum(l_run);
   if (qrow < it.sq) {
     const float inv = l_ref > 0.f ? 1.f / l_ref : 0.f;
     const int64_t tok = (int64_t)it.q_base + qrow;
