@@ -1,4 +1,4 @@
-"""fp64 CPU oracle for sliding-window FlashAttention (TND varlen, sparse_mode 0/4).
+"""fp64 CPU oracle for sliding-window FlashAttention (TND varlen, sparse_mode 0/2/3/4).
 
 TEST INFRASTRUCTURE ONLY.  Only the tests, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` may import this package.  The HIP product path
@@ -11,6 +11,7 @@ examples, brute-force mask enumeration, invariants).  See ``tests/test_oracle_*`
 """
 from .attention import (  # noqa: F401
     INT_MAX,
+    SPARSE_MODES,
     sequences,
     allowed_mask,
     forward,

@@ -21,9 +21,16 @@ What is computed, and where the pages define it:
       dP = dY V^T,  dS = P * (dP - Dv)
       dV = P^T dY,  dQ = scale dS K,  dK = scale dS^T Q
 * Masks (op-plugin sliding-window blog, section 1.3 "SparseMode说明"; API doc,
-  preTokensOptional / nextTokensOptional): sparse_mode 0 = no mask;
-  sparse_mode 4 (BAND) keeps key j for query i iff
-  -pre_tokens <= j - i <= next_tokens, with sequence-local indices.
+  preTokensOptional / nextTokensOptional; explainer 6.6), with
+  sequence-local indices i (query) and j (key) of a sequence with Sq queries
+  and Skv keys:
+      sparse_mode 0 (no mask)          every key;
+      sparse_mode 2 (LEFT_UP_CAUSAL)   j <= i        (causal, top-left corner);
+      sparse_mode 3 (RIGHT_DOWN_CAUSAL) j - i <= Skv - Sq (causal, bottom-right);
+      sparse_mode 4 (BAND)             -pre_tokens <= j - i <= next_tokens.
+  The pages name modes 2 and 3 but print no formula; the reading here takes
+  the corner in each name as the corner the diagonal starts from.  Modes 2
+  and 3 ignore pre_tokens / next_tokens.
 * Varlen TND packing (API doc, "算子功能" and inputLayout; explainer 4.2, 6.4):
   tokens of each batch are packed back to back; cumulative ends are inclusive,
   one per batch; trailing zeros mark batches that do not participate.
@@ -67,31 +74,54 @@ def sequences(cu_seqlens):
     return out
 
 
-def allowed_mask(rows, cols, sparse_mode, pre_tokens, next_tokens):
-    """Boolean [len(rows), len(cols)]: True where query i may attend key j."""
+SPARSE_MODES = (0, 2, 3, 4)
+
+
+def allowed_mask(rows, cols, sparse_mode, pre_tokens, next_tokens, sq=None, skv=None):
+    """Boolean [len(rows), len(cols)]: True where query i may attend key j.
+
+    ``sq`` / ``skv`` (the sequence's query and key lengths) are needed by
+    sparse_mode 3 only, whose diagonal ends in the bottom-right corner.
+    """
     i = torch.as_tensor(rows, dtype=torch.int64)[:, None]
     j = torch.as_tensor(cols, dtype=torch.int64)[None, :]
+    d = j - i
     if sparse_mode == 0:
         return torch.ones(i.shape[0], j.shape[1], dtype=torch.bool)
+    if sparse_mode == 2:
+        return d <= 0
+    if sparse_mode == 3:
+        if sq is None or skv is None:
+            raise ValueError("sparse_mode 3 needs the sequence lengths")
+        return d <= int(skv) - int(sq)
     if sparse_mode == 4:
-        d = j - i
         return (d >= -int(pre_tokens)) & (d <= int(next_tokens))
-    raise ValueError(f"The sparse_mode value should be 0 or 4, but got {sparse_mode}")
+    raise ValueError(f"The sparse_mode value should be 0, 2, 3 or 4, but got {sparse_mode}")
 
 
-def _col_window(r0, r1, skv, sparse_mode, pre, nxt, chunked):
-    """Columns that rows [r0, r1) can reach; all columns unless chunked."""
+def _col_window(r0, r1, sq, skv, sparse_mode, pre, nxt, chunked):
+    """Columns that rows [r0, r1) can reach; all columns unless chunked.
+
+    Only used to skip columns that are masked for every row of the block.
+    """
     if sparse_mode == 0 or not chunked:
         return 0, skv
-    lo = max(0, r0 - int(pre))
-    hi = min(skv, r1 - 1 + int(nxt) + 1)
+    if sparse_mode == 2:
+        lo, hi = 0, min(skv, r1)
+    elif sparse_mode == 3:
+        lo, hi = 0, min(skv, r1 + skv - sq)
+    else:
+        lo = max(0, r0 - int(pre))
+        hi = min(skv, r1 - 1 + int(nxt) + 1)
+    lo = min(lo, skv)
     return lo, max(lo, hi)
 
 
 def _scores(Q, K, rows, c0, c1, scale, sparse_mode, pre, nxt):
     """Scaled, masked scores for rows x columns [c0, c1) (masked = -inf)."""
     S = scale * (Q[rows] @ K[c0:c1].T)
-    M = allowed_mask(torch.as_tensor(rows), torch.arange(c0, c1), sparse_mode, pre, nxt)
+    M = allowed_mask(torch.as_tensor(rows), torch.arange(c0, c1), sparse_mode, pre, nxt,
+                     Q.shape[0], K.shape[0])
     return S.masked_fill(~M, -math.inf), M
 
 
@@ -108,7 +138,7 @@ def _softmax_stats(S):
 
 def _seq_head_forward(Q, K, V, scale, sparse_mode, pre, nxt, rows, chunked):
     r0, r1 = int(rows[0]), int(rows[-1]) + 1
-    c0, c1 = _col_window(r0, r1, K.shape[0], sparse_mode, pre, nxt, chunked)
+    c0, c1 = _col_window(r0, r1, Q.shape[0], K.shape[0], sparse_mode, pre, nxt, chunked)
     S, _ = _scores(Q, K, rows, c0, c1, scale, sparse_mode, pre, nxt)
     m, E, l = _softmax_stats(S)
     P = torch.where(l[:, None] > 0, E / torch.where(l > 0, l, 1.0)[:, None],
@@ -188,7 +218,7 @@ def backward(q, k, v, dy, out, softmax_max, softmax_sum, cu_seqlens_q, cu_seqlen
             Q, K, V = q[q0:q0 + sq, n], k[k0:k0 + skv, n], v[k0:k0 + skv, n]
             dY, O = dy[q0:q0 + sq, n], out[q0:q0 + sq, n]
             for rows in _row_chunks(sq, chunk):
-                c0, c1 = _col_window(int(rows[0]), int(rows[-1]) + 1, skv, sparse_mode,
+                c0, c1 = _col_window(int(rows[0]), int(rows[-1]) + 1, sq, skv, sparse_mode,
                                      pre_tokens, next_tokens, chunk is not None)
                 P = _recompute_p(Q, K, rows, c0, c1, scale, sparse_mode, pre_tokens,
                                  next_tokens, sm[q0 + rows, n], ss[q0 + rows, n])
@@ -239,7 +269,8 @@ def backward_rows(Q, K, V, dY, rows, scale, sparse_mode=0, pre_tokens=INT_MAX,
     O, m, l = forward_rows(Q, K, V, rows, scale, sparse_mode, pre_tokens, next_tokens)
     dq = torch.zeros(len(rows), Q.shape[1], dtype=F64)
     for idx, r in enumerate(rows.tolist()):
-        c0, c1 = _col_window(r, r + 1, K.shape[0], sparse_mode, pre_tokens, next_tokens, True)
+        c0, c1 = _col_window(r, r + 1, Q.shape[0], K.shape[0], sparse_mode, pre_tokens,
+                             next_tokens, True)
         rr = torch.tensor([r])
         P = _recompute_p(Q, K, rr, c0, c1, scale, sparse_mode, pre_tokens, next_tokens,
                          m[idx:idx + 1], l[idx:idx + 1])
@@ -257,10 +288,14 @@ def backward_keys(Q, K, V, dY, key_lo, key_hi, scale, sparse_mode=0, pre_tokens=
     (its statistics and O come from forward_rows over its whole band).
     """
     Q, K, V, dY = _as64(Q), _as64(K), _as64(V), _as64(dY)
-    sq = Q.shape[0]
+    sq, skv = Q.shape[0], K.shape[0]
     if sparse_mode == 4:
         r0 = max(0, key_lo - int(next_tokens))
         r1 = min(sq, key_hi - 1 + int(pre_tokens) + 1)
+    elif sparse_mode == 2:
+        r0, r1 = min(sq, key_lo), sq
+    elif sparse_mode == 3:
+        r0, r1 = min(sq, max(0, key_lo - (skv - sq))), sq
     else:
         r0, r1 = 0, sq
     dk = torch.zeros(key_hi - key_lo, K.shape[1], dtype=F64)

@@ -59,7 +59,7 @@ def enumerate_tiles(cu_seqlens_q, cu_seqlens_kv, sparse_mode, pre_tokens, next_t
             else:
                 rows = torch.arange(0, n_tiles * bm)
                 cols = torch.arange(it * bn, it * bn + bn)
-            m = allowed_mask(rows, cols, sparse_mode, pre_tokens, next_tokens)
+            m = allowed_mask(rows, cols, sparse_mode, pre_tokens, next_tokens, sq, skv)
             m &= (rows < sq)[:, None] & (cols < skv)[None, :]
             m = m.numpy()
             if direction == "fwd":
@@ -84,7 +84,7 @@ def count_pairs(cu_seqlens_q, cu_seqlens_kv, sparse_mode, pre_tokens, next_token
         for r0 in range(0, sq, row_chunk):
             rows = torch.arange(r0, min(sq, r0 + row_chunk))
             total += int(allowed_mask(rows, cols, sparse_mode, pre_tokens,
-                                      next_tokens).sum())
+                                      next_tokens, sq, skv).sum())
     return total
 
 
