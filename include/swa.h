@@ -12,9 +12,13 @@
  *     "反向公式" (P = exp(QK^T*scale - softmax_max) / softmax_sum);
  *   - TND packing with cumulative per-batch ends: API doc, "算子功能" and
  *     parameters actualSeqQLenOptional / actualSeqKvLenOptional;
- *   - masks: op-plugin sliding-window blog, section 1.3 "SparseMode说明":
- *     sparse_mode 0 = no mask; sparse_mode 4 (BAND) keeps key j for query i
- *     iff -pre_tokens <= j - i <= next_tokens (sequence-local indices).
+ *   - masks: op-plugin sliding-window blog, section 1.3 "SparseMode说明"
+ *     (and explainer 6.6), with sequence-local indices i (query), j (key) of
+ *     a batch with Sq queries and Skv keys:
+ *       sparse_mode 0           no mask;
+ *       sparse_mode 2 (LEFT_UP_CAUSAL)     keeps j <= i;
+ *       sparse_mode 3 (RIGHT_DOWN_CAUSAL)  keeps j - i <= Skv - Sq;
+ *       sparse_mode 4 (BAND)    keeps -pre_tokens <= j - i <= next_tokens.
  *
  * Operation (backward): aclnnFlashAttentionUnpaddingScoreGradV2 explainer,
  * sections 2.3 and 4.2, and the PyPTO-Gym article, "反向公式":
@@ -43,7 +47,10 @@
  *     softmax_sum = 0 and dq = 0; a key no query attends gets dk = dv = 0;
  *   - tokens after the last participating end get out = 0, softmax_max =
  *     -inf, softmax_sum = 0, dq = dk = dv = 0;
- *   - sparse_mode 0 ignores pre_tokens / next_tokens.
+ *   - sparse_mode 0, 2 and 3 ignore pre_tokens / next_tokens;
+ *   - the causal diagonal of modes 2 and 3 starts in the corner the name
+ *     gives (top-left: j <= i; bottom-right: j - i <= Skv - Sq), so with
+ *     Sq > Skv the first Sq - Skv rows of a mode-3 batch are empty.
  *
  * Ownership: every device buffer, the workspace included, belongs to the
  * caller; the library never allocates or frees caller memory.  Host arrays
@@ -71,7 +78,7 @@ typedef enum swa_status {
   SWA_OK = 0,
   /* a required pointer is NULL (the pages' ACLNN_ERR_PARAM_NULLPTR, 161001) */
   SWA_ERR_NULLPTR = 1,
-  /* an argument is out of range: sparse_mode not 0/4, sizes, inconsistent or
+  /* an argument is out of range: sparse_mode not 0/2/3/4, sizes, inconsistent or
    * decreasing cumulative ends, pre_tokens + next_tokens < 0, non-finite
    * scale (the pages' ACLNN_ERR_PARAM_INVALID, 161002) */
   SWA_ERR_INVALID = 2,

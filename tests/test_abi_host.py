@@ -61,8 +61,9 @@ def raw_forward(**kw):
 @pytest.mark.parametrize("kw,status,needle", [
     (dict(q=None), swa.SWA_ERR_NULLPTR, "NULL"),
     (dict(ws=None), swa.SWA_ERR_NULLPTR, "NULL"),
-    (dict(mode=2), swa.SWA_ERR_INVALID, "The sparse_mode value should be 0 or 4, but got 2"),
-    (dict(mode=1), swa.SWA_ERR_INVALID, "should be 0 or 4"),
+    (dict(mode=1), swa.SWA_ERR_INVALID, "The sparse_mode value should be 0, 2, 3 or 4, but got 1"),
+    (dict(mode=5), swa.SWA_ERR_INVALID, "should be 0, 2, 3 or 4"),
+    (dict(mode=8), swa.SWA_ERR_INVALID, "should be 0, 2, 3 or 4"),
     (dict(nseq=0), swa.SWA_ERR_INVALID, "num_seqs"),
     (dict(t_q=0), swa.SWA_ERR_INVALID, "t_q"),
     (dict(t_q=(1 << 20) + 1, cu_q=[16]), swa.SWA_ERR_INVALID, "t_q"),
@@ -91,6 +92,14 @@ def test_mode0_accepts_unequal_lengths_and_trailing_batches():
     rows, _, _ = swa.swa_debug_tile_schedule([5, 9, 0, 0], [7, 8, 0, 0], 9, 8, 64, 1,
                                              INT_MAX, INT_MAX, 0, 0)
     assert rows
+
+
+@pytest.mark.parametrize("mode", [2, 3])
+def test_causal_modes_accept_unequal_lengths_and_ignore_pre_next(mode):
+    # the causal modes take Sq != Skv per batch, and pre/next play no part
+    a = swa.swa_debug_tile_schedule([5, 900, 0], [70, 300, 0], 900, 300, 64, 1, 3, -50, mode, 0)
+    b = swa.swa_debug_tile_schedule([5, 900, 0], [70, 300, 0], 900, 300, 64, 1, 0, 0, mode, 0)
+    assert a[0] and a == b
 
 
 def test_workspace_sizes_monotone_and_backward_holds_dq_accumulator():
@@ -142,6 +151,14 @@ SCHEDULE_CASES = [
     ([1024], [1024], 4, 5, -3),
     ([640], [640], 4, -64, 64),
     ([4096], [4096], 4, 127, 1),
+    # causal modes 2 (top-left) and 3 (bottom-right), also with Sq != Skv
+    ([1000], [1000], 2, 0, 0),
+    ([1000], [1000], 3, 7, 7),
+    ([300, 345, 1045, 0], [900, 945, 1205, 0], 2, 0, 0),
+    ([300, 345, 1045, 0], [900, 945, 1205, 0], 3, 0, 0),
+    ([129, 130, 643], [1, 129, 2000], 3, 0, 0),
+    ([2000, 2064], [129, 640], 2, 0, 0),
+    ([2000, 2064], [129, 640], 3, 0, 0),
 ]
 
 

@@ -60,6 +60,20 @@ CUSTOM = {
     "bf16_band_wider_than_sequence": dict(lengths_q=[190, 66], num_heads=2, head_dim=128,
                                           sparse_mode=4, pre_tokens=65536, next_tokens=65536),
     "bf16_single_token": dict(lengths_q=[1], num_heads=4, head_dim=128),
+    # causal modes 2 (j <= i) and 3 (j - i <= Skv - Sq), with Sq != Skv per batch
+    "bf16_d128_left_up_causal": dict(lengths_q=[300, 77, 513], lengths_kv=[700, 77, 260],
+                                     num_heads=2, head_dim=128, sparse_mode=2),
+    "bf16_d128_right_down_causal": dict(lengths_q=[300, 77, 513], lengths_kv=[700, 77, 260],
+                                        num_heads=2, head_dim=128, sparse_mode=3),
+    "bf16_d64_causal_square": dict(lengths_q=[390, 129], num_heads=3, head_dim=64,
+                                   sparse_mode=2),
+    "bf16_d64_right_down_short_kv": dict(lengths_q=[400, 5], lengths_kv=[130, 70], num_heads=2,
+                                         head_dim=64, sparse_mode=3),
+    "fp32_d128_right_down_causal": dict(lengths_q=[150, 260], lengths_kv=[333, 90],
+                                        num_heads=2, head_dim=128, sparse_mode=3,
+                                        dtype=torch.float32),
+    "fp32_d64_left_up_causal": dict(lengths_q=[150, 260], lengths_kv=[333, 90], num_heads=2,
+                                    head_dim=64, sparse_mode=2, dtype=torch.float32),
 }
 
 

@@ -199,7 +199,7 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kernel(BwdArgs a) {
           const int r = 4 * g + e;
           float p = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -l4[e]));
           if constexpr (kMask)
-            p = allowed(tile * BM + rb + e, kw, it.sq, it.skv, a.mode, a.pre, a.next) ? p : 0.f;
+            p = allowed(tile * BM + rb + e, kw, it.sq, it.skv, a.mode, it.band[0], it.band[1]) ? p : 0.f;
           s[r] = p;
           dp[r] = p * (dp[r] - d4[e]);
         }
@@ -426,8 +426,8 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
   // Rows allowed for this lane's key: i in [i_min, i_max] (empty if the key
   // is past the sequence), from the band rule -pre <= kw - i <= next.
   int i_min = 0, i_max = it.sq - 1;
-  if (a.mode == 4) {  // 64-bit: pre / next may be near the int range
-    const int64_t lo64 = (int64_t)kw - a.next, hi64 = (int64_t)kw + a.pre;
+  if (a.mode != 0) {  // 64-bit: pre / next may be near the int range
+    const int64_t lo64 = (int64_t)kw - it.band[1], hi64 = (int64_t)kw + it.band[0];
     i_min = lo64 < 0 ? 0 : (lo64 > it.sq ? it.sq : (int)lo64);
     i_max = hi64 < i_max ? (hi64 < -1 ? -1 : (int)hi64) : i_max;
   }

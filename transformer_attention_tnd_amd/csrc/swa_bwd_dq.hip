@@ -85,8 +85,8 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_dq_kernel(BwdArgs a) {
   }
   // Keys allowed for this lane's row: j in [j_min, j_max] (empty past the end)
   int j_min = 0, j_max = it.skv - 1;
-  if (a.mode == 4) {  // 64-bit: pre / next may be near the int range
-    const int64_t lo64 = (int64_t)qrow - a.pre, hi64 = (int64_t)qrow + a.next;
+  if (a.mode != 0) {  // 64-bit: pre / next may be near the int range
+    const int64_t lo64 = (int64_t)qrow - it.band[0], hi64 = (int64_t)qrow + it.band[1];
     j_min = lo64 < 0 ? 0 : (lo64 > it.skv ? it.skv : (int)lo64);
     j_max = hi64 < j_max ? (hi64 < -1 ? -1 : (int)hi64) : j_max;
   }

@@ -245,6 +245,9 @@ __device__ inline int xcd_remap(int wg, int nwg) {
   return x * q + (x < r ? x : r) + idx;
 }
 
+// Element mask: inside the sequence and, unless mode is 0, inside the band
+// -pre <= j - i <= next (the item's band: sparse modes 2, 3 and 4 all reach the
+// kernels in this form).
 __device__ inline bool allowed(int i, int j, int sq, int skv, int mode, int pre, int next) {
   if (i >= sq || j >= skv) return false;
   if (mode == 0) return true;

@@ -198,7 +198,7 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int j = tile * BN + 32 * jb + c_row(r, h);
-          s[jb][r] = allowed(qrow, j, it.sq, it.skv, a.mode, a.pre, a.next) ? s[jb][r] : -INFINITY;
+          s[jb][r] = allowed(qrow, j, it.sq, it.skv, a.mode, it.band[0], it.band[1]) ? s[jb][r] : -INFINITY;
         }
       }
     }

@@ -5,7 +5,11 @@
 // values drive the tiling (aclnnFlashAttentionUnpaddingScoreGradV2 explainer,
 // section 8.1, where the actual_seq inputs are value-dependent), and with
 // sparse_mode 4 every tile outside the band -pre_tokens <= j - i <= next_tokens
-// is never visited (op-plugin sliding-window blog, section 1.3).
+// is never visited (op-plugin sliding-window blog, section 1.3).  The causal
+// modes 2 (LEFT_UP_CAUSAL) and 3 (RIGHT_DOWN_CAUSAL) of the same section are
+// bands too: j <= i, and j - i <= Skv - Sq (the diagonal from the top-left or
+// the bottom-right corner), so every mode reaches the kernels as a band per
+// sequence.
 
 #include <algorithm>
 #include <cmath>
@@ -38,6 +42,14 @@ int64_t floor_div(int64_t a, int64_t b) {
   return q;
 }
 int64_t ceil_div(int64_t a, int64_t b) { return -floor_div(-a, b); }
+
+// The mask of one sequence as a band: key j is allowed for query i iff
+// -pre <= j - i <= next (sequence-local indices); on == false: no mask.
+struct Band {
+  bool on;
+  int64_t pre, next;
+};
+constexpr int64_t kWide = int64_t(1) << 40;  // wider than any sequence
 
 constexpr int64_t kMaxT = int64_t(1) << 20;  // explainer 6.3: T in 1..1M
 
@@ -116,8 +128,8 @@ swa_status validate(const Problem& p, std::vector<Seq>& seqs, int64_t* end_q, in
   if (!p.cu_q || !p.cu_kv) return fail(SWA_ERR_NULLPTR, "cu_seqlens_q / cu_seqlens_kv is NULL");
   swa_status s = check_sizes(p.num_seqs, p.t_q, p.t_kv, p.num_heads, p.head_dim, p.dtype);
   if (s != SWA_OK) return s;
-  if (p.sparse_mode != 0 && p.sparse_mode != 4)
-    return fail(SWA_ERR_INVALID, "The sparse_mode value should be 0 or 4, but got " +
+  if (p.sparse_mode != 0 && p.sparse_mode != 2 && p.sparse_mode != 3 && p.sparse_mode != 4)
+    return fail(SWA_ERR_INVALID, "The sparse_mode value should be 0, 2, 3 or 4, but got " +
                                      std::to_string(p.sparse_mode));
   if (!std::isfinite(p.scale)) return fail(SWA_ERR_INVALID, "scale must be finite");
   if (p.sparse_mode == 4 && p.pre_tokens + p.next_tokens < 0)
@@ -153,6 +165,37 @@ BwdLayout bwd_layout(int64_t num_seqs, int64_t t_q, int64_t t_kv, int64_t n, int
   return l;
 }
 
+Band seq_band(const Problem& p, const Seq& s) {
+  switch (p.sparse_mode) {
+    case 2: return Band{true, kWide, 0};                 // j <= i
+    case 3: return Band{true, kWide, s.skv - s.sq};      // j - i <= Skv - Sq
+    case 4: return Band{true, p.pre_tokens, p.next_tokens};
+    default: return Band{false, kWide, kWide};
+  }
+}
+
+int32_t clamp_window(int64_t x) {
+  const int64_t lim = int64_t(1) << 30;
+  return static_cast<int32_t>(std::max(-lim, std::min(lim, x)));
+}
+
+// Item fields shared by every schedule
+Item make_item(const Problem& p, const Seq& s, int64_t block) {
+  const Band bd = seq_band(p, s);
+  Item it{};
+  it.q_base = static_cast<int32_t>(s.q0);
+  it.kv_base = static_cast<int32_t>(s.k0);
+  it.sq = static_cast<int32_t>(s.sq);
+  it.skv = static_cast<int32_t>(s.skv);
+  it.block = static_cast<int32_t>(block);
+  it.seq = s.b;
+  it.band[0] = clamp_window(bd.pre);
+  it.band[1] = clamp_window(bd.next);
+  it.tiles[1] = pack_range(1, 0);
+  it.full[1] = pack_range(1, 0);
+  return it;
+}
+
 // Forward schedule: one item per block of FWD_BM query rows, made of two
 // halves of FWD_HALF rows with their own key-tile ranges (tiles of FWD_BN).
 // For a block of rows, a tile is visited iff some (i < Sq, j < Skv) in it is
@@ -164,10 +207,11 @@ void forward_range(const Problem& p, const Seq& s, int64_t r0, int64_t* lo, int6
   *lo = 1, *hi = 0, *flo = 1, *fhi = 0;
   if (r0 >= s.sq || s.skv == 0) return;
   const int64_t r1 = std::min(r0 + BM, s.sq) - 1;
+  const Band bd = seq_band(p, s);
   int64_t jlo = 0, jhi = s.skv - 1;
-  if (p.sparse_mode == 4) {
-    jlo = std::max<int64_t>(0, r0 - p.pre_tokens);
-    jhi = std::min<int64_t>(s.skv - 1, r1 + p.next_tokens);
+  if (bd.on) {
+    jlo = std::max<int64_t>(0, r0 - bd.pre);
+    jhi = std::min<int64_t>(s.skv - 1, r1 + bd.next);
   }
   if (jlo > jhi) return;
   *lo = jlo / BN;
@@ -175,9 +219,9 @@ void forward_range(const Problem& p, const Seq& s, int64_t r0, int64_t* lo, int6
   if (r0 + BM <= s.sq) {
     *flo = *lo;
     *fhi = std::min(*hi, s.skv / BN - 1);
-    if (p.sparse_mode == 4) {
-      *flo = std::max(*flo, ceil_div(r0 + BM - 1 - p.pre_tokens, BN));
-      *fhi = std::min(*fhi, floor_div(r0 + p.next_tokens - BN + 1, BN));
+    if (bd.on) {
+      *flo = std::max(*flo, ceil_div(r0 + BM - 1 - bd.pre, BN));
+      *fhi = std::min(*fhi, floor_div(r0 + bd.next - BN + 1, BN));
     }
   }
 }
@@ -188,13 +232,7 @@ void schedule_forward(const Problem& p, const std::vector<Seq>& seqs, std::vecto
     if (s.sq == 0) continue;
     const int64_t nqb = ceil_div(s.sq, FWD_BM);
     for (int64_t qb = 0; qb < nqb; ++qb) {
-      Item it{};
-      it.q_base = static_cast<int32_t>(s.q0);
-      it.kv_base = static_cast<int32_t>(s.k0);
-      it.sq = static_cast<int32_t>(s.sq);
-      it.skv = static_cast<int32_t>(s.skv);
-      it.block = static_cast<int32_t>(qb);
-      it.seq = s.b;
+      Item it = make_item(p, s, qb);
       for (int half = 0; half < 2; ++half) {
         int64_t lo, hi, flo, fhi;
         forward_range(p, s, qb * FWD_BM + half * FWD_HALF, &lo, &hi, &flo, &fhi);
@@ -214,15 +252,16 @@ void schedule_backward(const Problem& p, const std::vector<Seq>& seqs,
   const int64_t BN = BWD_BN, BM = bwd_block_q(p.dtype, static_cast<int>(p.head_dim));
   for (const Seq& s : seqs) {
     if (s.skv == 0) continue;
+    const Band bd = seq_band(p, s);
     const int64_t nkb = ceil_div(s.skv, BN);
     for (int64_t kb = 0; kb < nkb; ++kb) {
       const int64_t k0 = kb * BN, k1 = std::min(k0 + BN, s.skv) - 1;
       int64_t lo = 1, hi = 0, flo = 1, fhi = 0;
       if (s.sq > 0) {
         int64_t ilo = 0, ihi = s.sq - 1;
-        if (p.sparse_mode == 4) {
-          ilo = std::max<int64_t>(0, k0 - p.next_tokens);
-          ihi = std::min<int64_t>(s.sq - 1, k1 + p.pre_tokens);
+        if (bd.on) {
+          ilo = std::max<int64_t>(0, k0 - bd.next);
+          ihi = std::min<int64_t>(s.sq - 1, k1 + bd.pre);
         }
         if (ilo <= ihi) {
           lo = ilo / BM;
@@ -230,24 +269,16 @@ void schedule_backward(const Problem& p, const std::vector<Seq>& seqs,
           if (k0 + BN <= s.skv) {
             flo = lo;
             fhi = std::min(hi, s.sq / BM - 1);
-            if (p.sparse_mode == 4) {
-              flo = std::max(flo, ceil_div(k0 + BN - 1 - p.next_tokens, BM));
-              fhi = std::min(fhi, floor_div(k0 + p.pre_tokens - BM + 1, BM));
+            if (bd.on) {
+              flo = std::max(flo, ceil_div(k0 + BN - 1 - bd.next, BM));
+              fhi = std::min(fhi, floor_div(k0 + bd.pre - BM + 1, BM));
             }
           }
         }
       }
-      Item it{};
-      it.q_base = static_cast<int32_t>(s.q0);
-      it.kv_base = static_cast<int32_t>(s.k0);
-      it.sq = static_cast<int32_t>(s.sq);
-      it.skv = static_cast<int32_t>(s.skv);
-      it.block = static_cast<int32_t>(kb);
+      Item it = make_item(p, s, kb);
       it.tiles[0] = pack_range(lo, hi);
       it.full[0] = pack_range(flo, fhi);
-      it.tiles[1] = pack_range(1, 0);
-      it.full[1] = pack_range(1, 0);
-      it.seq = s.b;
       items.push_back(it);
     }
   }
@@ -263,17 +294,9 @@ void schedule_dq(const Problem& p, const std::vector<Seq>& seqs, std::vector<Ite
     for (int64_t qb = 0; qb < nqb; ++qb) {
       int64_t lo, hi, flo, fhi;
       forward_range(p, s, qb * DQ_BM, &lo, &hi, &flo, &fhi);
-      Item it{};
-      it.q_base = static_cast<int32_t>(s.q0);
-      it.kv_base = static_cast<int32_t>(s.k0);
-      it.sq = static_cast<int32_t>(s.sq);
-      it.skv = static_cast<int32_t>(s.skv);
-      it.block = static_cast<int32_t>(qb);
+      Item it = make_item(p, s, qb);
       it.tiles[0] = pack_range(lo, hi);
       it.full[0] = pack_range(flo, fhi);
-      it.tiles[1] = pack_range(1, 0);
-      it.full[1] = pack_range(1, 0);
-      it.seq = s.b;
       items.push_back(it);
     }
   }
@@ -339,10 +362,6 @@ swa_status upload(const std::vector<Item>& items, void* dst, void* stream) {
   return SWA_OK;
 }
 
-int32_t clamp_window(int64_t x) {
-  const int64_t lim = int64_t(1) << 30;
-  return static_cast<int32_t>(std::max(-lim, std::min(lim, x)));
-}
 
 Problem make_problem(const int64_t* cu_q, const int64_t* cu_kv, int64_t num_seqs, int64_t t_q,
                      int64_t t_kv, int64_t n, int64_t d, int32_t dtype, double scale,
@@ -486,8 +505,6 @@ swa_status swa_forward(const void* q, const void* k, const void* v, const int64_
     a.num_heads = static_cast<int32_t>(num_heads);
     a.scale_log2 = static_cast<float>(scale * 1.4426950408889634);
     a.mode = static_cast<int32_t>(sparse_mode);
-    a.pre = clamp_window(pre_tokens);
-    a.next = clamp_window(next_tokens);
     if ((e = timed_launch(K_FWD, stream, [&] {
            return launch_forward(a, dtype, static_cast<int>(head_dim), stream);
          })) != 0)
@@ -557,8 +574,6 @@ swa_status swa_backward(const void* q, const void* k, const void* v, const void*
   a.scale = static_cast<float>(scale);
   a.scale_log2 = static_cast<float>(scale * 1.4426950408889634);
   a.mode = static_cast<int32_t>(sparse_mode);
-  a.pre = clamp_window(pre_tokens);
-  a.next = clamp_window(next_tokens);
   if (n_kv_items > 0) {
     if ((e = timed_launch(K_BWD, stream, [&] {
            return launch_backward(a, dtype, static_cast<int>(head_dim), stream);

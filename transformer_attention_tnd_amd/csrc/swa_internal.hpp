@@ -24,6 +24,9 @@ constexpr int bwd_block_q(int dtype, int head_dim) { return (dtype == 0 && head_
 // One schedule entry (48 bytes, uploaded to the workspace).
 //   tiles[i] = lo | hi << 16 : visited tile range [lo, hi] (empty if lo > hi)
 //   full[i]  = flo | fhi << 16 : tiles in [flo, fhi] need no element mask
+//   band     = {pre, next} of the sequence's mask (key j allowed for query i
+//              iff -pre <= j - i <= next), clamped to +-2^30; unused when the
+//              kernel's mode is 0 (no mask)
 // Forward items carry one range per FWD_HALF-row half (index 0, 1); backward
 // items (dK/dV and dQ) use index 0 only.
 struct Item {
@@ -35,7 +38,7 @@ struct Item {
   int32_t seq;      // batch index (diagnostics only)
   int32_t tiles[2];
   int32_t full[2];
-  int32_t pad[2];
+  int32_t band[2];
 };
 static_assert(sizeof(Item) == 48, "Item layout");
 
@@ -65,9 +68,7 @@ struct FwdArgs {
   int32_t n_items;
   int32_t num_heads;
   float scale_log2;  // scale * log2(e)
-  int32_t mode;
-  int32_t pre;       // clamped to +-2^30
-  int32_t next;
+  int32_t mode;      // 0: no mask; otherwise each item's band applies
 };
 
 struct BwdPreArgs {
@@ -100,9 +101,7 @@ struct BwdArgs {
   int32_t t_q;
   float scale;
   float scale_log2;
-  int32_t mode;
-  int32_t pre;
-  int32_t next;
+  int32_t mode;  // 0: no mask; otherwise each item's band applies
 };
 
 struct FinalizeArgs {
