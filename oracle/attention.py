@@ -31,6 +31,10 @@ What is computed, and where the pages define it:
   The pages name modes 2 and 3 but print no formula; the reading here takes
   the corner in each name as the corner the diagonal starts from.  Modes 2
   and 3 ignore pre_tokens / next_tokens.
+* Grouped heads (explainer 6.2): q has Nq heads and k / v have Nkv heads with
+  Nq / Nkv = G a whole number; query head n reads key/value head n // G
+  (floor division), and the gradients of a key/value head sum over the G
+  query heads that read it.  G = 1 is the ordinary multi-head case.
 * Varlen TND packing (API doc, "算子功能" and inputLayout; explainer 4.2, 6.4):
   tokens of each batch are packed back to back; cumulative ends are inclusive,
   one per batch; trailing zeros mark batches that do not participate.
@@ -159,6 +163,14 @@ def _as64(x):
     return x.detach().to("cpu").to(F64)
 
 
+def group_size(q, k):
+    """Query heads per key/value head (explainer 6.2: Nq / Nkv a whole number)."""
+    nq, nkv = q.shape[1], k.shape[1]
+    if nkv < 1 or nq % nkv:
+        raise ValueError(f"query heads ({nq}) must be a multiple of key/value heads ({nkv})")
+    return nq // nkv
+
+
 def forward(q, k, v, cu_seqlens_q, cu_seqlens_kv, scale, pre_tokens=INT_MAX,
             next_tokens=INT_MAX, sparse_mode=0, chunk=None, heads=None):
     """Attention forward over a TND batch.
@@ -168,6 +180,7 @@ def forward(q, k, v, cu_seqlens_q, cu_seqlens_kv, scale, pre_tokens=INT_MAX,
     """
     q, k, v = _as64(q), _as64(k), _as64(v)
     Tq, N, D = q.shape
+    G = group_size(q, k)
     out = torch.zeros(Tq, N, v.shape[2], dtype=F64)
     smax = torch.full((Tq, N), -math.inf, dtype=F64)
     ssum = torch.zeros((Tq, N), dtype=F64)
@@ -176,7 +189,7 @@ def forward(q, k, v, cu_seqlens_q, cu_seqlens_kv, scale, pre_tokens=INT_MAX,
         raise ValueError("query and key/value batches disagree")
     for (q0, sq), (k0, skv) in zip(sq_list, skv_list):
         for n in (range(N) if heads is None else heads):
-            Q, K, V = q[q0:q0 + sq, n], k[k0:k0 + skv, n], v[k0:k0 + skv, n]
+            Q, K, V = q[q0:q0 + sq, n], k[k0:k0 + skv, n // G], v[k0:k0 + skv, n // G]
             for rows in _row_chunks(sq, chunk):
                 O, m, l = _seq_head_forward(Q, K, V, scale, sparse_mode, pre_tokens,
                                             next_tokens, rows, chunk is not None)
@@ -210,12 +223,13 @@ def backward(q, k, v, dy, out, softmax_max, softmax_sum, cu_seqlens_q, cu_seqlen
     if sm.dim() == 3:
         sm, ss = sm[..., 0], ss[..., 0]
     Tq, N, D = q.shape
+    G = group_size(q, k)
     dq = torch.zeros_like(q)
     dk = torch.zeros_like(k)
     dv = torch.zeros(v.shape, dtype=F64)
     for (q0, sq), (k0, skv) in zip(sequences(cu_seqlens_q), sequences(cu_seqlens_kv)):
         for n in (range(N) if heads is None else heads):
-            Q, K, V = q[q0:q0 + sq, n], k[k0:k0 + skv, n], v[k0:k0 + skv, n]
+            Q, K, V = q[q0:q0 + sq, n], k[k0:k0 + skv, n // G], v[k0:k0 + skv, n // G]
             dY, O = dy[q0:q0 + sq, n], out[q0:q0 + sq, n]
             for rows in _row_chunks(sq, chunk):
                 c0, c1 = _col_window(int(rows[0]), int(rows[-1]) + 1, sq, skv, sparse_mode,
@@ -225,9 +239,9 @@ def backward(q, k, v, dy, out, softmax_max, softmax_sum, cu_seqlens_q, cu_seqlen
                 Dv = (dY[rows] * O[rows]).sum(dim=1)
                 dP = dY[rows] @ V[c0:c1].T
                 dS = P * (dP - Dv[:, None])
-                dv[k0 + c0:k0 + c1, n] += P.T @ dY[rows]
+                dv[k0 + c0:k0 + c1, n // G] += P.T @ dY[rows]
                 dq[q0 + rows, n] = scale * (dS @ K[c0:c1])
-                dk[k0 + c0:k0 + c1, n] += scale * (dS.T @ Q[rows])
+                dk[k0 + c0:k0 + c1, n // G] += scale * (dS.T @ Q[rows])
     return dq, dk, dv
 
 
