@@ -74,6 +74,22 @@ CUSTOM = {
                                         dtype=torch.float32),
     "fp32_d64_left_up_causal": dict(lengths_q=[150, 260], lengths_kv=[333, 90], num_heads=2,
                                     head_dim=64, sparse_mode=2, dtype=torch.float32),
+    # grouped key/value heads (query head n reads key/value head n // G); dk / dv
+    # sum G heads, so the bf16 cases draw std 0.5 (as the 32-head varlen
+    # workload does) to keep them near unit scale, where the absolute bf16
+    # tolerance is above the output's own rounding
+    "bf16_d128_gqa4_band": dict(lengths_q=[300, 77, 513], num_heads=8, num_kv_heads=2,
+                                head_dim=128, sparse_mode=4, pre_tokens=100, next_tokens=0,
+                                std=0.5),
+    "bf16_d64_gqa3_dense_unequal_kv": dict(lengths_q=[77, 190], lengths_kv=[50, 260],
+                                           num_heads=6, num_kv_heads=2, head_dim=64),
+    "bf16_d128_mqa_causal": dict(lengths_q=[257, 130], lengths_kv=[400, 100], num_heads=4,
+                                 num_kv_heads=1, head_dim=128, sparse_mode=3, std=0.5),
+    "fp32_d128_gqa2_band": dict(lengths_q=[300, 45], num_heads=4, num_kv_heads=2,
+                                head_dim=128, sparse_mode=4, pre_tokens=90, next_tokens=20,
+                                dtype=torch.float32),
+    "fp32_d64_gqa4_dense": dict(lengths_q=[150, 66], num_heads=4, num_kv_heads=1,
+                                head_dim=64, dtype=torch.float32),
 }
 
 
@@ -148,6 +164,37 @@ def test_backward_example_uses_given_statistics(dev):
     assert dq.abs().max().item() == 0 and dk.abs().max().item() == 0
     expect = 256 * math.exp(128 * 0.088388 - 3) / 3
     assert ((dv - expect).abs() / expect).max().item() <= 1e-5
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_gqa_equals_replicated_heads(dev, dtype):
+    """Grouped heads give the same out / dq as the ordinary multi-head call
+    on K / V repeated per query head, and dk / dv equal to the group sums of
+    that call's dk / dv (bf16: exact for out and dq, whose kernels read the
+    same values; dk / dv differ only in summation order)."""
+    G = 4
+    p = workloads.make_custom([300, 77, 513], num_heads=8, num_kv_heads=2, head_dim=128,
+                              dtype=dtype, sparse_mode=4, pre_tokens=100, next_tokens=3)
+    g = run_hip(p, dev)
+    rep = workloads.Problem(p.q, p.k.repeat_interleave(G, 1).contiguous(),
+                            p.v.repeat_interleave(G, 1).contiguous(), p.dy, p.cu_seqlens_q,
+                            p.cu_seqlens_kv, p.scale, p.pre_tokens, p.next_tokens,
+                            p.sparse_mode)
+    r = run_hip(rep, dev)
+    assert torch.equal(g["out"], r["out"]) and torch.equal(g["smax"], r["smax"])
+    if dtype == torch.bfloat16:
+        assert torch.equal(g["dq"], r["dq"])
+    for n in ("dk", "dv"):
+        per_head = r[n].double().view(r[n].shape[0], 2, G, -1)
+        summed = per_head.sum(2)
+        err = (g[n].double() - summed).abs()
+        if dtype == torch.bfloat16:
+            # each side rounds to bf16 (unit roundoff 2^-8): G roundings of the
+            # per-head values against one of the group sum, plus fp32 order
+            bound = 2.0 ** -8 * (per_head.abs().sum(2) + summed.abs()) + 1e-5
+            assert (err <= bound).all(), f"{n}: {float((err - bound).max()):.3e} over the bound"
+        else:
+            assert float(err.max()) <= 1e-4 * float(summed.abs().max())
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])

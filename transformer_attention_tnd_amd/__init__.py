@@ -7,7 +7,8 @@ Every step of the computation runs in the HIP kernels of ``libswa.so``;
 there is no fallback: if the library is missing the calls raise.
 
 ``forward`` and ``backward`` are conveniences that allocate the outputs and
-the workspace with torch and call ``swa_forward`` / ``swa_backward``.
+the workspace with torch and call ``swa_forward_gqa`` / ``swa_backward_gqa``
+(grouped key/value heads when k has fewer heads than q).
 """
 from __future__ import annotations
 
@@ -17,7 +18,8 @@ import os
 __all__ = [
     "INT_MAX", "SwaError", "load_library", "library_path",
     "swa_forward_workspace_size", "swa_backward_workspace_size",
-    "swa_forward", "swa_backward", "swa_last_error", "swa_debug_tile_schedule",
+    "swa_forward", "swa_backward", "swa_forward_gqa", "swa_backward_gqa",
+    "swa_last_error", "swa_debug_tile_schedule",
     "swa_profile_enable", "swa_profile_read",
     "forward", "backward", "DTYPE_FP32", "DTYPE_BF16", "DTYPE_FP16",
 ]
@@ -46,6 +48,12 @@ _SIGNATURES = {
     "swa_backward": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64p, _i64p, _i64, _i64, _i64, _i64,
                      _i64, _i32, ctypes.c_double, _i64, _i64, _i64, _vp, _vp, _vp, _vp,
                      ctypes.c_size_t, _vp],
+    "swa_forward_gqa": [_vp, _vp, _vp, _i64p, _i64p, _i64, _i64, _i64, _i64, _i64, _i64, _i32,
+                        ctypes.c_double, _i64, _i64, _i64, _vp, _vp, _vp, _vp, ctypes.c_size_t,
+                        _vp],
+    "swa_backward_gqa": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64p, _i64p, _i64, _i64, _i64,
+                         _i64, _i64, _i64, _i32, ctypes.c_double, _i64, _i64, _i64, _vp, _vp,
+                         _vp, _vp, ctypes.c_size_t, _vp],
     "swa_last_error": [],
     "swa_debug_tile_schedule": [_i64p, _i64p, _i64, _i64, _i64, _i64, _i32, _i64, _i64, _i64,
                                 _i32, _i32p, _i64, _i64p, _i32p, _i32p],
@@ -140,10 +148,11 @@ def swa_backward_workspace_size(num_seqs, t_q, t_kv, num_heads, head_dim, dtype)
     return out.value
 
 
-def _shape_checks(q, k, v, extra_q=(), extra_kv=()):
+def _shape_checks(q, k, v, extra_q=(), extra_kv=(), grouped=False):
     if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
         raise ValueError("q, k, v must be TND tensors [T, N, D]")
-    if k.shape != v.shape or q.shape[1:] != k.shape[1:]:
+    heads_ok = (q.shape[1] % k.shape[1] == 0) if grouped else q.shape[1] == k.shape[1]
+    if k.shape != v.shape or q.shape[2] != k.shape[2] or not heads_ok:
         raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
     for t in (q, k, v, *extra_q, *extra_kv):
         if not t.is_contiguous():
@@ -202,6 +211,40 @@ def swa_backward(q, k, v, dy, out, softmax_max, softmax_sum, cu_seqlens_q, cu_se
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q, stream)))
 
 
+def swa_forward_gqa(q, k, v, cu_seqlens_q, cu_seqlens_kv, scale, pre_tokens, next_tokens,
+                    sparse_mode, out, softmax_max, softmax_sum, workspace, stream=None):
+    """Marshal to swa_forward_gqa: k and v may have fewer heads than q (a divisor)."""
+    _shape_checks(q, k, v, extra_q=(out,), grouped=True)
+    _stats_check(q, softmax_max, softmax_sum)
+    cq, nq = _cu_array(cu_seqlens_q)
+    ck, nk = _cu_array(cu_seqlens_kv)
+    if nq != nk:
+        raise ValueError("cu_seqlens_q and cu_seqlens_kv must have the same length")
+    _check(load_library().swa_forward_gqa(
+        _ptr(q), _ptr(k), _ptr(v), cq, ck, nq, q.shape[0], k.shape[0], q.shape[1], k.shape[1],
+        q.shape[2], _dtype_code(q), float(scale), int(pre_tokens), int(next_tokens),
+        int(sparse_mode), _ptr(out), _ptr(softmax_max), _ptr(softmax_sum), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(q, stream)))
+
+
+def swa_backward_gqa(q, k, v, dy, out, softmax_max, softmax_sum, cu_seqlens_q, cu_seqlens_kv,
+                     scale, pre_tokens, next_tokens, sparse_mode, dq, dk, dv, workspace,
+                     stream=None):
+    """Marshal to swa_backward_gqa: k, v, dk, dv may have fewer heads than q."""
+    _shape_checks(q, k, v, extra_q=(dy, out, dq), extra_kv=(dk, dv), grouped=True)
+    _stats_check(q, softmax_max, softmax_sum)
+    cq, nq = _cu_array(cu_seqlens_q)
+    ck, nk = _cu_array(cu_seqlens_kv)
+    if nq != nk:
+        raise ValueError("cu_seqlens_q and cu_seqlens_kv must have the same length")
+    _check(load_library().swa_backward_gqa(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(dy), _ptr(out), _ptr(softmax_max), _ptr(softmax_sum),
+        cq, ck, nq, q.shape[0], k.shape[0], q.shape[1], k.shape[1], q.shape[2], _dtype_code(q),
+        float(scale), int(pre_tokens), int(next_tokens), int(sparse_mode), _ptr(dq), _ptr(dk),
+        _ptr(dv), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(q, stream)))
+
+
 def swa_debug_tile_schedule(cu_seqlens_q, cu_seqlens_kv, t_q, t_kv, head_dim, dtype,
                             pre_tokens, next_tokens, sparse_mode, direction):
     """Host-only schedule dump: (rows [n, 4] as a list of tuples, block_item, block_tile)."""
@@ -241,7 +284,8 @@ def _workspace(nbytes, device):
 
 def forward(q, k, v, cu_seqlens_q, cu_seqlens_kv, scale, pre_tokens=INT_MAX,
             next_tokens=INT_MAX, sparse_mode=0, workspace=None):
-    """Allocate (out, softmax_max, softmax_sum) and run swa_forward."""
+    """Allocate (out, softmax_max, softmax_sum) and run swa_forward_gqa (k / v may
+    have fewer heads than q)."""
     import torch
     out = torch.empty_like(q)
     smax = torch.empty(q.shape[0], q.shape[1], 8, dtype=torch.float32, device=q.device)
@@ -250,20 +294,21 @@ def forward(q, k, v, cu_seqlens_q, cu_seqlens_kv, scale, pre_tokens=INT_MAX,
         nbytes = swa_forward_workspace_size(len(cu_seqlens_q), q.shape[0], k.shape[0],
                                             q.shape[1], q.shape[2], _dtype_code(q))
         workspace = _workspace(nbytes, q.device)
-    swa_forward(q, k, v, cu_seqlens_q, cu_seqlens_kv, scale, pre_tokens, next_tokens,
-                sparse_mode, out, smax, ssum, workspace)
+    swa_forward_gqa(q, k, v, cu_seqlens_q, cu_seqlens_kv, scale, pre_tokens, next_tokens,
+                    sparse_mode, out, smax, ssum, workspace)
     return out, smax, ssum
 
 
 def backward(q, k, v, dy, out, softmax_max, softmax_sum, cu_seqlens_q, cu_seqlens_kv, scale,
              pre_tokens=INT_MAX, next_tokens=INT_MAX, sparse_mode=0, workspace=None):
-    """Allocate (dq, dk, dv) and run swa_backward."""
+    """Allocate (dq, dk, dv) and run swa_backward_gqa (k / v may have fewer heads
+    than q)."""
     import torch
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     if workspace is None:
         nbytes = swa_backward_workspace_size(len(cu_seqlens_q), q.shape[0], k.shape[0],
                                              q.shape[1], q.shape[2], _dtype_code(q))
         workspace = _workspace(nbytes, q.device)
-    swa_backward(q, k, v, dy, out, softmax_max, softmax_sum, cu_seqlens_q, cu_seqlens_kv, scale,
-                 pre_tokens, next_tokens, sparse_mode, dq, dk, dv, workspace)
+    swa_backward_gqa(q, k, v, dy, out, softmax_max, softmax_sum, cu_seqlens_q, cu_seqlens_kv,
+                     scale, pre_tokens, next_tokens, sparse_mode, dq, dk, dv, workspace)
     return dq, dk, dv

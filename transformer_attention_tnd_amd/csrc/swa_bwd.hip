@@ -104,16 +104,28 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kernel(BwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, h = lane >> 5, c = lane & 31;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int head = L / a.n_items;
-  const Item it = a.items[L - head * a.n_items];
+  const int kvh = L / a.n_items;  // the grid runs over key/value heads
+  const Item it = a.items[L - kvh * a.n_items];
   const int N = a.num_heads;
-  const int64_t ld = (int64_t)N * D;
-  const T* qg = static_cast<const T*>(a.q) + (int64_t)it.q_base * ld + head * D;
-  const T* dyg = static_cast<const T*>(a.dy) + (int64_t)it.q_base * ld + head * D;
-  const T* kg = static_cast<const T*>(a.k) + (int64_t)it.kv_base * ld + head * D;
-  const T* vg = static_cast<const T*>(a.v) + (int64_t)it.kv_base * ld + head * D;
-  const float* lse_g = a.lse2 + (int64_t)head * a.t_q + it.q_base;
-  const float* drow_g = a.drow + (int64_t)head * a.t_q + it.q_base;
+  const int G = N / a.num_kv_heads;                  // query heads sharing this K / V
+  const int64_t ld = (int64_t)N * D;                 // q / dy / dq row stride
+  const int64_t ldkv = (int64_t)a.num_kv_heads * D;  // k / v / dk / dv row stride
+  const T* kg = static_cast<const T*>(a.k) + (int64_t)it.kv_base * ldkv + kvh * D;
+  const T* vg = static_cast<const T*>(a.v) + (int64_t)it.kv_base * ldkv + kvh * D;
+  // the query head being processed (the group's heads run one after another,
+  // accumulating into the same dK / dV) and its tensors
+  int head = kvh * G;
+  const T* qg = nullptr;
+  const T* dyg = nullptr;
+  const float* lse_g = nullptr;
+  const float* drow_g = nullptr;
+  auto set_head = [&](int hq) {
+    head = hq;
+    qg = static_cast<const T*>(a.q) + (int64_t)it.q_base * ld + hq * D;
+    dyg = static_cast<const T*>(a.dy) + (int64_t)it.q_base * ld + hq * D;
+    lse_g = a.lse2 + (int64_t)hq * a.t_q + it.q_base;
+    drow_g = a.drow + (int64_t)hq * a.t_q + it.q_base;
+  };
   const int kb0 = it.block * BN;          // first key of the block (sequence-local)
   const int kw = kb0 + 32 * w + c;        // this lane's key
   const int lo = it.tiles[0] & 0xffff, hi = (it.tiles[0] >> 16) & 0xffff;
@@ -127,7 +139,7 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kernel(BwdArgs a) {
   op_t kf[kKVlds ? 1 : DSTEPS], vf[kKVlds ? 1 : DSTEPS];
   if constexpr (!kKVlds) {
     const bool ok = kw < it.skv;
-    const int64_t off = (int64_t)(ok ? kw : 0) * ld;
+    const int64_t off = (int64_t)(ok ? kw : 0) * ldkv;
 #pragma unroll
     for (int t = 0; t < DSTEPS; ++t) {
       kf[t] = ok ? M::load(kg + off + KSTEP * t + KPL * h) : op_t{};
@@ -250,63 +262,70 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kernel(BwdArgs a) {
     }
   };
 
-  if (lo <= hi) {
-    tile_load_lds<T, D, BN>(kg + (int64_t)kb0 * ld, ld, it.skv - kb0, kblk, tid);
-    if constexpr (kKVlds) tile_load_lds<T, D, BN>(vg + (int64_t)kb0 * ld, ld, it.skv - kb0, vblk, tid);
-    load_qtile(lo, 0);
-    store_rows(0);
-    wait_vmem();
-    __syncthreads();
-  }
-  for (int tile = lo; tile <= hi; ++tile) {
-    const int b = (tile - lo) & 1;
-    if (tile < hi) load_qtile(tile + 1, b ^ 1);
-    if (tile < flo || tile > fhi)
-      phase_a(std::true_type{}, tile, b);
-    else
-      phase_a(std::false_type{}, tile, b);
-    __syncthreads();
-
-    // dQ[32 rows x 32 d] = dS[rows, 128 keys] K[128 keys, d-block wd]
-    const int nrows = it.sq - tile * BM < BM ? it.sq - tile * BM : BM;
-    const bool full_rows = nrows == BM;
-    const __amdgpu_buffer_rsrc_t dq_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        a.dq_acc + ((int64_t)it.q_base + tile * BM) * ld + head * D, (short)0,
-        (int)(((int64_t)(nrows - 1) * ld + D) * 4), 0x00020000);
-#pragma unroll
-    for (int k = 0; k < TASKS; ++k) {
-      const int qb = w / NDB + k * WPD;
-      floatx16 acc = floatx16{};
-#pragma unroll
-      for (int t = 0; t < KSTEPS; ++t) {
-        const op_t sa = M::load(reinterpret_cast<const T*>(
-            sbuf + tile_off<SRB>(32 * qb + c, (KSTEP * t + KPL * h) * ES)));
-        op_t kb;
-        if constexpr (sizeof(T) == 2)
-          kb = tr_operand<RB, false>(kblk, KSTEP * t, wd, lane);
-        else
-          kb = *reinterpret_cast<const T*>(kblk + tile_off<RB>(KSTEP * t + h, (32 * wd + c) * ES));
-        acc = M::mma(sa, kb, acc);
+  for (int gi = 0; gi < G; ++gi) {
+    set_head(kvh * G + gi);
+    if (lo <= hi) {
+      if (gi == 0) {
+        tile_load_lds<T, D, BN>(kg + (int64_t)kb0 * ldkv, ldkv, it.skv - kb0, kblk, tid);
+        if constexpr (kKVlds)
+          tile_load_lds<T, D, BN>(vg + (int64_t)kb0 * ldkv, ldkv, it.skv - kb0, vblk, tid);
       }
-      // buffer atomics: wave-uniform row offset in an SGPR, one lane offset
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = tile * BM + 32 * qb + c_row(r, h);
-        const int soff = (32 * qb + 8 * (r >> 2) + (r & 3)) * ld4;
-        if (full_rows || i < it.sq)
-          __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[r], dq_rsrc, dq_lane_off, soff, 0);
-      }
+      load_qtile(lo, 0);
+      store_rows(0);
+      wait_vmem();
+      __syncthreads();
     }
-    if (tile < hi) store_rows(b ^ 1);
-    wait_vmem();
-    __syncthreads();
-  }
+    for (int tile = lo; tile <= hi; ++tile) {
+      const int b = (tile - lo) & 1;
+      if (tile < hi) load_qtile(tile + 1, b ^ 1);
+      if (tile < flo || tile > fhi)
+        phase_a(std::true_type{}, tile, b);
+      else
+        phase_a(std::false_type{}, tile, b);
+      __syncthreads();
+
+      // dQ[32 rows x 32 d] = dS[rows, 128 keys] K[128 keys, d-block wd]
+      const int nrows = it.sq - tile * BM < BM ? it.sq - tile * BM : BM;
+      const bool full_rows = nrows == BM;
+      const __amdgpu_buffer_rsrc_t dq_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+          a.dq_acc + ((int64_t)it.q_base + tile * BM) * ld + head * D, (short)0,
+          (int)(((int64_t)(nrows - 1) * ld + D) * 4), 0x00020000);
+  #pragma unroll
+      for (int k = 0; k < TASKS; ++k) {
+        const int qb = w / NDB + k * WPD;
+        floatx16 acc = floatx16{};
+  #pragma unroll
+        for (int t = 0; t < KSTEPS; ++t) {
+          const op_t sa = M::load(reinterpret_cast<const T*>(
+              sbuf + tile_off<SRB>(32 * qb + c, (KSTEP * t + KPL * h) * ES)));
+          op_t kb;
+          if constexpr (sizeof(T) == 2)
+            kb = tr_operand<RB, false>(kblk, KSTEP * t, wd, lane);
+          else
+            kb = *reinterpret_cast<const T*>(kblk + tile_off<RB>(KSTEP * t + h, (32 * wd + c) * ES));
+          acc = M::mma(sa, kb, acc);
+        }
+        // buffer atomics: wave-uniform row offset in an SGPR, one lane offset
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int i = tile * BM + 32 * qb + c_row(r, h);
+          const int soff = (32 * qb + 8 * (r >> 2) + (r & 3)) * ld4;
+          if (full_rows || i < it.sq)
+            __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[r], dq_rsrc, dq_lane_off, soff, 0);
+        }
+      }
+      if (tile < hi) store_rows(b ^ 1);
+      wait_vmem();
+      __syncthreads();
+    }
+
+  }  // query heads of the group
 
   // epilogue: this lane's key column of dK^T / dV^T
   if (kw < it.skv) {
     const int64_t tok = (int64_t)it.kv_base + kw;
-    T* dkp = static_cast<T*>(a.dk) + tok * ld + head * D;
-    T* dvp = static_cast<T*>(a.dv) + tok * ld + head * D;
+    T* dkp = static_cast<T*>(a.dk) + tok * ldkv + kvh * D;
+    T* dvp = static_cast<T*>(a.dv) + tok * ldkv + kvh * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -356,7 +375,7 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kernel(BwdArgs a) {
 // scheduling fences keeping that order.  LDS holds two slabs (the tiles of
 // query/key tile t and t+1, loaded straight from HBM); the lane offsets into
 // them sit in registers and move to the other slab once per tile.
-template <int D>
+template <int D, bool kGroups>
 __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
   using M = Mfma<bf16>;
   using op_t = M::op_t;
@@ -392,15 +411,26 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, h = lane >> 5, c = lane & 31;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int head = L / a.n_items;
-  const Item it = a.items[L - head * a.n_items];
-  const int64_t ld = (int64_t)a.num_heads * D;
-  const bf16* qg = static_cast<const bf16*>(a.q) + (int64_t)it.q_base * ld + head * D;
-  const bf16* dyg = static_cast<const bf16*>(a.dy) + (int64_t)it.q_base * ld + head * D;
-  const bf16* kg = static_cast<const bf16*>(a.k) + (int64_t)it.kv_base * ld + head * D;
-  const bf16* vg = static_cast<const bf16*>(a.v) + (int64_t)it.kv_base * ld + head * D;
-  const float* lse_g = a.lse2 + (int64_t)head * a.t_q + it.q_base;
-  const float* drow_g = a.drow + (int64_t)head * a.t_q + it.q_base;
+  const int kvh = L / a.n_items;  // the grid runs over key/value heads
+  const Item it = a.items[L - kvh * a.n_items];
+  // query heads sharing this K / V (kGroups == false: exactly one)
+  const int G = kGroups ? a.num_heads / a.num_kv_heads : 1;
+  const int64_t ld = (int64_t)a.num_heads * D;       // q / dy row stride
+  const int64_t ldkv = (int64_t)a.num_kv_heads * D;  // k / v / dk / dv row stride
+  const bf16* kg = static_cast<const bf16*>(a.k) + (int64_t)it.kv_base * ldkv + kvh * D;
+  const bf16* vg = static_cast<const bf16*>(a.v) + (int64_t)it.kv_base * ldkv + kvh * D;
+  // the query head being processed (the group's heads run one after another,
+  // accumulating into the same dK / dV registers) and its tensors
+  const bf16* qg = nullptr;
+  const bf16* dyg = nullptr;
+  const float* lse_g = nullptr;
+  const float* drow_g = nullptr;
+  auto set_head = [&](int hq) {
+    qg = static_cast<const bf16*>(a.q) + (int64_t)it.q_base * ld + hq * D;
+    dyg = static_cast<const bf16*>(a.dy) + (int64_t)it.q_base * ld + hq * D;
+    lse_g = a.lse2 + (int64_t)hq * a.t_q + it.q_base;
+    drow_g = a.drow + (int64_t)hq * a.t_q + it.q_base;
+  };
   const int kw = it.block * BN + 32 * w + c;  // this lane's key (sequence-local)
   const int lo = it.tiles[0] & 0xffff, hi = (it.tiles[0] >> 16) & 0xffff;
   const int flo = it.full[0] & 0xffff, fhi = (it.full[0] >> 16) & 0xffff;
@@ -416,7 +446,7 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
   op_t kr[DSTEPS], vr[DSTEPS];
   {
     const bool ok = kw < it.skv;
-    const int64_t off = (int64_t)(ok ? kw : 0) * ld + 8 * h;
+    const int64_t off = (int64_t)(ok ? kw : 0) * ldkv + 8 * h;
 #pragma unroll
     for (int t = 0; t < DSTEPS; ++t) {
       kr[t] = ok ? M::load(kg + off + 16 * t) : op_t{};
@@ -567,13 +597,6 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
     });
   };
 
-  if (lo <= hi) {
-    load_tile(lo, 0);
-    wait_vmem();
-    store_rows(0);
-    __syncthreads();
-    if (lo < hi) load_tile(lo + 1, 1);
-  }
   auto flip = [&](int b) {  // move the lane offsets to the other slab
     const int dr = b ? -SLAB : SLAB;
 #pragma unroll
@@ -602,19 +625,31 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
       flip(b);
     }
   };
-  if (flo <= fhi) {  // masked tiles before and after the mask-free range
-    run(std::true_type{}, lo, flo - 1);
-    run(std::false_type{}, flo, fhi);
-    run(std::true_type{}, fhi + 1, hi);
-  } else {
-    run(std::true_type{}, lo, hi);
+  for (int gi = 0; gi < G; ++gi) {
+    set_head(kvh * G + gi);
+    if (lo <= hi) {
+      load_tile(lo, 0);
+      wait_vmem();
+      store_rows(0);
+      __syncthreads();
+      if (lo < hi) load_tile(lo + 1, 1);
+    }
+    if (flo <= fhi) {  // masked tiles before and after the mask-free range
+      run(std::true_type{}, lo, flo - 1);
+      run(std::false_type{}, flo, fhi);
+      run(std::true_type{}, fhi + 1, hi);
+    } else {
+      run(std::true_type{}, lo, hi);
+    }
+    // the next head starts on slab 0 again
+    if (lo <= hi && ((hi - lo + 1) & 1)) flip(1);
   }
 
   // this lane's key column of dK^T / dV^T
   if (kw < it.skv) {
     const int64_t tok = (int64_t)it.kv_base + kw;
-    bf16* dkp = static_cast<bf16*>(a.dk) + tok * ld + head * D;
-    bf16* dvp = static_cast<bf16*>(a.dv) + tok * ld + head * D;
+    bf16* dkp = static_cast<bf16*>(a.dk) + tok * ldkv + kvh * D;
+    bf16* dvp = static_cast<bf16*>(a.dv) + tok * ldkv + kvh * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -689,14 +724,19 @@ int launch_bwd_pre(const BwdPreArgs& a, int dtype, int head_dim, void* stream) {
 
 template <typename T, int D>
 static int launch_bwd_t(const BwdArgs& a, void* stream) {
-  const int64_t nwg = (int64_t)a.n_items * a.num_heads;
+  const int64_t nwg = (int64_t)a.n_items * a.num_kv_heads;  // one workgroup per key block and K/V head
   constexpr int BM = bwd_block_q(sizeof(T) == 2 ? 1 : 0, D);
-  if constexpr (sizeof(T) == 2)
-    hipLaunchKernelGGL((swa_bwd_kv_kernel<D>), dim3((unsigned)nwg), dim3(256), 0,
-                       static_cast<hipStream_t>(stream), a);
-  else
+  if constexpr (sizeof(T) == 2) {
+    if (a.num_kv_heads == a.num_heads)
+      hipLaunchKernelGGL((swa_bwd_kv_kernel<D, false>), dim3((unsigned)nwg), dim3(256), 0,
+                         static_cast<hipStream_t>(stream), a);
+    else
+      hipLaunchKernelGGL((swa_bwd_kv_kernel<D, true>), dim3((unsigned)nwg), dim3(256), 0,
+                         static_cast<hipStream_t>(stream), a);
+  } else {
     hipLaunchKernelGGL((swa_bwd_kernel<T, D, BM>), dim3((unsigned)nwg), dim3(256), 0,
                        static_cast<hipStream_t>(stream), a);
+  }
   return (int)hipGetLastError();
 }
 

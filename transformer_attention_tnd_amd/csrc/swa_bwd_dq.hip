@@ -57,11 +57,13 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_dq_kernel(BwdArgs a) {
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   const int head = L / a.n_items;
   const Item it = a.items[L - head * a.n_items];
-  const int64_t ld = (int64_t)a.num_heads * D;
+  const int64_t ld = (int64_t)a.num_heads * D;       // q / dy / dq row stride
+  const int64_t ldkv = (int64_t)a.num_kv_heads * D;  // k / v row stride
+  const int kvh = head / (a.num_heads / a.num_kv_heads);  // grouped heads share K / V
   const bf16* qg = static_cast<const bf16*>(a.q) + (int64_t)it.q_base * ld + head * D;
   const bf16* dyg = static_cast<const bf16*>(a.dy) + (int64_t)it.q_base * ld + head * D;
-  const bf16* kg = static_cast<const bf16*>(a.k) + (int64_t)it.kv_base * ld + head * D;
-  const bf16* vg = static_cast<const bf16*>(a.v) + (int64_t)it.kv_base * ld + head * D;
+  const bf16* kg = static_cast<const bf16*>(a.k) + (int64_t)it.kv_base * ldkv + kvh * D;
+  const bf16* vg = static_cast<const bf16*>(a.v) + (int64_t)it.kv_base * ldkv + kvh * D;
   const int qrow = it.block * BQ + 32 * w + c;  // this lane's query row (sequence-local)
   const int lo = it.tiles[0] & 0xffff, hi = (it.tiles[0] >> 16) & 0xffff;
   const int flo = it.full[0] & 0xffff, fhi = (it.full[0] >> 16) & 0xffff;
@@ -113,8 +115,8 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_dq_kernel(BwdArgs a) {
   auto load_tile = [&](int tile, int b) {
     const int nvalid = it.skv - tile * BN;
     char* slab = lds + b * SLAB;
-    tile_load_lds<bf16, D, BN>(kg + (int64_t)tile * BN * ld, ld, nvalid, slab, tid);
-    tile_load_lds<bf16, D, BN>(vg + (int64_t)tile * BN * ld, ld, nvalid, slab + KTB, tid);
+    tile_load_lds<bf16, D, BN>(kg + (int64_t)tile * BN * ldkv, ldkv, nvalid, slab, tid);
+    tile_load_lds<bf16, D, BN>(vg + (int64_t)tile * BN * ldkv, ldkv, nvalid, slab + KTB, tid);
   };
   auto rd128 = [&](int off) { return *reinterpret_cast<const op_t*>(lds + off); };
 

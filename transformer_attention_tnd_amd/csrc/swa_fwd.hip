@@ -93,10 +93,12 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   const int head = L / a.n_items;
   const Item it = a.items[L - head * a.n_items];
-  const int64_t ld = (int64_t)a.num_heads * D;
+  const int64_t ld = (int64_t)a.num_heads * D;       // q / out row stride
+  const int64_t ldkv = (int64_t)a.num_kv_heads * D;  // k / v row stride
+  const int kvh = head / (a.num_heads / a.num_kv_heads);  // grouped heads share K / V
   const T* qg = static_cast<const T*>(a.q) + (int64_t)it.q_base * ld + head * D;
-  const T* kg = static_cast<const T*>(a.k) + (int64_t)it.kv_base * ld + head * D;
-  const T* vg = static_cast<const T*>(a.v) + (int64_t)it.kv_base * ld + head * D;
+  const T* kg = static_cast<const T*>(a.k) + (int64_t)it.kv_base * ldkv + kvh * D;
+  const T* vg = static_cast<const T*>(a.v) + (int64_t)it.kv_base * ldkv + kvh * D;
   const int qrow = it.block * 2 * HALF + HALF * g + 32 * (w & 3) + c;  // sequence-local
   // this group's tile range, and the union over both groups (the loop range)
   const int32_t mtiles = g ? it.tiles[1] : it.tiles[0], mfull = g ? it.full[1] : it.full[0];
@@ -133,11 +135,11 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
   }
 
   auto load_k = [&](int tile, int b) {
-    tile_load_lds<T, D, BN, NT>(kg + (int64_t)tile * BN * ld, ld, it.skv - tile * BN,
+    tile_load_lds<T, D, BN, NT>(kg + (int64_t)tile * BN * ldkv, ldkv, it.skv - tile * BN,
                                 kbuf0 + b * TB, tid);
   };
   auto load_v = [&](int tile, int b) {
-    tile_load_lds<T, D, BN, NT>(vg + (int64_t)tile * BN * ld, ld, it.skv - tile * BN,
+    tile_load_lds<T, D, BN, NT>(vg + (int64_t)tile * BN * ldkv, ldkv, it.skv - tile * BN,
                                 vbuf0 + b * TB, tid);
   };
 

@@ -128,6 +128,11 @@ swa_status validate(const Problem& p, std::vector<Seq>& seqs, int64_t* end_q, in
   if (!p.cu_q || !p.cu_kv) return fail(SWA_ERR_NULLPTR, "cu_seqlens_q / cu_seqlens_kv is NULL");
   swa_status s = check_sizes(p.num_seqs, p.t_q, p.t_kv, p.num_heads, p.head_dim, p.dtype);
   if (s != SWA_OK) return s;
+  // explainer 6.2: the query head count is a whole multiple of the key/value head count
+  if (p.num_kv_heads < 1 || p.num_kv_heads > p.num_heads || p.num_heads % p.num_kv_heads != 0)
+    return fail(SWA_ERR_INVALID, "num_heads (" + std::to_string(p.num_heads) +
+                                     ") must be a positive multiple of num_kv_heads (" +
+                                     std::to_string(p.num_kv_heads) + ")");
   if (p.sparse_mode != 0 && p.sparse_mode != 2 && p.sparse_mode != 3 && p.sparse_mode != 4)
     return fail(SWA_ERR_INVALID, "The sparse_mode value should be 0, 2, 3 or 4, but got " +
                                      std::to_string(p.sparse_mode));
@@ -364,13 +369,14 @@ swa_status upload(const std::vector<Item>& items, void* dst, void* stream) {
 
 
 Problem make_problem(const int64_t* cu_q, const int64_t* cu_kv, int64_t num_seqs, int64_t t_q,
-                     int64_t t_kv, int64_t n, int64_t d, int32_t dtype, double scale,
-                     int64_t pre, int64_t next, int64_t mode) {
+                     int64_t t_kv, int64_t n, int64_t nkv, int64_t d, int32_t dtype,
+                     double scale, int64_t pre, int64_t next, int64_t mode) {
   Problem p;
   p.num_seqs = num_seqs;
   p.t_q = t_q;
   p.t_kv = t_kv;
   p.num_heads = n;
+  p.num_kv_heads = nkv;
   p.head_dim = d;
   p.dtype = dtype;
   p.scale = scale;
@@ -463,16 +469,18 @@ swa_status swa_backward_workspace_size(int64_t num_seqs, int64_t t_q, int64_t t_
   return SWA_OK;
 }
 
-swa_status swa_forward(const void* q, const void* k, const void* v, const int64_t* cu_seqlens_q,
-                       const int64_t* cu_seqlens_kv, int64_t num_seqs, int64_t t_q,
-                       int64_t t_kv, int64_t num_heads, int64_t head_dim, int32_t dtype,
-                       double scale, int64_t pre_tokens, int64_t next_tokens,
-                       int64_t sparse_mode, void* out, float* softmax_max, float* softmax_sum,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+swa_status swa_forward_gqa(const void* q, const void* k, const void* v,
+                           const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,
+                           int64_t num_seqs, int64_t t_q, int64_t t_kv, int64_t num_heads,
+                           int64_t num_kv_heads, int64_t head_dim, int32_t dtype, double scale,
+                           int64_t pre_tokens, int64_t next_tokens, int64_t sparse_mode,
+                           void* out, float* softmax_max, float* softmax_sum, void* workspace,
+                           size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !out || !softmax_max || !softmax_sum || !workspace)
     return fail(SWA_ERR_NULLPTR, "a required tensor or the workspace is NULL");
   Problem p = make_problem(cu_seqlens_q, cu_seqlens_kv, num_seqs, t_q, t_kv, num_heads,
-                           head_dim, dtype, scale, pre_tokens, next_tokens, sparse_mode);
+                           num_kv_heads, head_dim, dtype, scale, pre_tokens, next_tokens,
+                           sparse_mode);
   std::vector<Seq> seqs;
   int64_t end_q = 0, end_kv = 0;
   swa_status s = validate(p, seqs, &end_q, &end_kv);
@@ -503,6 +511,7 @@ swa_status swa_forward(const void* q, const void* k, const void* v, const int64_
     a.items = static_cast<const Item*>(workspace);
     a.n_items = static_cast<int32_t>(items.size());
     a.num_heads = static_cast<int32_t>(num_heads);
+    a.num_kv_heads = static_cast<int32_t>(num_kv_heads);
     a.scale_log2 = static_cast<float>(scale * 1.4426950408889634);
     a.mode = static_cast<int32_t>(sparse_mode);
     if ((e = timed_launch(K_FWD, stream, [&] {
@@ -513,18 +522,32 @@ swa_status swa_forward(const void* q, const void* k, const void* v, const int64_
   return SWA_OK;
 }
 
-swa_status swa_backward(const void* q, const void* k, const void* v, const void* dy,
-                        const void* out, const float* softmax_max, const float* softmax_sum,
-                        const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,
-                        int64_t num_seqs, int64_t t_q, int64_t t_kv, int64_t num_heads,
-                        int64_t head_dim, int32_t dtype, double scale, int64_t pre_tokens,
-                        int64_t next_tokens, int64_t sparse_mode, void* dq, void* dk, void* dv,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+swa_status swa_forward(const void* q, const void* k, const void* v, const int64_t* cu_seqlens_q,
+                       const int64_t* cu_seqlens_kv, int64_t num_seqs, int64_t t_q,
+                       int64_t t_kv, int64_t num_heads, int64_t head_dim, int32_t dtype,
+                       double scale, int64_t pre_tokens, int64_t next_tokens,
+                       int64_t sparse_mode, void* out, float* softmax_max, float* softmax_sum,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  return swa_forward_gqa(q, k, v, cu_seqlens_q, cu_seqlens_kv, num_seqs, t_q, t_kv, num_heads,
+                         num_heads, head_dim, dtype, scale, pre_tokens, next_tokens,
+                         sparse_mode, out, softmax_max, softmax_sum, workspace, workspace_bytes,
+                         stream);
+}
+
+swa_status swa_backward_gqa(const void* q, const void* k, const void* v, const void* dy,
+                            const void* out, const float* softmax_max,
+                            const float* softmax_sum, const int64_t* cu_seqlens_q,
+                            const int64_t* cu_seqlens_kv, int64_t num_seqs, int64_t t_q,
+                            int64_t t_kv, int64_t num_heads, int64_t num_kv_heads,
+                            int64_t head_dim, int32_t dtype, double scale, int64_t pre_tokens,
+                            int64_t next_tokens, int64_t sparse_mode, void* dq, void* dk,
+                            void* dv, void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !dy || !out || !softmax_max || !softmax_sum || !dq || !dk || !dv ||
       !workspace)
     return fail(SWA_ERR_NULLPTR, "a required tensor or the workspace is NULL");
   Problem p = make_problem(cu_seqlens_q, cu_seqlens_kv, num_seqs, t_q, t_kv, num_heads,
-                           head_dim, dtype, scale, pre_tokens, next_tokens, sparse_mode);
+                           num_kv_heads, head_dim, dtype, scale, pre_tokens, next_tokens,
+                           sparse_mode);
   std::vector<Seq> seqs;
   int64_t end_q = 0, end_kv = 0;
   swa_status s = validate(p, seqs, &end_q, &end_kv);
@@ -570,6 +593,7 @@ swa_status swa_backward(const void* q, const void* k, const void* v, const void*
   a.items = reinterpret_cast<const Item*>(ws + L.items);
   a.n_items = static_cast<int32_t>(n_kv_items);
   a.num_heads = static_cast<int32_t>(num_heads);
+  a.num_kv_heads = static_cast<int32_t>(num_kv_heads);
   a.t_q = static_cast<int32_t>(t_q);
   a.scale = static_cast<float>(scale);
   a.scale_log2 = static_cast<float>(scale * 1.4426950408889634);
@@ -602,8 +626,8 @@ swa_status swa_backward(const void* q, const void* k, const void* v, const void*
       return fail(SWA_ERR_HIP, hip_error_string(e));
   }
   if (end_kv < t_kv) {
-    FillArgs f{dk, static_cast<int64_t>(elem_bytes(dtype)), num_heads * head_dim, end_kv, t_kv,
-               nullptr, nullptr, 0};
+    FillArgs f{dk, static_cast<int64_t>(elem_bytes(dtype)), num_kv_heads * head_dim, end_kv,
+               t_kv, nullptr, nullptr, 0};
     if ((e = timed_launch(K_FILL, stream, [&] { return launch_fill(f, stream); })) != 0)
       return fail(SWA_ERR_HIP, hip_error_string(e));
     f.x = dv;
@@ -611,6 +635,19 @@ swa_status swa_backward(const void* q, const void* k, const void* v, const void*
       return fail(SWA_ERR_HIP, hip_error_string(e));
   }
   return SWA_OK;
+}
+
+swa_status swa_backward(const void* q, const void* k, const void* v, const void* dy,
+                        const void* out, const float* softmax_max, const float* softmax_sum,
+                        const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,
+                        int64_t num_seqs, int64_t t_q, int64_t t_kv, int64_t num_heads,
+                        int64_t head_dim, int32_t dtype, double scale, int64_t pre_tokens,
+                        int64_t next_tokens, int64_t sparse_mode, void* dq, void* dk, void* dv,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  return swa_backward_gqa(q, k, v, dy, out, softmax_max, softmax_sum, cu_seqlens_q,
+                          cu_seqlens_kv, num_seqs, t_q, t_kv, num_heads, num_heads, head_dim,
+                          dtype, scale, pre_tokens, next_tokens, sparse_mode, dq, dk, dv,
+                          workspace, workspace_bytes, stream);
 }
 
 swa_status swa_debug_tile_schedule(const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,
@@ -624,8 +661,8 @@ swa_status swa_debug_tile_schedule(const int64_t* cu_seqlens_q, const int64_t* c
   if (direction < 0 || direction > 2)
     return fail(SWA_ERR_INVALID,
                 "direction must be 0 (forward), 1 (backward dK/dV) or 2 (backward dQ)");
-  Problem p = make_problem(cu_seqlens_q, cu_seqlens_kv, num_seqs, t_q, t_kv, 1, head_dim, dtype,
-                           1.0, pre_tokens, next_tokens, sparse_mode);
+  Problem p = make_problem(cu_seqlens_q, cu_seqlens_kv, num_seqs, t_q, t_kv, 1, 1, head_dim,
+                           dtype, 1.0, pre_tokens, next_tokens, sparse_mode);
   std::vector<Seq> seqs;
   int64_t end_q = 0, end_kv = 0;
   swa_status s = validate(p, seqs, &end_q, &end_kv);

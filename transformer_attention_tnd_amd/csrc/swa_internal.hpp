@@ -48,7 +48,7 @@ inline int32_t pack_range(int64_t lo, int64_t hi) {
 }
 
 struct Problem {
-  int64_t num_seqs, t_q, t_kv, num_heads, head_dim;
+  int64_t num_seqs, t_q, t_kv, num_heads, num_kv_heads, head_dim;
   int32_t dtype;
   double scale;
   int64_t pre_tokens, next_tokens, sparse_mode;
@@ -66,7 +66,8 @@ struct FwdArgs {
   float* ssum;
   const Item* items;
   int32_t n_items;
-  int32_t num_heads;
+  int32_t num_heads;     // query heads (q, out, statistics)
+  int32_t num_kv_heads;  // key/value heads; query head n reads head n / (num_heads / num_kv_heads)
   float scale_log2;  // scale * log2(e)
   int32_t mode;      // 0: no mask; otherwise each item's band applies
 };
@@ -97,7 +98,8 @@ struct BwdArgs {
   void* dv;
   const Item* items;
   int32_t n_items;
-  int32_t num_heads;
+  int32_t num_heads;     // query heads (q, dy, dq, D, lse2)
+  int32_t num_kv_heads;  // key/value heads (k, v, dk, dv); the dK/dV grid runs over these
   int32_t t_q;
   float scale;
   float scale_log2;

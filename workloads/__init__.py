@@ -143,20 +143,23 @@ def make_problem(w: Workload | str, seed: int | None = None) -> Problem:
 
 def make_custom(lengths_q, lengths_kv=None, num_heads=2, head_dim=64, dtype=torch.bfloat16,
                 sparse_mode=0, pre_tokens=INT_MAX, next_tokens=INT_MAX, scale=None,
-                std=1.0, seed=42, trailing=0, extra_tokens=0, name="custom") -> Problem:
+                std=1.0, seed=42, trailing=0, extra_tokens=0, name="custom",
+                num_kv_heads=None) -> Problem:
     """Small seeded problem with explicit sequence lengths.
 
     ``trailing`` appends that many non-participating batches (zeros in the
     cumulative arrays); ``extra_tokens`` appends tokens after the last
-    sequence that belong to no batch.
+    sequence that belong to no batch.  ``num_kv_heads`` (default: num_heads) gives k
+    and v fewer heads than q (grouped heads).
     """
     lengths_kv = list(lengths_q) if lengths_kv is None else list(lengths_kv)
     g = torch.Generator("cpu").manual_seed(seed)
     tq = sum(lengths_q) + extra_tokens
     tkv = sum(lengths_kv) + extra_tokens
     q = _randn(g, (tq, num_heads, head_dim), std, dtype)
-    k = _randn(g, (tkv, num_heads, head_dim), std, dtype)
-    v = _randn(g, (tkv, num_heads, head_dim), std, dtype)
+    nkv = num_heads if num_kv_heads is None else num_kv_heads
+    k = _randn(g, (tkv, nkv, head_dim), std, dtype)
+    v = _randn(g, (tkv, nkv, head_dim), std, dtype)
     dy = _randn(g, (tq, num_heads, head_dim), std, dtype)
     cu_q = cumulative(lengths_q) + [0] * trailing
     cu_kv = cumulative(lengths_kv) + [0] * trailing
