@@ -39,10 +39,11 @@ _HDRS = tuple(_CSRC + f for f in ("swa_common.hpp", "swa_internal.hpp"))
 # record of a kernel is valid only for the exact text of these files)
 KERNEL_SOURCES = {
     "forward": (_CSRC + "swa_fwd.hip",) + _HDRS,
-    "backward": (_CSRC + "swa_bwd.hip", _CSRC + "swa_pipe.hpp") + _HDRS,
+    "backward": (_CSRC + "swa_bwd_kv.hip", _CSRC + "swa_bwd_kv.hpp",
+                 _CSRC + "swa_pipe.hpp") + _HDRS,
     "bwd_dq": (_CSRC + "swa_bwd_dq.hip", _CSRC + "swa_pipe.hpp") + _HDRS,
-    "bwd_pre": (_CSRC + "swa_bwd.hip", _CSRC + "swa_pipe.hpp") + _HDRS,
-    "dq_finalize": (_CSRC + "swa_bwd.hip", _CSRC + "swa_pipe.hpp") + _HDRS,
+    "bwd_pre": (_CSRC + "swa_bwd.hip",) + _HDRS,
+    "dq_finalize": (_CSRC + "swa_bwd.hip",) + _HDRS,
 }
 BWD_KERNELS = ("bwd_pre", "backward", "bwd_dq", "dq_finalize")
 

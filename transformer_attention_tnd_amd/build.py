@@ -17,8 +17,10 @@ SOURCES = {
     "swa_host.cpp": [],
     "swa_fwd.hip": [],
     "swa_bwd.hip": [],
-    # matrix-core results in ordinary vector registers: the dQ kernel's
-    # softmax then reads them without accumulator-register copies
+    # matrix-core results in ordinary vector registers: the softmax of the
+    # bf16 backward kernels then reads them without accumulator-register copies
+    "swa_bwd_kv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "swa_bwd_kv_gqa.hip": [],
     "swa_bwd_dq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 ARCH = os.environ.get("SWA_OFFLOAD_ARCH", "gfx950")

@@ -12,8 +12,8 @@
 // swa_bwd_pre_kernel: D and the per-row log2-domain normaliser
 //   lse2 = softmax_max * log2(e) + log2(softmax_sum), so that P = exp2(s*c - lse2)
 //   with c = scale * log2(e); for fp32 it also zeroes the dq accumulator.
-// bf16: swa_bwd_kv_kernel (dK, dV) and swa_bwd_dq_kernel (dQ, in swa_bwd_dq.hip), the two-pass
-//   structure with no atomics (described below).
+// bf16: swa_bwd_kv_kernel (dK, dV, in swa_bwd_kv.hip) and swa_bwd_dq_kernel
+//   (dQ, in swa_bwd_dq.hip), the two-pass structure with no atomics.
 // fp32: swa_bwd_kernel, one pass: one workgroup per (block of 128 keys,
 //   head); each of its 4 waves owns 32 keys and keeps its dK, dV
 //   accumulators in registers while it walks the query tiles of the band.
@@ -33,7 +33,6 @@
 #include <utility>
 
 #include "swa_common.hpp"
-#include "swa_pipe.hpp"
 
 namespace swa {
 
@@ -355,319 +354,6 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kernel(BwdArgs a) {
   }
 }
 
-// bf16 backward in two kernels, no atomics (deterministic): the two-pass
-// structure of the PyPTO-Gym FlashAttentionScoreGrad article (两趟循环结构),
-// which recomputes P and dS in both passes.
-//   swa_bwd_kv_kernel: one workgroup per (block of 128 keys, head); each of
-//     its 4 waves owns 32 keys, keeps its K and V rows in registers (B
-//     operands of S = Q K^T and dP = dY V^T) and its dK^T, dV^T accumulators,
-//     and walks the query tiles (64 rows) of the band.
-//   swa_bwd_dq_kernel: one workgroup per (block of 128 query rows, head);
-//     each wave owns 32 rows, keeps its Q and dY rows in registers (B operands
-//     of S^T = K Q^T and dP^T = V dY^T) and its dQ^T accumulator, and walks the
-//     key tiles (64 keys) of the band; dQ^T += K^T dS^T takes K^T from the
-//     key tile through transposing LDS reads.  dq is written once, in the
-//     input type.
-// Both are organised for one wave per SIMD.  The products of a tile form one
-// software pipeline in a fixed order; each LDS operand is read a fixed number
-// of products ahead into a small register ring, and the vector work (the
-// softmax elements) is spread over the slots between products, with
-// scheduling fences keeping that order.  LDS holds two slabs (the tiles of
-// query/key tile t and t+1, loaded straight from HBM); the lane offsets into
-// them sit in registers and move to the other slab once per tile.
-template <int D, bool kGroups>
-__global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
-  using M = Mfma<bf16>;
-  using op_t = M::op_t;
-  constexpr int BN = BWD_BN;           // keys per workgroup
-  constexpr int BM = 64;               // query rows per tile
-  constexpr int RB = D * 2;            // row bytes
-  constexpr int QTB = BM * RB;         // Q or dY tile bytes
-  constexpr int SLAB = 2 * QTB;        // Q | dY
-  constexpr int NDB = D / 32;          // head-dim blocks
-  constexpr int DSTEPS = D / 16;       // contraction steps over d
-  // products of one tile, in issue order: S/dP of rows 0-31, of rows 32-63,
-  // dV/dK of rows 0-31, of rows 32-63
-  constexpr int NS = 2 * DSTEPS, NV = 4 * NDB;
-  constexpr int G_S1 = NS, G_V0 = 2 * NS, G_V1 = G_V0 + NV, NOPS = G_V1 + NV;
-  constexpr int AHEAD = SWA_BWD_AHEAD, RING = AHEAD + 1;
-  static_assert(BN == 128 && (D == 64 || D == 128), "4 waves x 32 keys, 64-row tiles");
-  // Slot of the first softmax stage of register r of block qb: the 16
-  // registers are spread evenly from the end of the block's S / dP products
-  // to two slots before the dV / dK products that use registers 8..15;
-  // registers 0..7 then finish before the products that use them.
-  constexpr auto kv_soft_slot = [](int qb, int r) {
-    const int rel = qb == 0 ? G_S1 : G_V0, last = (qb == 0 ? G_V0 : G_V1) + NV / 2 - 2;
-    return rel + (r * (last - rel)) / 15;
-  };
-  static_assert(kv_soft_slot(0, 7) + 1 < G_V0 && kv_soft_slot(1, 7) + 1 < G_V1 &&
-                kv_soft_slot(0, 15) + 1 < G_V0 + NV / 2 && kv_soft_slot(1, 15) + 1 < G_V1 + NV / 2,
-                "softmax stages finish before the products that use them");
-
-  __shared__ __attribute__((aligned(1024))) char lds[2 * SLAB];
-  __shared__ floatx4 lse_s[2][BM / 4];   // lse2 of the tile's rows
-  __shared__ floatx4 drow_s[2][BM / 4];  // D of the tile's rows
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6, h = lane >> 5, c = lane & 31;
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int kvh = L / a.n_items;  // the grid runs over key/value heads
-  const Item it = a.items[L - kvh * a.n_items];
-  // query heads sharing this K / V (kGroups == false: exactly one)
-  const int G = kGroups ? a.num_heads / a.num_kv_heads : 1;
-  const int64_t ld = (int64_t)a.num_heads * D;       // q / dy row stride
-  const int64_t ldkv = (int64_t)a.num_kv_heads * D;  // k / v / dk / dv row stride
-  const bf16* kg = static_cast<const bf16*>(a.k) + (int64_t)it.kv_base * ldkv + kvh * D;
-  const bf16* vg = static_cast<const bf16*>(a.v) + (int64_t)it.kv_base * ldkv + kvh * D;
-  // the query head being processed (the group's heads run one after another,
-  // accumulating into the same dK / dV registers) and its tensors
-  const bf16* qg = nullptr;
-  const bf16* dyg = nullptr;
-  const float* lse_g = nullptr;
-  const float* drow_g = nullptr;
-  auto set_head = [&](int hq) {
-    qg = static_cast<const bf16*>(a.q) + (int64_t)it.q_base * ld + hq * D;
-    dyg = static_cast<const bf16*>(a.dy) + (int64_t)it.q_base * ld + hq * D;
-    lse_g = a.lse2 + (int64_t)hq * a.t_q + it.q_base;
-    drow_g = a.drow + (int64_t)hq * a.t_q + it.q_base;
-  };
-  const int kw = it.block * BN + 32 * w + c;  // this lane's key (sequence-local)
-  const int lo = it.tiles[0] & 0xffff, hi = (it.tiles[0] >> 16) & 0xffff;
-  const int flo = it.full[0] & 0xffff, fhi = (it.full[0] >> 16) & 0xffff;
-  const float c2 = a.scale_log2;
-
-  floatx16 dk[NDB], dv[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    dk[db] = floatx16{};
-    dv[db] = floatx16{};
-  }
-  // B operands of S and dP: lane (column kw) holds K[kw][16t + 8h + e], V likewise
-  op_t kr[DSTEPS], vr[DSTEPS];
-  {
-    const bool ok = kw < it.skv;
-    const int64_t off = (int64_t)(ok ? kw : 0) * ldkv + 8 * h;
-#pragma unroll
-    for (int t = 0; t < DSTEPS; ++t) {
-      kr[t] = ok ? M::load(kg + off + 16 * t) : op_t{};
-      vr[t] = ok ? M::load(vg + off + 16 * t) : op_t{};
-    }
-  }
-  // Rows allowed for this lane's key: i in [i_min, i_max] (empty if the key
-  // is past the sequence), from the band rule -pre <= kw - i <= next.
-  int i_min = 0, i_max = it.sq - 1;
-  if (a.mode != 0) {  // 64-bit: pre / next may be near the int range
-    const int64_t lo64 = (int64_t)kw - it.band[1], hi64 = (int64_t)kw + it.band[0];
-    i_min = lo64 < 0 ? 0 : (lo64 > it.sq ? it.sq : (int)lo64);
-    i_max = hi64 < i_max ? (hi64 < -1 ? -1 : (int)hi64) : i_max;
-  }
-  if (kw >= it.skv) i_max = -1;
-
-  // Lane offsets (slab of the current tile).  Rows 16 apart share a swizzle,
-  // so the 32-row block, the 16-row step and Q vs dY are immediate offsets.
-  int oq[DSTEPS];   // 128-bit read of row c, chunk 2t + h
-  int otr[NDB][2];  // transposing reads, head-dim block db
-  int olr = 16 * h; // lse2 / D of rows 4h .. 4h + 3 of each 8
-#pragma unroll
-  for (int t = 0; t < DSTEPS; ++t) oq[t] = tile_off<RB>(c, (16 * t + 8 * h) * 2);
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) tr_offsets<RB>(lane, db, otr[db][0], otr[db][1]);
-
-  float sreg = 0.f;
-  auto load_tile = [&](int tile, int b) {
-    const int nvalid = it.sq - tile * BM;
-    char* slab = lds + b * SLAB;
-    tile_load_lds<bf16, D, BM>(qg + (int64_t)tile * BM * ld, ld, nvalid, slab, tid);
-    tile_load_lds<bf16, D, BM>(dyg + (int64_t)tile * BM * ld, ld, nvalid, slab + QTB, tid);
-    if (tid < 2 * BM) {
-      const int row = tid & (BM - 1), i = tile * BM + row;
-      if (tid < BM)
-        sreg = i < it.sq ? lse_g[i] : INFINITY;
-      else
-        sreg = i < it.sq ? drow_g[i] : 0.f;
-    }
-  };
-  auto store_rows = [&](int b) {
-    if (tid < BM)
-      reinterpret_cast<float*>(lse_s[b])[tid] = sreg;
-    else if (tid < 2 * BM)
-      reinterpret_cast<float*>(drow_s[b])[tid - BM] = sreg;
-  };
-  auto rd128 = [&](int off) { return *reinterpret_cast<const op_t*>(lds + off); };
-
-  // One query tile: S, dP, P, dS, dV^T += dY^T P, dK^T += Q^T dS.
-  auto step = [&](auto mask_tag, int tile) {
-    constexpr bool kMask = decltype(mask_tag)::value;
-    // row 32 qb + 8 g + 4 h + e is allowed iff 32 qb + 8 g + e is in [rel_lo, rel_hi]
-    int rel_lo = 0, rel_hi = 0;
-    if constexpr (kMask) {
-      rel_lo = i_min - tile * BM - 4 * h;
-      rel_hi = i_max - tile * BM - 4 * h;
-      asm volatile("" : "+v"(rel_lo), "+v"(rel_hi));
-    }
-    op_t ring[RING];
-    floatx16 s[2], dp[2];
-    floatx4 lv[2][4], dv4[2][4];
-    op_t pk[2][2], sk[2][2];
-
-    auto read = [&](auto ic) {
-      constexpr int i = decltype(ic)::value;
-      if constexpr (i < G_V0) {
-        constexpr int qb = i / NS, t = (i % NS) / 2, isdp = i % 2;
-        ring[i % RING] = rd128(oq[t] + isdp * QTB + 32 * qb * RB);
-      } else {
-        constexpr int j = i - G_V0, qb = j / NV, jj = j % NV;
-        constexpr int t2 = jj / (2 * NDB), db = (jj / 2) % NDB, isdv = 1 - jj % 2;
-        constexpr int imm = isdv * QTB + (32 * qb + 16 * t2) * RB;
-        ring[i % RING] = tr_pair(lds + otr[db][0] + imm, lds + otr[db][1] + imm);
-      }
-    };
-    auto mfma = [&](auto ic) {
-      constexpr int i = decltype(ic)::value;
-      const op_t& x = ring[i % RING];
-      if constexpr (i < G_V0) {
-        constexpr int qb = i / NS, t = (i % NS) / 2;
-        if constexpr (i % 2 == 0)
-          s[qb] = M::mma(x, kr[t], t == 0 ? floatx16{} : s[qb]);
-        else
-          dp[qb] = M::mma(x, vr[t], t == 0 ? floatx16{} : dp[qb]);
-      } else {
-        constexpr int j = i - G_V0, qb = j / NV, jj = j % NV;
-        constexpr int t2 = jj / (2 * NDB), db = (jj / 2) % NDB;
-        if constexpr (jj % 2 == 0)
-          dv[db] = M::mma(x, pk[qb][t2], dv[db]);
-        else
-          dk[db] = M::mma(x, sk[qb][t2], dk[db]);
-      }
-    };
-    // Softmax of accumulator register r of block qb in two stages one slot
-    // apart (so no instruction waits on the one before it):
-    //   A: P = exp2(s c - lse2), masked;   B: dS = P (dP - D), and each
-    //   completed pair of P and dS is rounded into the dV / dK operands.
-    auto soft_a = [&](int qb, int r) {
-      const int g = r >> 2, e = r & 3;
-      float p = __builtin_amdgcn_exp2f(fmaf(s[qb][r], c2, -lv[qb][g][e]));
-      if constexpr (kMask) {
-        const int rel = 32 * qb + 8 * g + e;
-        p = (rel >= rel_lo && rel <= rel_hi) ? p : 0.f;
-      }
-      s[qb][r] = p;
-    };
-    auto soft_b = [&](int qb, int r) {
-      dp[qb][r] = s[qb][r] * (dp[qb][r] - dv4[qb][r >> 2][r & 3]);
-      if (r & 1) {
-        pk[qb][r >> 3][(r & 7) - 1] = static_cast<bf16>(s[qb][r - 1]);
-        pk[qb][r >> 3][r & 7] = static_cast<bf16>(s[qb][r]);
-        sk[qb][r >> 3][(r & 7) - 1] = static_cast<bf16>(dp[qb][r - 1]);
-        sk[qb][r >> 3][r & 7] = static_cast<bf16>(dp[qb][r]);
-      }
-    };
-    auto valu = [&](auto mc) {
-      constexpr int m = decltype(mc)::value;
-      // lse2 / D rows of block qb early in its S / dP products
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        if (m == qb * NS + 1) {
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int off = olr + (32 * qb + 8 * g) * 4;
-            lv[qb][g] = *reinterpret_cast<const floatx4*>(reinterpret_cast<const char*>(lse_s) + off);
-            dv4[qb][g] = *reinterpret_cast<const floatx4*>(reinterpret_cast<const char*>(drow_s) + off);
-          }
-        }
-      }
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          if (m == kv_soft_slot(qb, r)) soft_a(qb, r);
-          if (m == kv_soft_slot(qb, r) + 1) soft_b(qb, r);
-        }
-      }
-    };
-
-    static_for<NOPS + AHEAD>([&](auto sc) {
-      constexpr int sl = decltype(sc)::value;
-      if constexpr (sl < NOPS) read(std::integral_constant<int, sl>{});
-      if constexpr (sl >= AHEAD) {
-        mfma(std::integral_constant<int, sl - AHEAD>{});
-        valu(std::integral_constant<int, sl - AHEAD>{});
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    });
-  };
-
-  auto flip = [&](int b) {  // move the lane offsets to the other slab
-    const int dr = b ? -SLAB : SLAB;
-#pragma unroll
-    for (int t = 0; t < DSTEPS; ++t) {
-      oq[t] += dr;
-      asm volatile("" : "+v"(oq[t]));
-    }
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      otr[db][0] += dr;
-      otr[db][1] += dr;
-      asm volatile("" : "+v"(otr[db][0]), "+v"(otr[db][1]));
-    }
-    olr += b ? -(int)sizeof(lse_s[0]) : (int)sizeof(lse_s[0]);
-    asm volatile("" : "+v"(olr));
-  };
-  // tiles [from, to] in order, each body branch-free (masked or not)
-  auto run = [&](auto mask_tag, int from, int to) {
-    for (int tile = from; tile <= to; ++tile) {
-      const int b = (tile - lo) & 1;
-      step(mask_tag, tile);
-      if (tile < hi) store_rows(b ^ 1);
-      wait_vmem();
-      __syncthreads();
-      if (tile + 2 <= hi) load_tile(tile + 2, b);
-      flip(b);
-    }
-  };
-  for (int gi = 0; gi < G; ++gi) {
-    set_head(kvh * G + gi);
-    if (lo <= hi) {
-      load_tile(lo, 0);
-      wait_vmem();
-      store_rows(0);
-      __syncthreads();
-      if (lo < hi) load_tile(lo + 1, 1);
-    }
-    if (flo <= fhi) {  // masked tiles before and after the mask-free range
-      run(std::true_type{}, lo, flo - 1);
-      run(std::false_type{}, flo, fhi);
-      run(std::true_type{}, fhi + 1, hi);
-    } else {
-      run(std::true_type{}, lo, hi);
-    }
-    // the next head starts on slab 0 again
-    if (lo <= hi && ((hi - lo + 1) & 1)) flip(1);
-  }
-
-  // this lane's key column of dK^T / dV^T
-  if (kw < it.skv) {
-    const int64_t tok = (int64_t)it.kv_base + kw;
-    bf16* dkp = static_cast<bf16*>(a.dk) + tok * ldkv + kvh * D;
-    bf16* dvp = static_cast<bf16*>(a.dv) + tok * ldkv + kvh * D;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * db + 8 * g + 4 * h;
-        bf16x4 k4, v4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          k4[e] = static_cast<bf16>(dk[db][4 * g + e] * a.scale);
-          v4[e] = static_cast<bf16>(dv[db][4 * g + e]);
-        }
-        *reinterpret_cast<bf16x4*>(dkp + d0) = k4;
-        *reinterpret_cast<bf16x4*>(dvp + d0) = v4;
-      }
-    }
-  }
-}
-
 template <typename T>
 __global__ __launch_bounds__(256) void swa_dq_finalize_kernel(FinalizeArgs a) {
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
@@ -726,23 +412,13 @@ template <typename T, int D>
 static int launch_bwd_t(const BwdArgs& a, void* stream) {
   const int64_t nwg = (int64_t)a.n_items * a.num_kv_heads;  // one workgroup per key block and K/V head
   constexpr int BM = bwd_block_q(sizeof(T) == 2 ? 1 : 0, D);
-  if constexpr (sizeof(T) == 2) {
-    if (a.num_kv_heads == a.num_heads)
-      hipLaunchKernelGGL((swa_bwd_kv_kernel<D, false>), dim3((unsigned)nwg), dim3(256), 0,
-                         static_cast<hipStream_t>(stream), a);
-    else
-      hipLaunchKernelGGL((swa_bwd_kv_kernel<D, true>), dim3((unsigned)nwg), dim3(256), 0,
-                         static_cast<hipStream_t>(stream), a);
-  } else {
-    hipLaunchKernelGGL((swa_bwd_kernel<T, D, BM>), dim3((unsigned)nwg), dim3(256), 0,
-                       static_cast<hipStream_t>(stream), a);
-  }
+  hipLaunchKernelGGL((swa_bwd_kernel<T, D, BM>), dim3((unsigned)nwg), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), a);
   return (int)hipGetLastError();
 }
 
 int launch_backward(const BwdArgs& a, int dtype, int head_dim, void* stream) {
-  if (dtype == 1) return head_dim == 128 ? launch_bwd_t<bf16, 128>(a, stream)
-                                         : launch_bwd_t<bf16, 64>(a, stream);
+  if (dtype == 1) return launch_bwd_kv(a, head_dim, stream);  // swa_bwd_kv.hip
   return head_dim == 128 ? launch_bwd_t<float, 128>(a, stream)
                          : launch_bwd_t<float, 64>(a, stream);
 }

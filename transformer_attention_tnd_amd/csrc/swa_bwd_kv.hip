@@ -1,0 +1,22 @@
+// Launch of the bf16 dK/dV kernel with one query head per key/value head.
+// This file is compiled with the matrix-core results in ordinary vector
+// registers (see build.py), so the softmax reads the S and dP accumulators
+// without accumulator-register copies.
+
+#include "swa_bwd_kv.hpp"
+
+namespace swa {
+
+int launch_bwd_kv(const BwdArgs& a, int head_dim, void* stream) {
+  if (a.num_kv_heads != a.num_heads) return launch_bwd_kv_grouped(a, head_dim, stream);
+  const int64_t nwg = (int64_t)a.n_items * a.num_kv_heads;  // one workgroup per key block and head
+  if (head_dim == 128)
+    hipLaunchKernelGGL((swa_bwd_kv_kernel<128, false>), dim3((unsigned)nwg), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), a);
+  else
+    hipLaunchKernelGGL((swa_bwd_kv_kernel<64, false>), dim3((unsigned)nwg), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), a);
+  return (int)hipGetLastError();
+}
+
+}  // namespace swa

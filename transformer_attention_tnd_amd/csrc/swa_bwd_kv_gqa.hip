@@ -1,0 +1,20 @@
+// Launch of the bf16 dK/dV kernel for grouped key/value heads (each
+// workgroup runs the query heads of its group one after another).  Compiled
+// with the default register assignment.
+
+#include "swa_bwd_kv.hpp"
+
+namespace swa {
+
+int launch_bwd_kv_grouped(const BwdArgs& a, int head_dim, void* stream) {
+  const int64_t nwg = (int64_t)a.n_items * a.num_kv_heads;  // one workgroup per key block and K/V head
+  if (head_dim == 128)
+    hipLaunchKernelGGL((swa_bwd_kv_kernel<128, true>), dim3((unsigned)nwg), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), a);
+  else
+    hipLaunchKernelGGL((swa_bwd_kv_kernel<64, true>), dim3((unsigned)nwg), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), a);
+  return (int)hipGetLastError();
+}
+
+}  // namespace swa

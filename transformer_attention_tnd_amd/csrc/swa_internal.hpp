@@ -130,6 +130,10 @@ int launch_forward(const FwdArgs& a, int dtype, int head_dim, void* stream);
 int launch_bwd_pre(const BwdPreArgs& a, int dtype, int head_dim, void* stream);
 // fp32: the one-pass kernel (dK, dV and the dq accumulator); bf16: the dK/dV kernel
 int launch_backward(const BwdArgs& a, int dtype, int head_dim, void* stream);
+// bf16 only: the dK/dV kernel over the dK/dV schedule (writes dk, dv);
+// grouped key/value heads go to launch_bwd_kv_grouped
+int launch_bwd_kv(const BwdArgs& a, int head_dim, void* stream);
+int launch_bwd_kv_grouped(const BwdArgs& a, int head_dim, void* stream);
 // bf16 only: the dQ kernel over the dQ schedule (writes dq)
 int launch_bwd_dq(const BwdArgs& a, int head_dim, void* stream);
 int launch_dq_finalize(const FinalizeArgs& a, int dtype, void* stream);
