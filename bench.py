@@ -60,6 +60,10 @@ def allowed_pairs(cu_q, cu_kv, mode, pre, nxt):
         pq, pk = cq, ck
         if mode == 0:
             total += sq * skv
+        elif mode in (2, 3):  # causal from the top-left / bottom-right corner
+            i = np.arange(sq, dtype=np.int64)
+            hi = np.minimum(skv - 1, i if mode == 2 else i + skv - sq)
+            total += int(np.clip(hi + 1, 0, None).sum())
         else:
             i = np.arange(sq, dtype=np.int64)
             hi = np.minimum(skv - 1, i + nxt)
@@ -97,9 +101,11 @@ def cpu_baseline(p, n_heads_total, pairs_per_head, budget_s=12.0):
     D = p.head_dim
     t0 = time.perf_counter()
     done = 0
+    G = p.q.shape[1] // p.k.shape[1]  # query heads per key/value head
     while done < n_heads_total:
-        sl = slice(done, done + 1)
-        q, k, v, dy = (x[:, sl].contiguous() for x in (p.q, p.k, p.v, p.dy))
+        sl, skv = slice(done, done + 1), slice(done // G, done // G + 1)
+        q, dy = (x[:, sl].contiguous() for x in (p.q, p.dy))
+        k, v = (x[:, skv].contiguous() for x in (p.k, p.v))
         out, sm, ss = oracle.forward(q, k, v, p.cu_seqlens_q, p.cu_seqlens_kv, p.scale,
                                      p.pre_tokens, p.next_tokens, p.sparse_mode, chunk=256)
         oracle.backward(q, k, v, dy, out, sm, ss, p.cu_seqlens_q, p.cu_seqlens_kv, p.scale,
@@ -173,8 +179,8 @@ def main():
                    p.sparse_mode)
 
     def step():
-        swa.swa_forward(q, k, v, *args_common, out, smax, ssum, ws_f)
-        swa.swa_backward(q, k, v, dy, out, smax, ssum, *args_common, dq, dk, dv, ws_b)
+        swa.swa_forward_gqa(q, k, v, *args_common, out, smax, ssum, ws_f)
+        swa.swa_backward_gqa(q, k, v, dy, out, smax, ssum, *args_common, dq, dk, dv, ws_b)
 
     for _ in range(args.warmup):
         step()
@@ -253,7 +259,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if q.dtype == torch.bfloat16 else "f32",
         "data": "synthetic (seeded N(0,std) inputs shaped like the workload)",
-        "config": {"workload": name, "tokens": T, "num_heads": N, "head_dim": D,
+        "config": {"workload": name, "tokens": T, "num_heads": N,
+                   "num_kv_heads": k.shape[1], "head_dim": D,
                    "sparse_mode": p.sparse_mode, "pre_tokens": p.pre_tokens,
                    "next_tokens": p.next_tokens, "num_seqs": nseq,
                    "cu_seqlens": p.cu_seqlens_q if nseq <= 16 else None},

@@ -20,6 +20,9 @@ import bench  # noqa: E402
     ([300, 377, 890], [300, 377, 890], 4, 5, -3),
     ([100, 250, 0, 0], [80, 300, 0, 0], 0, 0, 0),
     ([0, 64, 64, 99], [0, 64, 64, 99], 4, 2147483647, 2147483647),
+    ([300, 377, 890], [500, 577, 600], 2, 0, 0),
+    ([300, 377, 890], [500, 577, 600], 3, 0, 0),
+    ([900, 1000], [400, 1200], 3, 7, 7),
 ])
 def test_pair_count_matches_oracle(case):
     cu_q, cu_kv, mode, pre, nxt = case

@@ -238,22 +238,29 @@ def sampled_check(p, g, samples):
     seqs = oracle.sequences(p.cu_seqlens_q)
     errs = {"out": [], "dq": [], "dk": [], "dv": []}
     smax_g, ssum_g, smax_o, ssum_o = [], [], [], []
+    G = p.q.shape[1] // p.k.shape[1]  # query heads per key/value head
     for b, n, r0, width in samples:
         s0, L = seqs[b]
         r0 = min(r0, L - width)
-        Q, K, V, dY = (x[s0:s0 + L, n] for x in (p.q, p.k, p.v, p.dy))
+        Q, dY = (x[s0:s0 + L, n] for x in (p.q, p.dy))
+        K, V = (x[s0:s0 + L, n // G] for x in (p.k, p.v))
         rows = list(range(r0, r0 + width))
         O, m, l = oracle.forward_rows(Q, K, V, rows, p.scale, p.sparse_mode, p.pre_tokens,
                                       p.next_tokens)
         dq = oracle.backward_rows(Q, K, V, dY, rows, p.scale, p.sparse_mode, p.pre_tokens,
                                   p.next_tokens)
-        dk, dv = oracle.backward_keys(Q, K, V, dY, r0, r0 + width, p.scale, p.sparse_mode,
-                                      p.pre_tokens, p.next_tokens)
+        # dk / dv of key/value head n // G sum over the query heads of its group
+        dk, dv = 0, 0
+        for nq in range((n // G) * G, (n // G + 1) * G):
+            a_, b_ = oracle.backward_keys(p.q[s0:s0 + L, nq], K, V, p.dy[s0:s0 + L, nq], r0,
+                                          r0 + width, p.scale, p.sparse_mode, p.pre_tokens,
+                                          p.next_tokens)
+            dk, dv = dk + a_, dv + b_
         t = slice(s0 + r0, s0 + r0 + width)
         errs["out"].append((g["out"][t, n], O))
         errs["dq"].append((g["dq"][t, n], dq))
-        errs["dk"].append((g["dk"][t, n], dk))
-        errs["dv"].append((g["dv"][t, n], dv))
+        errs["dk"].append((g["dk"][t, n // G], dk))
+        errs["dv"].append((g["dv"][t, n // G], dv))
         smax_g.append(g["smax"][t, n])
         ssum_g.append(g["ssum"][t, n])
         smax_o.append(m)
@@ -268,7 +275,8 @@ def invariants_check(p, g):
     """sum_j dV_j = sum_i dY_i and sum_j dK_j = 0 per (sequence, head)."""
     for s0, L in oracle.sequences(p.cu_seqlens_q):
         dv_sum = g["dv"][s0:s0 + L].double().sum(0)
-        dy_sum = p.dy[s0:s0 + L].double().sum(0)
+        nkv = dv_sum.shape[0]
+        dy_sum = p.dy[s0:s0 + L].double().sum(0).view(nkv, -1, dv_sum.shape[1]).sum(1)
         dk_sum = g["dk"][s0:s0 + L].double().sum(0)
         scale_dv = float(g["dv"][s0:s0 + L].double().abs().sum(0).max())
         scale_dk = float(g["dk"][s0:s0 + L].double().abs().sum(0).max())
@@ -285,6 +293,11 @@ LARGE = [
      [(0, 0, 0, 64), (0, 5, 2000, 96), (0, 11, 9000, 64), (0, 15, 10**9, 64)]),
     ("varlen_swa_bf16_n32_d128_4seq_16kto32k_pre4096_next512",
      [(0, 0, 0, 64), (1, 13, 4500, 64), (2, 31, 20000, 64), (3, 20, 10**9, 64)]),
+    # causal: keys near the end (few rows attend them, so the oracle's
+    # key-side check stays cheap); the row-side check covers each sample too
+    ("causal_bf16_b1_n16_s16384_d128", [(0, 0, 16000, 64), (0, 9, 15000, 32), (0, 15, 10**9, 32)]),
+    ("gqa_swa_bf16_b1_n16kv4_s16384_d128_pre2048_next0",
+     [(0, 0, 0, 64), (0, 6, 5000, 64), (0, 15, 10**9, 64)]),
 ]
 
 

@@ -48,11 +48,13 @@ class Workload:
     len_lo: int = 0
     len_hi: int = 0
     seed: int = 42
+    num_kv_heads: int = 0   # 0: as many key/value heads as query heads
     note: str = field(default="", compare=False)
 
 
-# Five workloads shaped like the pages' cases; the fourth is the headline
-# sliding-window case (S = 16K, window of 2048 past tokens).
+# Five workloads shaped like the pages' cases (the fourth is the headline
+# sliding-window case: S = 16K, window of 2048 past tokens), then two that
+# measure the other masks and grouped heads at the headline's shape.
 WORKLOADS = {
     w.name: w
     for w in [
@@ -67,6 +69,13 @@ WORKLOADS = {
         Workload("varlen_swa_bf16_n32_d128_4seq_16kto32k_pre4096_next512", torch.bfloat16,
                  32, 128, 4, 1.0 / math.sqrt(128), pre_tokens=4096, next_tokens=512, std=0.5,
                  nseq=4, len_lo=16384, len_hi=32768),
+        # the 16K shape under the other masks and head layouts the library
+        # takes: causal (sparse_mode 2) and 4:1 grouped key/value heads
+        Workload("causal_bf16_b1_n16_s16384_d128", torch.bfloat16, 16, 128, 2,
+                 1.0 / math.sqrt(128), batch=1, seqlen=16384),
+        Workload("gqa_swa_bf16_b1_n16kv4_s16384_d128_pre2048_next0", torch.bfloat16, 16, 128, 4,
+                 1.0 / math.sqrt(128), pre_tokens=2048, next_tokens=0, batch=1, seqlen=16384,
+                 num_kv_heads=4),
     ]
 }
 
@@ -122,18 +131,18 @@ def make_problem(w: Workload | str, seed: int | None = None) -> Problem:
     if isinstance(w, str):
         w = WORKLOADS[w]
     g = torch.Generator("cpu").manual_seed(w.seed if seed is None else seed)
+    heads = [w.num_heads, w.num_kv_heads or w.num_heads, w.num_kv_heads or w.num_heads,
+             w.num_heads]  # q, k, v, dy
     if w.nseq:
         lengths = torch.randint(w.len_lo, w.len_hi + 1, (w.nseq,), generator=g).tolist()
         T = sum(lengths)
-        shape = (T, w.num_heads, w.head_dim)
-        tensors = [_randn(g, shape, w.std, w.dtype) for _ in range(4)]
+        tensors = [_randn(g, (T, n, w.head_dim), w.std, w.dtype) for n in heads]
     else:
         lengths = [w.seqlen] * w.batch
-        shape = (w.batch, w.num_heads, w.seqlen, w.head_dim)
         tensors = [
-            _randn(g, shape, w.std, w.dtype).permute(0, 2, 1, 3).reshape(
-                w.batch * w.seqlen, w.num_heads, w.head_dim).contiguous()
-            for _ in range(4)
+            _randn(g, (w.batch, n, w.seqlen, w.head_dim), w.std, w.dtype).permute(
+                0, 2, 1, 3).reshape(w.batch * w.seqlen, n, w.head_dim).contiguous()
+            for n in heads
         ]
     cu = cumulative(lengths)
     q, k, v, dy = tensors
