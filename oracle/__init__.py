@@ -19,5 +19,7 @@ from .attention import (  # noqa: F401
     forward_rows,
     backward_rows,
     backward_keys,
+    drop_mask_bits,
+    unpack_drop_mask,
 )
 from .tiles import enumerate_tiles, count_pairs  # noqa: F401

@@ -35,6 +35,19 @@ What is computed, and where the pages define it:
   Nq / Nkv = G a whole number; query head n reads key/value head n // G
   (floor division), and the gradients of a key/value head sum over the G
   query heads that read it.  G = 1 is the ordinary multi-head case.
+* Dropout with a given mask (API doc, 计算公式 and dropMaskOptional /
+  keepProbOptional; explainer 2.2, 6.3): attention_out = Dropout(P, keep_prob) V,
+  where the mask keeps an element where its bit is 1 (keep_prob is the
+  fraction of ones) and a kept element is scaled by 1 / keep_prob (the usual
+  inverted dropout; the pages print no scaling).  The statistics are those
+  of the undropped softmax.  The mask is uint8 holding 8 one-bit booleans per
+  byte, (sum_b sum_n Sq*Skv)/8 bytes: bit e of the whole array is byte e // 8,
+  bit e % 8 (least significant first), and e runs over batches, then heads,
+  then the Sq x Skv matrix of that (batch, head) row by row.  The backward
+  applies the same mask: dV = (P * Z / kp)^T dY, dP = (dY V^T) * Z / kp,
+  dS = P * (dP - Dv) with Dv = rowsum(dY * O).  The byte order, bit order and
+  the batch-before-head order are readings: the pages give only the size
+  formula.
 * Varlen TND packing (API doc, "算子功能" and inputLayout; explainer 4.2, 6.4):
   tokens of each batch are packed back to back; cumulative ends are inclusive,
   one per batch; trailing zeros mark batches that do not participate.
@@ -140,14 +153,22 @@ def _softmax_stats(S):
     return m, E, l
 
 
-def _seq_head_forward(Q, K, V, scale, sparse_mode, pre, nxt, rows, chunked):
+def _dropped(P, Z, rows, c0, c1, keep_prob):
+    """P * Z / keep_prob over rows x columns [c0, c1) (Z = None: no dropout)."""
+    if Z is None:
+        return P
+    return torch.where(Z[rows][:, c0:c1], P / keep_prob, torch.zeros((), dtype=F64))
+
+
+def _seq_head_forward(Q, K, V, scale, sparse_mode, pre, nxt, rows, chunked, Z=None,
+                      keep_prob=1.0):
     r0, r1 = int(rows[0]), int(rows[-1]) + 1
     c0, c1 = _col_window(r0, r1, Q.shape[0], K.shape[0], sparse_mode, pre, nxt, chunked)
     S, _ = _scores(Q, K, rows, c0, c1, scale, sparse_mode, pre, nxt)
     m, E, l = _softmax_stats(S)
     P = torch.where(l[:, None] > 0, E / torch.where(l > 0, l, 1.0)[:, None],
                     torch.zeros((), dtype=F64))
-    O = P @ V[c0:c1]
+    O = _dropped(P, Z, rows, c0, c1, keep_prob) @ V[c0:c1]
     return O, m, l
 
 
@@ -163,6 +184,29 @@ def _as64(x):
     return x.detach().to("cpu").to(F64)
 
 
+def drop_mask_bits(cu_seqlens_q, cu_seqlens_kv, num_heads):
+    """Number of mask bits: sum over participating batches b and heads n of Sq*Skv."""
+    return sum(num_heads * sq * skv for (_, sq), (_, skv) in
+               zip(sequences(cu_seqlens_q), sequences(cu_seqlens_kv)))
+
+
+def unpack_drop_mask(drop_mask, cu_seqlens_q, cu_seqlens_kv, num_heads):
+    """{(b, n): bool [Sq, Skv]} from the packed mask (True = keep)."""
+    import numpy as np
+    raw = np.asarray(torch.as_tensor(drop_mask, dtype=torch.uint8).cpu().numpy(), dtype=np.uint8)
+    nbits = drop_mask_bits(cu_seqlens_q, cu_seqlens_kv, num_heads)
+    if raw.size * 8 < nbits:
+        raise ValueError(f"drop mask has {raw.size} bytes, needs {(nbits + 7) // 8}")
+    bits = np.unpackbits(raw, bitorder="little")
+    out, e = {}, 0
+    for b, ((_, sq), (_, skv)) in enumerate(zip(sequences(cu_seqlens_q),
+                                                sequences(cu_seqlens_kv))):
+        for n in range(num_heads):
+            out[(b, n)] = torch.from_numpy(bits[e:e + sq * skv].reshape(sq, skv).astype(bool))
+            e += sq * skv
+    return out
+
+
 def group_size(q, k):
     """Query heads per key/value head (explainer 6.2: Nq / Nkv a whole number)."""
     nq, nkv = q.shape[1], k.shape[1]
@@ -172,27 +216,33 @@ def group_size(q, k):
 
 
 def forward(q, k, v, cu_seqlens_q, cu_seqlens_kv, scale, pre_tokens=INT_MAX,
-            next_tokens=INT_MAX, sparse_mode=0, chunk=None, heads=None):
+            next_tokens=INT_MAX, sparse_mode=0, chunk=None, heads=None, drop_mask=None,
+            keep_prob=1.0):
     """Attention forward over a TND batch.
 
     Returns (out [Tq, N, D], softmax_max [Tq, N], softmax_sum [Tq, N]) in fp64.
     ``chunk`` (rows per block) only changes evaluation order, not the result.
+    ``drop_mask`` (packed uint8, see the module docstring) applies dropout with
+    ``keep_prob``.
     """
     q, k, v = _as64(q), _as64(k), _as64(v)
     Tq, N, D = q.shape
     G = group_size(q, k)
+    Zs = None if drop_mask is None else unpack_drop_mask(drop_mask, cu_seqlens_q,
+                                                         cu_seqlens_kv, N)
     out = torch.zeros(Tq, N, v.shape[2], dtype=F64)
     smax = torch.full((Tq, N), -math.inf, dtype=F64)
     ssum = torch.zeros((Tq, N), dtype=F64)
     sq_list, skv_list = sequences(cu_seqlens_q), sequences(cu_seqlens_kv)
     if len(sq_list) != len(skv_list):
         raise ValueError("query and key/value batches disagree")
-    for (q0, sq), (k0, skv) in zip(sq_list, skv_list):
+    for b, ((q0, sq), (k0, skv)) in enumerate(zip(sq_list, skv_list)):
         for n in (range(N) if heads is None else heads):
             Q, K, V = q[q0:q0 + sq, n], k[k0:k0 + skv, n // G], v[k0:k0 + skv, n // G]
+            Z = None if Zs is None else Zs[(b, n)]
             for rows in _row_chunks(sq, chunk):
                 O, m, l = _seq_head_forward(Q, K, V, scale, sparse_mode, pre_tokens,
-                                            next_tokens, rows, chunk is not None)
+                                            next_tokens, rows, chunk is not None, Z, keep_prob)
                 out[q0 + rows, n] = O
                 smax[q0 + rows, n] = m
                 ssum[q0 + rows, n] = l
@@ -211,7 +261,8 @@ def _recompute_p(Q, K, rows, c0, c1, scale, sparse_mode, pre, nxt, m_rows, l_row
 
 
 def backward(q, k, v, dy, out, softmax_max, softmax_sum, cu_seqlens_q, cu_seqlens_kv, scale,
-             pre_tokens=INT_MAX, next_tokens=INT_MAX, sparse_mode=0, chunk=None, heads=None):
+             pre_tokens=INT_MAX, next_tokens=INT_MAX, sparse_mode=0, chunk=None, heads=None,
+             drop_mask=None, keep_prob=1.0):
     """Attention backward; uses the caller's out and statistics verbatim.
 
     ``softmax_max``/``softmax_sum`` may be [T, N] or [T, N, 8] (column 0 is
@@ -224,22 +275,26 @@ def backward(q, k, v, dy, out, softmax_max, softmax_sum, cu_seqlens_q, cu_seqlen
         sm, ss = sm[..., 0], ss[..., 0]
     Tq, N, D = q.shape
     G = group_size(q, k)
+    Zs = None if drop_mask is None else unpack_drop_mask(drop_mask, cu_seqlens_q,
+                                                         cu_seqlens_kv, N)
     dq = torch.zeros_like(q)
     dk = torch.zeros_like(k)
     dv = torch.zeros(v.shape, dtype=F64)
-    for (q0, sq), (k0, skv) in zip(sequences(cu_seqlens_q), sequences(cu_seqlens_kv)):
+    for b, ((q0, sq), (k0, skv)) in enumerate(zip(sequences(cu_seqlens_q),
+                                                  sequences(cu_seqlens_kv))):
         for n in (range(N) if heads is None else heads):
             Q, K, V = q[q0:q0 + sq, n], k[k0:k0 + skv, n // G], v[k0:k0 + skv, n // G]
             dY, O = dy[q0:q0 + sq, n], out[q0:q0 + sq, n]
+            Z = None if Zs is None else Zs[(b, n)]
             for rows in _row_chunks(sq, chunk):
                 c0, c1 = _col_window(int(rows[0]), int(rows[-1]) + 1, sq, skv, sparse_mode,
                                      pre_tokens, next_tokens, chunk is not None)
                 P = _recompute_p(Q, K, rows, c0, c1, scale, sparse_mode, pre_tokens,
                                  next_tokens, sm[q0 + rows, n], ss[q0 + rows, n])
                 Dv = (dY[rows] * O[rows]).sum(dim=1)
-                dP = dY[rows] @ V[c0:c1].T
+                dP = _dropped(dY[rows] @ V[c0:c1].T, Z, rows, c0, c1, keep_prob)
                 dS = P * (dP - Dv[:, None])
-                dv[k0 + c0:k0 + c1, n // G] += P.T @ dY[rows]
+                dv[k0 + c0:k0 + c1, n // G] += _dropped(P, Z, rows, c0, c1, keep_prob).T @ dY[rows]
                 dq[q0 + rows, n] = scale * (dS @ K[c0:c1])
                 dk[k0 + c0:k0 + c1, n // G] += scale * (dS.T @ Q[rows])
     return dq, dk, dv

@@ -108,8 +108,9 @@ def test_gqa_head_count_must_divide():
 MUTATIONS = {
     "kv_head_modulo": ("k[k0:k0 + skv, n // G], v[k0:k0 + skv, n // G]",
                        "k[k0:k0 + skv, n % k.shape[1]], v[k0:k0 + skv, n % k.shape[1]]"),
-    "dv_not_summed": ("dv[k0 + c0:k0 + c1, n // G] += P.T @ dY[rows]",
-                      "dv[k0 + c0:k0 + c1, n // G] = P.T @ dY[rows]"),
+    "dv_not_summed": (
+        "dv[k0 + c0:k0 + c1, n // G] += _dropped(P, Z, rows, c0, c1, keep_prob).T @ dY[rows]",
+        "dv[k0 + c0:k0 + c1, n // G] = _dropped(P, Z, rows, c0, c1, keep_prob).T @ dY[rows]"),
 }
 
 

@@ -340,8 +340,10 @@ def test_sampled_restrictions_equal_full(mode, pre, nxt):
 MUTATIONS = {
     "dk_without_scale": ("dk[k0 + c0:k0 + c1, n // G] += scale * (dS.T @ Q[rows])",
                          "dk[k0 + c0:k0 + c1, n // G] += (dS.T @ Q[rows])"),
-    "dv_transposed_operand": ("dv[k0 + c0:k0 + c1, n // G] += P.T @ dY[rows]",
-                              "dv[k0 + c0:k0 + c1, n // G] += (P.T @ dY[rows]).flip(0)"),
+    "dv_transposed_operand": (
+        "dv[k0 + c0:k0 + c1, n // G] += _dropped(P, Z, rows, c0, c1, keep_prob).T @ dY[rows]",
+        "dv[k0 + c0:k0 + c1, n // G] += (_dropped(P, Z, rows, c0, c1, keep_prob).T @ dY[rows])"
+        ".flip(0)"),
     "ds_sign": ("dS = P * (dP - Dv[:, None])", "dS = P * (Dv[:, None] - dP)"),
     "band_mirrored": ("return (d >= -int(pre_tokens)) & (d <= int(next_tokens))",
                       "return (d >= -int(next_tokens)) & (d <= int(pre_tokens))"),
