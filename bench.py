@@ -179,8 +179,9 @@ def main():
                    p.sparse_mode)
 
     def step():
-        swa.swa_forward_gqa(q, k, v, *args_common, out, smax, ssum, ws_f)
-        swa.swa_backward_gqa(q, k, v, dy, out, smax, ssum, *args_common, dq, dk, dv, ws_b)
+        swa.swa_forward_ex(q, k, v, *args_common, None, 1.0, out, smax, ssum, ws_f)
+        swa.swa_backward_ex(q, k, v, dy, out, smax, ssum, *args_common, None, 1.0, dq, dk, dv,
+                            ws_b)
 
     for _ in range(args.warmup):
         step()

@@ -34,7 +34,7 @@
  * Layouts (all row-major, contiguous, device memory unless stated):
  *   q, out, dy, dq     [t_q,  num_heads, head_dim]   element type `dtype`
  *   k, v, dk, dv       [t_kv, num_kv_heads, head_dim] element type `dtype`
- *                      (num_kv_heads = num_heads except in the *_gqa calls)
+ *                      (num_kv_heads = num_heads except in the *_ex calls)
  *   softmax_max/_sum   [t_q,  num_heads, 8] float32; all 8 entries of a row
  *                      hold the same value (TND statistics layout of the
  *                      explainer, section 4.2; column 0 is the one read).
@@ -143,30 +143,50 @@ swa_status swa_backward(const void* q, const void* k, const void* v, const void*
                         int64_t next_tokens, int64_t sparse_mode, void* dq, void* dk, void* dv,
                         void* workspace, size_t workspace_bytes, void* stream);
 
-/* Grouped key/value heads (GQA, explainer section 6.2): q, out, dy, dq and
- * the statistics have num_heads heads, k, v, dk and dv have num_kv_heads,
- * and num_heads must be a whole multiple G of num_kv_heads (else
+/* Extended calls: grouped key/value heads and dropout with a given mask.
+ * swa_forward / swa_backward are these with num_kv_heads = num_heads and
+ * drop_mask = NULL.  Every other argument, the workspace sizes included (they
+ * take num_heads = the query head count), is as there.
+ *
+ * Grouped heads (GQA, explainer section 6.2): q, out, dy, dq and the
+ * statistics have num_heads heads, k, v, dk and dv have num_kv_heads, and
+ * num_heads must be a whole multiple G of num_kv_heads (else
  * SWA_ERR_INVALID).  Query head n reads key/value head n / G (integer
  * division); dk and dv of a key/value head sum the contributions of its G
  * query heads (inside one workgroup, so the bf16 backward stays
- * deterministic).  Every other argument, the workspace sizes included (they
- * take num_heads = the query head count), is as in swa_forward /
- * swa_backward, which are these calls with num_kv_heads = num_heads. */
-swa_status swa_forward_gqa(const void* q, const void* k, const void* v,
+ * deterministic).
+ *
+ * Dropout (VarLenScore API doc, 计算公式: attention_out =
+ * Dropout(softmax(...), keep_prob) * value; dropMaskOptional,
+ * keepProbOptional; explainer section 6.3): drop_mask is DEVICE memory,
+ * 4-byte aligned, holding one keep bit per (batch, query head, query row,
+ * key): bit e is bit e % 8 (least significant first) of byte e / 8, and e
+ * runs over the participating batches, then the heads, then the Sq x Skv
+ * matrix of that batch and head row by row, so there are
+ * sum_b num_heads * Sq_b * Skv_b bits; drop_mask_bytes must cover them
+ * rounded up to whole 32-bit words (else SWA_ERR_INVALID).  A kept
+ * probability is scaled by 1 / keep_prob (keep_prob in (0, 1], the fraction
+ * of ones; else SWA_ERR_INVALID), a dropped one is zero; softmax_max /
+ * softmax_sum are those of the undropped softmax.  The backward takes the
+ * same mask and keep_prob.  drop_mask = NULL: no dropout (keep_prob and
+ * drop_mask_bytes are ignored). */
+swa_status swa_forward_ex(const void* q, const void* k, const void* v,
+                          const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,
+                          int64_t num_seqs, int64_t t_q, int64_t t_kv, int64_t num_heads,
+                          int64_t num_kv_heads, int64_t head_dim, int32_t dtype, double scale,
+                          int64_t pre_tokens, int64_t next_tokens, int64_t sparse_mode,
+                          const void* drop_mask, size_t drop_mask_bytes, double keep_prob,
+                          void* out, float* softmax_max, float* softmax_sum, void* workspace,
+                          size_t workspace_bytes, void* stream);
+swa_status swa_backward_ex(const void* q, const void* k, const void* v, const void* dy,
+                           const void* out, const float* softmax_max, const float* softmax_sum,
                            const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,
                            int64_t num_seqs, int64_t t_q, int64_t t_kv, int64_t num_heads,
                            int64_t num_kv_heads, int64_t head_dim, int32_t dtype, double scale,
                            int64_t pre_tokens, int64_t next_tokens, int64_t sparse_mode,
-                           void* out, float* softmax_max, float* softmax_sum, void* workspace,
+                           const void* drop_mask, size_t drop_mask_bytes, double keep_prob,
+                           void* dq, void* dk, void* dv, void* workspace,
                            size_t workspace_bytes, void* stream);
-swa_status swa_backward_gqa(const void* q, const void* k, const void* v, const void* dy,
-                            const void* out, const float* softmax_max,
-                            const float* softmax_sum, const int64_t* cu_seqlens_q,
-                            const int64_t* cu_seqlens_kv, int64_t num_seqs, int64_t t_q,
-                            int64_t t_kv, int64_t num_heads, int64_t num_kv_heads,
-                            int64_t head_dim, int32_t dtype, double scale, int64_t pre_tokens,
-                            int64_t next_tokens, int64_t sparse_mode, void* dq, void* dk,
-                            void* dv, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Message for the last non-OK status returned on this thread ("" if none).
  * The pointer stays valid until the next call on the same thread. */

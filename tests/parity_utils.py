@@ -35,27 +35,31 @@ def require_gpu():
     return torch.device("cuda:0")
 
 
-def run_hip(p, device, with_backward=True):
-    """Forward (+ backward) of problem p through the C ABI; host copies."""
+def run_hip(p, device, with_backward=True, drop_mask=None, keep_prob=1.0):
+    """Forward (+ backward) of problem p through the C ABI; host copies.
+    ``drop_mask`` (host uint8, packed keep bits) applies dropout."""
     q, k, v, dy = (x.to(device) for x in (p.q, p.k, p.v, p.dy))
+    mask = None if drop_mask is None else drop_mask.to(device)
     out, smax, ssum = swa.forward(q, k, v, p.cu_seqlens_q, p.cu_seqlens_kv, p.scale,
-                                  p.pre_tokens, p.next_tokens, p.sparse_mode)
+                                  p.pre_tokens, p.next_tokens, p.sparse_mode,
+                                  drop_mask=mask, keep_prob=keep_prob)
     res = {"out": out, "smax": smax, "ssum": ssum}
     if with_backward:
         dq, dk, dv = swa.backward(q, k, v, dy, out, smax, ssum, p.cu_seqlens_q,
                                   p.cu_seqlens_kv, p.scale, p.pre_tokens, p.next_tokens,
-                                  p.sparse_mode)
+                                  p.sparse_mode, drop_mask=mask, keep_prob=keep_prob)
         res.update(dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
     return {k_: v_.cpu() for k_, v_ in res.items()}
 
 
-def run_oracle(p, chunk=256):
+def run_oracle(p, chunk=256, drop_mask=None, keep_prob=1.0):
+    kw = dict(drop_mask=drop_mask, keep_prob=keep_prob)
     out, sm, ss = oracle.forward(p.q, p.k, p.v, p.cu_seqlens_q, p.cu_seqlens_kv, p.scale,
-                                 p.pre_tokens, p.next_tokens, p.sparse_mode, chunk=chunk)
+                                 p.pre_tokens, p.next_tokens, p.sparse_mode, chunk=chunk, **kw)
     dq, dk, dv = oracle.backward(p.q, p.k, p.v, p.dy, out, sm, ss, p.cu_seqlens_q,
                                  p.cu_seqlens_kv, p.scale, p.pre_tokens, p.next_tokens,
-                                 p.sparse_mode, chunk=chunk)
+                                 p.sparse_mode, chunk=chunk, **kw)
     return {"out": out, "smax": sm, "ssum": ss, "dq": dq, "dk": dk, "dv": dv}
 
 

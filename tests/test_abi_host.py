@@ -87,6 +87,39 @@ def test_forward_validation_statuses(kw, status, needle):
     assert needle in swa.swa_last_error()
 
 
+def raw_forward_ex(**kw):
+    """Call swa_forward_ex through ctypes with fake (never dereferenced) pointers;
+    only argument combinations that fail validation are used."""
+    lib = swa.load_library()
+    a = dict(q=1, k=1, v=1, cu_q=[16, 30], cu_kv=[16, 30], t_q=30, t_kv=30, n=4, nkv=2, d=64,
+             dtype=1, scale=0.125, pre=INT_MAX, nxt=INT_MAX, mode=0, mask=256,
+             mask_bytes=1 << 20, keep=0.9, out=1, smax=1, ssum=1, ws=1, ws_bytes=1 << 30)
+    a.update(kw)
+    cq = (ctypes.c_int64 * len(a["cu_q"]))(*a["cu_q"])
+    ck = (ctypes.c_int64 * len(a["cu_kv"]))(*a["cu_kv"])
+    return lib.swa_forward_ex(a["q"], a["k"], a["v"], cq, ck, len(a["cu_q"]), a["t_q"],
+                              a["t_kv"], a["n"], a["nkv"], a["d"], a["dtype"], a["scale"],
+                              a["pre"], a["nxt"], a["mode"], a["mask"], a["mask_bytes"],
+                              a["keep"], a["out"], a["smax"], a["ssum"], a["ws"], a["ws_bytes"],
+                              None)
+
+
+# mask bits: 4 heads x (16*16 + 14*14) = 1808 bits -> 57 words = 228 bytes
+@pytest.mark.parametrize("kw,needle", [
+    (dict(keep=0.0), "keep_prob"),
+    (dict(keep=1.5), "keep_prob"),
+    (dict(keep=float("nan")), "keep_prob"),
+    (dict(mask=258), "4-byte aligned"),
+    (dict(mask_bytes=227), "drop_mask has 227 bytes, needs 228"),
+    (dict(nkv=3), "multiple of num_kv_heads"),
+    (dict(nkv=0), "multiple of num_kv_heads"),
+    (dict(nkv=8), "multiple of num_kv_heads"),
+])
+def test_extended_call_validation(kw, needle):
+    assert raw_forward_ex(**kw) == swa.SWA_ERR_INVALID
+    assert needle in swa.swa_last_error()
+
+
 def test_mode0_accepts_unequal_lengths_and_trailing_batches():
     # only the schedule is built (host); the dump proves validation passed
     rows, _, _ = swa.swa_debug_tile_schedule([5, 9, 0, 0], [7, 8, 0, 0], 9, 8, 64, 1,

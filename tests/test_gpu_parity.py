@@ -110,6 +110,47 @@ def test_custom_cases_full_parity(dev, case):
         assert g["dk"][endk:].abs().max() == 0 and g["dv"][endk:].abs().max() == 0
 
 
+DROPOUT = {
+    "bf16_d128_band_dropout": (dict(lengths_q=[1, 130, 257, 700], num_heads=3, head_dim=128,
+                                    sparse_mode=4, pre_tokens=64, next_tokens=5), 0.8),
+    "bf16_d64_dense_unequal_kv_dropout": (dict(lengths_q=[77, 190], lengths_kv=[50, 260],
+                                               num_heads=2, head_dim=64), 0.6),
+    "bf16_d128_gqa_causal_dropout": (dict(lengths_q=[257, 130], lengths_kv=[300, 100],
+                                          num_heads=4, num_kv_heads=2, head_dim=128,
+                                          sparse_mode=3, std=0.5), 0.9),
+    "fp32_d128_band_dropout": (dict(lengths_q=[300, 45], num_heads=2, head_dim=128,
+                                    sparse_mode=4, pre_tokens=90, next_tokens=20,
+                                    dtype=torch.float32), 0.7),
+    "fp32_d64_dense_dropout": (dict(lengths_q=[150, 66], lengths_kv=[90, 130], num_heads=2,
+                                    head_dim=64, dtype=torch.float32), 0.5),
+}
+
+
+@pytest.mark.parametrize("case", sorted(DROPOUT))
+def test_dropout_cases_full_parity(dev, case):
+    """Dropout with a seeded caller mask (packed keep bits) against the oracle."""
+    kw, keep_prob = DROPOUT[case]
+    p = workloads.make_custom(name=case, **kw)
+    mask = workloads.make_drop_mask(p, keep_prob)
+    note(f"[parity] {case} keep_prob={keep_prob} mask bytes={mask.numel()}")
+    g = run_hip(p, dev, drop_mask=mask, keep_prob=keep_prob)
+    o = run_oracle(p, chunk=None, drop_mask=mask, keep_prob=keep_prob)
+    compare_full(p, g, o)
+
+
+def test_dropout_keep_all_equals_no_dropout(dev):
+    """An all-ones mask with keep_prob 1 reproduces the call without dropout
+    bit for bit (the dropout kernels apply the same products)."""
+    p = workloads.make_custom([300, 77], num_heads=2, head_dim=128, sparse_mode=4,
+                              pre_tokens=100, next_tokens=0)
+    mask = workloads.make_drop_mask(p, 1.0)
+    a = run_hip(p, dev)
+    b = run_hip(p, dev, drop_mask=mask, keep_prob=1.0)
+    for n in ("out", "smax", "ssum", "dk", "dv"):
+        assert torch.equal(a[n], b[n]), n
+    assert (a["dq"].float() - b["dq"].float()).abs().max() <= 1e-2
+
+
 # ------------------------------------------------------------ exact cases
 
 def test_query_zero_counts_are_exact(dev):

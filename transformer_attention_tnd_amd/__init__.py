@@ -7,8 +7,9 @@ Every step of the computation runs in the HIP kernels of ``libswa.so``;
 there is no fallback: if the library is missing the calls raise.
 
 ``forward`` and ``backward`` are conveniences that allocate the outputs and
-the workspace with torch and call ``swa_forward_gqa`` / ``swa_backward_gqa``
-(grouped key/value heads when k has fewer heads than q).
+the workspace with torch and call ``swa_forward_ex`` / ``swa_backward_ex``
+(grouped key/value heads when k has fewer heads than q; dropout when a mask
+is given).
 """
 from __future__ import annotations
 
@@ -18,7 +19,7 @@ import os
 __all__ = [
     "INT_MAX", "SwaError", "load_library", "library_path",
     "swa_forward_workspace_size", "swa_backward_workspace_size",
-    "swa_forward", "swa_backward", "swa_forward_gqa", "swa_backward_gqa",
+    "swa_forward", "swa_backward", "swa_forward_ex", "swa_backward_ex",
     "swa_last_error", "swa_debug_tile_schedule",
     "swa_profile_enable", "swa_profile_read",
     "forward", "backward", "DTYPE_FP32", "DTYPE_BF16", "DTYPE_FP16",
@@ -48,12 +49,13 @@ _SIGNATURES = {
     "swa_backward": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64p, _i64p, _i64, _i64, _i64, _i64,
                      _i64, _i32, ctypes.c_double, _i64, _i64, _i64, _vp, _vp, _vp, _vp,
                      ctypes.c_size_t, _vp],
-    "swa_forward_gqa": [_vp, _vp, _vp, _i64p, _i64p, _i64, _i64, _i64, _i64, _i64, _i64, _i32,
-                        ctypes.c_double, _i64, _i64, _i64, _vp, _vp, _vp, _vp, ctypes.c_size_t,
+    "swa_forward_ex": [_vp, _vp, _vp, _i64p, _i64p, _i64, _i64, _i64, _i64, _i64, _i64, _i32,
+                       ctypes.c_double, _i64, _i64, _i64, _vp, ctypes.c_size_t, ctypes.c_double,
+                       _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp],
+    "swa_backward_ex": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64p, _i64p, _i64, _i64, _i64,
+                        _i64, _i64, _i64, _i32, ctypes.c_double, _i64, _i64, _i64, _vp,
+                        ctypes.c_size_t, ctypes.c_double, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                         _vp],
-    "swa_backward_gqa": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64p, _i64p, _i64, _i64, _i64,
-                         _i64, _i64, _i64, _i32, ctypes.c_double, _i64, _i64, _i64, _vp, _vp,
-                         _vp, _vp, ctypes.c_size_t, _vp],
     "swa_last_error": [],
     "swa_debug_tile_schedule": [_i64p, _i64p, _i64, _i64, _i64, _i64, _i32, _i64, _i64, _i64,
                                 _i32, _i32p, _i64, _i64p, _i32p, _i32p],
@@ -211,37 +213,52 @@ def swa_backward(q, k, v, dy, out, softmax_max, softmax_sum, cu_seqlens_q, cu_se
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q, stream)))
 
 
-def swa_forward_gqa(q, k, v, cu_seqlens_q, cu_seqlens_kv, scale, pre_tokens, next_tokens,
-                    sparse_mode, out, softmax_max, softmax_sum, workspace, stream=None):
-    """Marshal to swa_forward_gqa: k and v may have fewer heads than q (a divisor)."""
+def _mask_args(drop_mask, keep_prob, device):
+    import torch
+    if drop_mask is None:
+        return None, 0, 1.0
+    if drop_mask.dtype != torch.uint8 or not drop_mask.is_contiguous() or \
+            drop_mask.device != device:
+        raise ValueError("drop_mask must be a contiguous uint8 tensor on the device of q")
+    return _ptr(drop_mask), drop_mask.numel(), float(keep_prob)
+
+
+def swa_forward_ex(q, k, v, cu_seqlens_q, cu_seqlens_kv, scale, pre_tokens, next_tokens,
+                   sparse_mode, drop_mask, keep_prob, out, softmax_max, softmax_sum, workspace,
+                   stream=None):
+    """Marshal to swa_forward_ex: k and v may have fewer heads than q (a
+    divisor); drop_mask (packed uint8 keep bits, or None) applies dropout."""
     _shape_checks(q, k, v, extra_q=(out,), grouped=True)
     _stats_check(q, softmax_max, softmax_sum)
     cq, nq = _cu_array(cu_seqlens_q)
     ck, nk = _cu_array(cu_seqlens_kv)
     if nq != nk:
         raise ValueError("cu_seqlens_q and cu_seqlens_kv must have the same length")
-    _check(load_library().swa_forward_gqa(
+    mp, mb, kp = _mask_args(drop_mask, keep_prob, q.device)
+    _check(load_library().swa_forward_ex(
         _ptr(q), _ptr(k), _ptr(v), cq, ck, nq, q.shape[0], k.shape[0], q.shape[1], k.shape[1],
         q.shape[2], _dtype_code(q), float(scale), int(pre_tokens), int(next_tokens),
-        int(sparse_mode), _ptr(out), _ptr(softmax_max), _ptr(softmax_sum), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _stream(q, stream)))
+        int(sparse_mode), mp, mb, kp, _ptr(out), _ptr(softmax_max), _ptr(softmax_sum),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q, stream)))
 
 
-def swa_backward_gqa(q, k, v, dy, out, softmax_max, softmax_sum, cu_seqlens_q, cu_seqlens_kv,
-                     scale, pre_tokens, next_tokens, sparse_mode, dq, dk, dv, workspace,
-                     stream=None):
-    """Marshal to swa_backward_gqa: k, v, dk, dv may have fewer heads than q."""
+def swa_backward_ex(q, k, v, dy, out, softmax_max, softmax_sum, cu_seqlens_q, cu_seqlens_kv,
+                    scale, pre_tokens, next_tokens, sparse_mode, drop_mask, keep_prob, dq, dk,
+                    dv, workspace, stream=None):
+    """Marshal to swa_backward_ex: k, v, dk, dv may have fewer heads than q;
+    drop_mask / keep_prob as in the forward call."""
     _shape_checks(q, k, v, extra_q=(dy, out, dq), extra_kv=(dk, dv), grouped=True)
     _stats_check(q, softmax_max, softmax_sum)
     cq, nq = _cu_array(cu_seqlens_q)
     ck, nk = _cu_array(cu_seqlens_kv)
     if nq != nk:
         raise ValueError("cu_seqlens_q and cu_seqlens_kv must have the same length")
-    _check(load_library().swa_backward_gqa(
+    mp, mb, kp = _mask_args(drop_mask, keep_prob, q.device)
+    _check(load_library().swa_backward_ex(
         _ptr(q), _ptr(k), _ptr(v), _ptr(dy), _ptr(out), _ptr(softmax_max), _ptr(softmax_sum),
         cq, ck, nq, q.shape[0], k.shape[0], q.shape[1], k.shape[1], q.shape[2], _dtype_code(q),
-        float(scale), int(pre_tokens), int(next_tokens), int(sparse_mode), _ptr(dq), _ptr(dk),
-        _ptr(dv), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        float(scale), int(pre_tokens), int(next_tokens), int(sparse_mode), mp, mb, kp, _ptr(dq),
+        _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(q, stream)))
 
 
@@ -283,9 +300,9 @@ def _workspace(nbytes, device):
 
 
 def forward(q, k, v, cu_seqlens_q, cu_seqlens_kv, scale, pre_tokens=INT_MAX,
-            next_tokens=INT_MAX, sparse_mode=0, workspace=None):
-    """Allocate (out, softmax_max, softmax_sum) and run swa_forward_gqa (k / v may
-    have fewer heads than q)."""
+            next_tokens=INT_MAX, sparse_mode=0, workspace=None, drop_mask=None, keep_prob=1.0):
+    """Allocate (out, softmax_max, softmax_sum) and run swa_forward_ex (k / v may
+    have fewer heads than q; drop_mask applies dropout)."""
     import torch
     out = torch.empty_like(q)
     smax = torch.empty(q.shape[0], q.shape[1], 8, dtype=torch.float32, device=q.device)
@@ -294,21 +311,23 @@ def forward(q, k, v, cu_seqlens_q, cu_seqlens_kv, scale, pre_tokens=INT_MAX,
         nbytes = swa_forward_workspace_size(len(cu_seqlens_q), q.shape[0], k.shape[0],
                                             q.shape[1], q.shape[2], _dtype_code(q))
         workspace = _workspace(nbytes, q.device)
-    swa_forward_gqa(q, k, v, cu_seqlens_q, cu_seqlens_kv, scale, pre_tokens, next_tokens,
-                    sparse_mode, out, smax, ssum, workspace)
+    swa_forward_ex(q, k, v, cu_seqlens_q, cu_seqlens_kv, scale, pre_tokens, next_tokens,
+                   sparse_mode, drop_mask, keep_prob, out, smax, ssum, workspace)
     return out, smax, ssum
 
 
 def backward(q, k, v, dy, out, softmax_max, softmax_sum, cu_seqlens_q, cu_seqlens_kv, scale,
-             pre_tokens=INT_MAX, next_tokens=INT_MAX, sparse_mode=0, workspace=None):
-    """Allocate (dq, dk, dv) and run swa_backward_gqa (k / v may have fewer heads
-    than q)."""
+             pre_tokens=INT_MAX, next_tokens=INT_MAX, sparse_mode=0, workspace=None,
+             drop_mask=None, keep_prob=1.0):
+    """Allocate (dq, dk, dv) and run swa_backward_ex (k / v may have fewer heads
+    than q; drop_mask / keep_prob as in the forward call)."""
     import torch
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     if workspace is None:
         nbytes = swa_backward_workspace_size(len(cu_seqlens_q), q.shape[0], k.shape[0],
                                              q.shape[1], q.shape[2], _dtype_code(q))
         workspace = _workspace(nbytes, q.device)
-    swa_backward_gqa(q, k, v, dy, out, softmax_max, softmax_sum, cu_seqlens_q, cu_seqlens_kv,
-                     scale, pre_tokens, next_tokens, sparse_mode, dq, dk, dv, workspace)
+    swa_backward_ex(q, k, v, dy, out, softmax_max, softmax_sum, cu_seqlens_q, cu_seqlens_kv,
+                    scale, pre_tokens, next_tokens, sparse_mode, drop_mask, keep_prob, dq, dk,
+                    dv, workspace)
     return dq, dk, dv

@@ -38,8 +38,6 @@ def common_flags():
         "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
         # no packed fp32 VALU instructions in device code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        # no NaN inputs are assumed: max/min need no NaN-quieting (infinities are kept)
-        "-fno-honor-nans",
         "-Wall", "-Wno-unused-function",
         "-I", os.path.join(ROOT, "include"),
     ]
@@ -47,7 +45,10 @@ def common_flags():
 
 def _compile(src, extra):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + common_flags() + extra + ["-c", os.path.join(CSRC, src), "-o", obj]
+    # kernels: no NaN inputs are assumed, so max/min need no NaN-quieting
+    # (infinities are kept); the host code validates arguments, NaN included
+    kern = ["-fno-honor-nans"] if src.endswith(".hip") else []
+    cmd = [hipcc()] + common_flags() + kern + extra + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)

@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256) void swa_bwd_pre_kernel(BwdPreArgs a) {
   }
 }
 
-template <typename T, int D, int BM>
+template <typename T, int D, int BM, bool kDrop>
 __global__ __launch_bounds__(256, 1) void swa_bwd_kernel(BwdArgs a) {
   using M = Mfma<T>;
   using op_t = typename M::op_t;
@@ -94,6 +94,8 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds[4 * QTB + (kKVlds ? 2 : 1) * KTB + STB];
   __shared__ __attribute__((aligned(16))) float lse_s[2][BM];
   __shared__ __attribute__((aligned(16))) float drow_s[2][BM];
+  // dropout keep bits of the tile: [slot][key word kw / 32 of the block][row]
+  __shared__ __attribute__((aligned(16))) uint32_t mask_s[kDrop ? 2 * 4 * BM : 1];
   char* const qbuf = lds;               // Q tiles [2]
   char* const ybuf = lds + 2 * QTB;     // dY tiles [2]
   char* const kblk = lds + 4 * QTB;     // K block (operand of S and of dQ)
@@ -118,8 +120,10 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kernel(BwdArgs a) {
   const T* dyg = nullptr;
   const float* lse_g = nullptr;
   const float* drow_g = nullptr;
+  int64_t drop_head = 0;  // first dropout-mask bit of (sequence, query head)
   auto set_head = [&](int hq) {
     head = hq;
+    drop_head = it.drop_base + (int64_t)hq * it.sq * it.skv;
     qg = static_cast<const T*>(a.q) + (int64_t)it.q_base * ld + hq * D;
     dyg = static_cast<const T*>(a.dy) + (int64_t)it.q_base * ld + hq * D;
     lse_g = a.lse2 + (int64_t)hq * a.t_q + it.q_base;
@@ -153,8 +157,11 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kernel(BwdArgs a) {
     dv[db] = floatx16{};
   }
 
-  // Q / dY tiles straight to LDS; lse2 / D rows through registers.
+  // Q / dY tiles straight to LDS; lse2 / D rows (and, with dropout, the keep
+  // bits: thread (row = tid % BM, word = tid / BM) takes keys 32 word ..
+  // 32 word + 31 of the block) through registers.
   float sreg = 0.f;
+  uint32_t mreg[2] = {0u, 0u}, msh = 0;
   auto load_qtile = [&](int tile, int b) {
     const int nvalid = it.sq - tile * BM;
     tile_load_lds<T, D, BM>(qg + (int64_t)tile * BM * ld, ld, nvalid, qbuf + b * QTB, tid);
@@ -166,12 +173,27 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kernel(BwdArgs a) {
       else
         sreg = i < it.sq ? drow_g[i] : 0.f;
     }
+    if constexpr (kDrop) {
+      if (tid < 4 * BM) {
+        const int row = tid & (BM - 1), i = tile * BM + row;
+        const int64_t bit = drop_head + (int64_t)i * it.skv + kb0 + 32 * (tid / BM);
+        const int64_t wd = bit >> 5;
+        msh = (uint32_t)(bit & 31);
+        mreg[0] = (i < it.sq && wd < a.drop.n_words) ? a.drop.words[wd] : 0u;
+        mreg[1] = (i < it.sq && wd + 1 < a.drop.n_words) ? a.drop.words[wd + 1] : 0u;
+      }
+    }
   };
   auto store_rows = [&](int b) {
     if (tid < BM)
       lse_s[b][tid] = sreg;
     else if (tid < 2 * BM)
       drow_s[b][tid - BM] = sreg;
+    if constexpr (kDrop) {
+      if (tid < 4 * BM)
+        mask_s[b * 4 * BM + (tid / BM) * BM + (tid & (BM - 1))] =
+            __builtin_amdgcn_alignbit(mreg[1], mreg[0], msh);
+    }
   };
 
   // Phase A for one query tile: P, dS, dV^T += dY^T P, dK^T += Q^T dS, dS -> LDS.
@@ -205,14 +227,26 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kernel(BwdArgs a) {
         const int rb = 32 * qb + 8 * g + 4 * h;
         const floatx4 l4 = *reinterpret_cast<const floatx4*>(&lse_s[b][rb]);
         const floatx4 d4 = *reinterpret_cast<const floatx4*>(&drow_s[b][rb]);
+        uint32_t m4[4] = {0u, 0u, 0u, 0u};  // keep words of rows rb .. rb + 3, this wave's keys
+        if constexpr (kDrop) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) m4[e] = mask_s[b * 4 * BM + w * BM + rb + e];
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g + e;
           float p = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -l4[e]));
           if constexpr (kMask)
             p = allowed(tile * BM + rb + e, kw, it.sq, it.skv, a.mode, it.band[0], it.band[1]) ? p : 0.f;
-          s[r] = p;
-          dp[r] = p * (dp[r] - d4[e]);
+          if constexpr (kDrop) {
+            // dV takes P Z / kp, dS = P (Z dP / kp - D)
+            const bool kept = (m4[e] >> c) & 1u;
+            dp[r] = p * ((kept ? dp[r] * a.drop.rkp : 0.f) - d4[e]);
+            s[r] = kept ? p * a.drop.rkp : 0.f;
+          } else {
+            s[r] = p;
+            dp[r] = p * (dp[r] - d4[e]);
+          }
         }
       }
       // dV^T += dY^T P ;  dK^T += Q^T dS   (contraction over the 32 query rows)
@@ -408,19 +442,22 @@ int launch_bwd_pre(const BwdPreArgs& a, int dtype, int head_dim, void* stream) {
                          : launch_pre_t<float, 64>(a, stream);
 }
 
-template <typename T, int D>
+template <typename T, int D, bool kDrop>
 static int launch_bwd_t(const BwdArgs& a, void* stream) {
   const int64_t nwg = (int64_t)a.n_items * a.num_kv_heads;  // one workgroup per key block and K/V head
   constexpr int BM = bwd_block_q(sizeof(T) == 2 ? 1 : 0, D);
-  hipLaunchKernelGGL((swa_bwd_kernel<T, D, BM>), dim3((unsigned)nwg), dim3(256), 0,
+  hipLaunchKernelGGL((swa_bwd_kernel<T, D, BM, kDrop>), dim3((unsigned)nwg), dim3(256), 0,
                      static_cast<hipStream_t>(stream), a);
   return (int)hipGetLastError();
 }
 
 int launch_backward(const BwdArgs& a, int dtype, int head_dim, void* stream) {
   if (dtype == 1) return launch_bwd_kv(a, head_dim, stream);  // swa_bwd_kv.hip
-  return head_dim == 128 ? launch_bwd_t<float, 128>(a, stream)
-                         : launch_bwd_t<float, 64>(a, stream);
+  if (a.drop.words)
+    return head_dim == 128 ? launch_bwd_t<float, 128, true>(a, stream)
+                           : launch_bwd_t<float, 64, true>(a, stream);
+  return head_dim == 128 ? launch_bwd_t<float, 128, false>(a, stream)
+                         : launch_bwd_t<float, 64, false>(a, stream);
 }
 
 int launch_dq_finalize(const FinalizeArgs& a, int dtype, void* stream) {

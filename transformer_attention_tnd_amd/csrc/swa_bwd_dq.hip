@@ -23,7 +23,7 @@
 
 namespace swa {
 
-template <int D>
+template <int D, bool kDrop>
 __global__ __launch_bounds__(256, 1) void swa_bwd_dq_kernel(BwdArgs a) {
   using M = Mfma<bf16>;
   using op_t = M::op_t;
@@ -95,10 +95,31 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_dq_kernel(BwdArgs a) {
   if (qrow >= it.sq) j_max = -1;
 
   // dP^T chains start from -D instead of zero, so the accumulator ends as
-  // dP - D and dS = P (dP - D) is one multiply
+  // dP - D and dS = P (dP - D) is one multiply (with dropout, dS = P (Z dP / kp
+  // - D) needs dP alone: the chains start from zero)
   floatx16 ndrow;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) ndrow[r] = -drow;
+  for (int r = 0; r < 16; ++r) ndrow[r] = kDrop ? 0.f : -drow;
+
+  // Dropout keep bits of this lane's row for the 64 keys of a tile (three
+  // 32-bit words, funnel-shifted in the softmax; bit k = key 64 t + k).  The
+  // words of tile t + 1 are loaded during tile t; the wait at the end of each
+  // tile covers them.
+  uint32_t mw[3] = {0u, 0u, 0u}, mnext[3] = {0u, 0u, 0u};
+  uint32_t msh = 0, mshnext = 0;
+  const int64_t drop_row = kDrop ? it.drop_base + (int64_t)head * it.sq * it.skv +
+                                       (int64_t)(qrow < it.sq ? qrow : 0) * it.skv
+                                 : 0;
+  auto load_mask = [&](int tile) {
+    if constexpr (kDrop) {
+      const int64_t bit = drop_row + (int64_t)tile * BN;
+      const int64_t w = bit >> 5;
+      mshnext = (uint32_t)(bit & 31);
+#pragma unroll
+      for (int e = 0; e < 3; ++e)
+        mnext[e] = (qrow < it.sq && w + e < a.drop.n_words) ? a.drop.words[w + e] : 0u;
+    }
+  };
 
   floatx16 acc[NDB];  // dQ^T: rows = head dim 32 db + c_row(r, h), column = this lane's row
 #pragma unroll
@@ -133,6 +154,12 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_dq_kernel(BwdArgs a) {
     op_t ring[RING];
     floatx16 s[2], dp[2];
     op_t sk[2][2];
+    // keep bits of this lane's keys: block jb, register r -> key 32 jb + c_row(r, h)
+    uint32_t keep[2] = {0u, 0u};
+    if constexpr (kDrop) {
+      keep[0] = __builtin_amdgcn_alignbit(mw[1], mw[0], msh) >> (4 * h);
+      keep[1] = __builtin_amdgcn_alignbit(mw[2], mw[1], msh) >> (4 * h);
+    }
 
     auto read = [&](auto ic) {
       constexpr int i = decltype(ic)::value;
@@ -153,7 +180,7 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_dq_kernel(BwdArgs a) {
         if constexpr (i % 2 == 0)
           s[jb] = M::mma(x, qf[t], t == 0 ? floatx16{} : s[jb]);
         else
-          dp[jb] = M::mma(x, yf[t], t == 0 ? ndrow : dp[jb]);
+          dp[jb] = M::mma(x, yf[t], t == 0 ? ndrow : dp[jb]);  // ndrow: -D (no dropout) or 0
       } else {
         constexpr int j = i - G_Q0, jb = j / NQ, t2 = (j % NQ) / NDB, db = j % NDB;
         acc[db] = M::mma(x, sk[jb][t2], acc[db]);
@@ -172,7 +199,12 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_dq_kernel(BwdArgs a) {
       s[jb][r] = p;
     };
     auto soft_b = [&](int jb, int r) {
-      dp[jb][r] = s[jb][r] * dp[jb][r];
+      if constexpr (kDrop) {
+        const bool kept = (keep[jb] >> (8 * (r >> 2) + (r & 3))) & 1u;
+        dp[jb][r] = s[jb][r] * ((kept ? dp[jb][r] * a.drop.rkp : 0.f) - drow);
+      } else {
+        dp[jb][r] = s[jb][r] * dp[jb][r];
+      }
       if (r & 1) {
         sk[jb][r >> 3][(r & 7) - 1] = static_cast<bf16>(dp[jb][r - 1]);
         sk[jb][r >> 3][r & 7] = static_cast<bf16>(dp[jb][r]);
@@ -203,6 +235,7 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_dq_kernel(BwdArgs a) {
 
   if (lo <= hi) {
     load_tile(lo, 0);
+    load_mask(lo);
     wait_vmem();
     __syncthreads();
     if (lo < hi) load_tile(lo + 1, 1);
@@ -224,6 +257,12 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_dq_kernel(BwdArgs a) {
   auto run = [&](auto mask_tag, int from, int to) {
     for (int tile = from; tile <= to; ++tile) {
       const int b = (tile - lo) & 1;
+      if constexpr (kDrop) {  // this tile's keep words; fetch the next tile's
+#pragma unroll
+        for (int e = 0; e < 3; ++e) mw[e] = mnext[e];
+        msh = mshnext;
+        if (tile < hi) load_mask(tile + 1);
+      }
       step(mask_tag, tile);
       wait_vmem();
       __syncthreads();
@@ -255,15 +294,21 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_dq_kernel(BwdArgs a) {
   }
 }
 
-int launch_bwd_dq(const BwdArgs& a, int head_dim, void* stream) {
+template <bool kDrop>
+static int launch_dq_t(const BwdArgs& a, int head_dim, void* stream) {
   const int64_t nwg = (int64_t)a.n_items * a.num_heads;
   if (head_dim == 128)
-    hipLaunchKernelGGL((swa_bwd_dq_kernel<128>), dim3((unsigned)nwg), dim3(256), 0,
+    hipLaunchKernelGGL((swa_bwd_dq_kernel<128, kDrop>), dim3((unsigned)nwg), dim3(256), 0,
                        static_cast<hipStream_t>(stream), a);
   else
-    hipLaunchKernelGGL((swa_bwd_dq_kernel<64>), dim3((unsigned)nwg), dim3(256), 0,
+    hipLaunchKernelGGL((swa_bwd_dq_kernel<64, kDrop>), dim3((unsigned)nwg), dim3(256), 0,
                        static_cast<hipStream_t>(stream), a);
   return (int)hipGetLastError();
+}
+
+int launch_bwd_dq(const BwdArgs& a, int head_dim, void* stream) {
+  return a.drop.words ? launch_dq_t<true>(a, head_dim, stream)
+                      : launch_dq_t<false>(a, head_dim, stream);
 }
 
 }  // namespace swa

@@ -7,16 +7,22 @@
 
 namespace swa {
 
-int launch_bwd_kv(const BwdArgs& a, int head_dim, void* stream) {
-  if (a.num_kv_heads != a.num_heads) return launch_bwd_kv_grouped(a, head_dim, stream);
+template <bool kDrop>
+static int launch_bwd_kv_t(const BwdArgs& a, int head_dim, void* stream) {
   const int64_t nwg = (int64_t)a.n_items * a.num_kv_heads;  // one workgroup per key block and head
   if (head_dim == 128)
-    hipLaunchKernelGGL((swa_bwd_kv_kernel<128, false>), dim3((unsigned)nwg), dim3(256), 0,
+    hipLaunchKernelGGL((swa_bwd_kv_kernel<128, false, kDrop>), dim3((unsigned)nwg), dim3(256), 0,
                        static_cast<hipStream_t>(stream), a);
   else
-    hipLaunchKernelGGL((swa_bwd_kv_kernel<64, false>), dim3((unsigned)nwg), dim3(256), 0,
+    hipLaunchKernelGGL((swa_bwd_kv_kernel<64, false, kDrop>), dim3((unsigned)nwg), dim3(256), 0,
                        static_cast<hipStream_t>(stream), a);
   return (int)hipGetLastError();
+}
+
+int launch_bwd_kv(const BwdArgs& a, int head_dim, void* stream) {
+  if (a.num_kv_heads != a.num_heads) return launch_bwd_kv_grouped(a, head_dim, stream);
+  return a.drop.words ? launch_bwd_kv_t<true>(a, head_dim, stream)
+                      : launch_bwd_kv_t<false>(a, head_dim, stream);
 }
 
 }  // namespace swa

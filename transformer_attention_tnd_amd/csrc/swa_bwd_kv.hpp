@@ -35,7 +35,7 @@ namespace swa {
 // scheduling fences keeping that order.  LDS holds two slabs (the tiles of
 // query/key tile t and t+1, loaded straight from HBM); the lane offsets into
 // them sit in registers and move to the other slab once per tile.
-template <int D, bool kGroups>
+template <int D, bool kGroups, bool kDrop>
 __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
   using M = Mfma<bf16>;
   using op_t = M::op_t;
@@ -67,6 +67,9 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds[2 * SLAB];
   __shared__ floatx4 lse_s[2][BM / 4];   // lse2 of the tile's rows
   __shared__ floatx4 drow_s[2][BM / 4];  // D of the tile's rows
+  // dropout keep bits of the tile: [slot][key word kw / 32 of the block][row],
+  // bit c of a word = key 32 * word + c
+  __shared__ uint32_t mask_s[kDrop ? 2 * 4 * BM : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, h = lane >> 5, c = lane & 31;
@@ -85,7 +88,9 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
   const bf16* dyg = nullptr;
   const float* lse_g = nullptr;
   const float* drow_g = nullptr;
+  int64_t drop_head = 0;  // first dropout-mask bit of (sequence, query head)
   auto set_head = [&](int hq) {
+    drop_head = it.drop_base + (int64_t)hq * it.sq * it.skv;
     qg = static_cast<const bf16*>(a.q) + (int64_t)it.q_base * ld + hq * D;
     dyg = static_cast<const bf16*>(a.dy) + (int64_t)it.q_base * ld + hq * D;
     lse_g = a.lse2 + (int64_t)hq * a.t_q + it.q_base;
@@ -128,12 +133,17 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
   int oq[DSTEPS];   // 128-bit read of row c, chunk 2t + h
   int otr[NDB][2];  // transposing reads, head-dim block db
   int olr = 16 * h; // lse2 / D of rows 4h .. 4h + 3 of each 8
+  int omk = (w * BM + 4 * h) * 4;  // keep words of this wave's keys, rows 4h .. 4h + 3 of each 8
 #pragma unroll
   for (int t = 0; t < DSTEPS; ++t) oq[t] = tile_off<RB>(c, (16 * t + 8 * h) * 2);
 #pragma unroll
   for (int db = 0; db < NDB; ++db) tr_offsets<RB>(lane, db, otr[db][0], otr[db][1]);
 
   float sreg = 0.f;
+  // dropout: thread (row = tid % 64, word = tid / 64) fetches the 32 keep bits
+  // of its row for keys 32 word .. 32 word + 31 of the block (two words and a
+  // shift, joined when they are stored)
+  uint32_t mreg[2] = {0u, 0u}, msh = 0;
   auto load_tile = [&](int tile, int b) {
     const int nvalid = it.sq - tile * BM;
     char* slab = lds + b * SLAB;
@@ -146,12 +156,23 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
       else
         sreg = i < it.sq ? drow_g[i] : 0.f;
     }
+    if constexpr (kDrop) {
+      const int row = tid & (BM - 1), i = tile * BM + row;
+      const int64_t bit = drop_head + (int64_t)i * it.skv + it.block * BN + 32 * (tid / BM);
+      const int64_t wd = bit >> 5;
+      msh = (uint32_t)(bit & 31);
+      mreg[0] = (i < it.sq && wd < a.drop.n_words) ? a.drop.words[wd] : 0u;
+      mreg[1] = (i < it.sq && wd + 1 < a.drop.n_words) ? a.drop.words[wd + 1] : 0u;
+    }
   };
   auto store_rows = [&](int b) {
     if (tid < BM)
       reinterpret_cast<float*>(lse_s[b])[tid] = sreg;
     else if (tid < 2 * BM)
       reinterpret_cast<float*>(drow_s[b])[tid - BM] = sreg;
+    if constexpr (kDrop)
+      mask_s[b * 4 * BM + (tid / BM) * BM + (tid & (BM - 1))] =
+          __builtin_amdgcn_alignbit(mreg[1], mreg[0], msh);
   };
   auto rd128 = [&](int off) { return *reinterpret_cast<const op_t*>(lds + off); };
 
@@ -168,6 +189,7 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
     op_t ring[RING];
     floatx16 s[2], dp[2];
     floatx4 lv[2][4], dv4[2][4];
+    uint32_t mk[2][4][4];  // keep words of rows 32 qb + 8 g + 4 h + e (this wave's keys)
     op_t pk[2][2], sk[2][2];
 
     auto read = [&](auto ic) {
@@ -214,7 +236,14 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
       s[qb][r] = p;
     };
     auto soft_b = [&](int qb, int r) {
-      dp[qb][r] = s[qb][r] * (dp[qb][r] - dv4[qb][r >> 2][r & 3]);
+      if constexpr (kDrop) {
+        // dV takes P Z / kp, dS = P (Z dP / kp - D)
+        const bool kept = (mk[qb][r >> 2][r & 3] >> c) & 1u;
+        dp[qb][r] = s[qb][r] * ((kept ? dp[qb][r] * a.drop.rkp : 0.f) - dv4[qb][r >> 2][r & 3]);
+        s[qb][r] = kept ? s[qb][r] * a.drop.rkp : 0.f;
+      } else {
+        dp[qb][r] = s[qb][r] * (dp[qb][r] - dv4[qb][r >> 2][r & 3]);
+      }
       if (r & 1) {
         pk[qb][r >> 3][(r & 7) - 1] = static_cast<bf16>(s[qb][r - 1]);
         pk[qb][r >> 3][r & 7] = static_cast<bf16>(s[qb][r]);
@@ -234,6 +263,13 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
             const int off = olr + (32 * qb + 8 * g) * 4;
             lv[qb][g] = *reinterpret_cast<const floatx4*>(reinterpret_cast<const char*>(lse_s) + off);
             dv4[qb][g] = *reinterpret_cast<const floatx4*>(reinterpret_cast<const char*>(drow_s) + off);
+            if constexpr (kDrop) {
+              typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+              const u32x4_t m4 = *reinterpret_cast<const u32x4_t*>(
+                  reinterpret_cast<const char*>(mask_s) + omk + (32 * qb + 8 * g) * 4);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) mk[qb][g][e] = m4[e];
+            }
           }
         }
       }
@@ -273,6 +309,10 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
     }
     olr += b ? -(int)sizeof(lse_s[0]) : (int)sizeof(lse_s[0]);
     asm volatile("" : "+v"(olr));
+    if constexpr (kDrop) {
+      omk += b ? -4 * 4 * BM : 4 * 4 * BM;
+      asm volatile("" : "+v"(omk));
+    }
   };
   // tiles [from, to] in order, each body branch-free (masked or not)
   auto run = [&](auto mask_tag, int from, int to) {

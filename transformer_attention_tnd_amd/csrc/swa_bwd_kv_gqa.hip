@@ -6,15 +6,21 @@
 
 namespace swa {
 
-int launch_bwd_kv_grouped(const BwdArgs& a, int head_dim, void* stream) {
+template <bool kDrop>
+static int launch_bwd_kv_grouped_t(const BwdArgs& a, int head_dim, void* stream) {
   const int64_t nwg = (int64_t)a.n_items * a.num_kv_heads;  // one workgroup per key block and K/V head
   if (head_dim == 128)
-    hipLaunchKernelGGL((swa_bwd_kv_kernel<128, true>), dim3((unsigned)nwg), dim3(256), 0,
+    hipLaunchKernelGGL((swa_bwd_kv_kernel<128, true, kDrop>), dim3((unsigned)nwg), dim3(256), 0,
                        static_cast<hipStream_t>(stream), a);
   else
-    hipLaunchKernelGGL((swa_bwd_kv_kernel<64, true>), dim3((unsigned)nwg), dim3(256), 0,
+    hipLaunchKernelGGL((swa_bwd_kv_kernel<64, true, kDrop>), dim3((unsigned)nwg), dim3(256), 0,
                        static_cast<hipStream_t>(stream), a);
   return (int)hipGetLastError();
+}
+
+int launch_bwd_kv_grouped(const BwdArgs& a, int head_dim, void* stream) {
+  return a.drop.words ? launch_bwd_kv_grouped_t<true>(a, head_dim, stream)
+                      : launch_bwd_kv_grouped_t<false>(a, head_dim, stream);
 }
 
 }  // namespace swa

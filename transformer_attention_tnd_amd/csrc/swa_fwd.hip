@@ -66,7 +66,7 @@ __device__ inline float pair_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <typename T, int D, bool kPos>
+template <typename T, int D, bool kPos, bool kDrop>
 __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
   using M = Mfma<T>;
   using op_t = typename M::op_t;
@@ -120,6 +120,25 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
     }
   }
   const float cs = kPos ? a.scale_log2 : 1.f;  // raw score -> exp2 units
+
+  // Dropout keep bits of this lane's row for the 64 keys of a tile: three
+  // 32-bit words loaded in the matrix phase that forms the tile's scores,
+  // funnel-shifted into the window in its softmax (bit k = key 64 t + k).
+  uint32_t mw[3] = {0u, 0u, 0u};
+  uint32_t msh = 0;
+  const int64_t drop_row = kDrop ? it.drop_base + (int64_t)head * it.sq * it.skv +
+                                       (int64_t)(qrow < it.sq ? qrow : 0) * it.skv
+                                 : 0;
+  auto load_mask = [&](int tile) {
+    if constexpr (kDrop) {
+      const int64_t bit = drop_row + (int64_t)tile * BN;
+      const int64_t w = bit >> 5;
+      msh = (uint32_t)(bit & 31);
+#pragma unroll
+      for (int e = 0; e < 3; ++e)
+        mw[e] = (qrow < it.sq && w + e < a.drop.n_words) ? a.drop.words[w + e] : 0u;
+    }
+  };
 
   // Q fragments: B operand of S^T = K Q^T, lane (column qrow) holds
   // Q[qrow][KSTEP*t + KPL*h + e].
@@ -221,14 +240,23 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
       for (int db = 0; db < NDB; ++db) o[db] *= alpha;
     }
     const float moff = m_ref == -INFINITY ? 0.f : -m_ref * cs;
+    // keep bits of this lane's keys: block jb, register r -> key 32 jb + c_row(r, h)
+    uint32_t keep[NJB] = {};
+    if constexpr (kDrop) {
+      keep[0] = __builtin_amdgcn_alignbit(mw[1], mw[0], msh) >> (4 * h);
+      keep[1] = __builtin_amdgcn_alignbit(mw[2], mw[1], msh) >> (4 * h);
+    }
     float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int jb = 0; jb < NJB; ++jb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float p = __builtin_amdgcn_exp2f(fmaf(s[jb][r], cs, moff));
-        s[jb][r] = p;
-        ls[r & 3] += p;
+        ls[r & 3] += p;  // the row sum is that of the undropped softmax
+        if constexpr (kDrop)
+          s[jb][r] = ((keep[jb] >> (8 * (r >> 2) + (r & 3))) & 1u) ? p * a.drop.rkp : 0.f;
+        else
+          s[jb][r] = p;
       }
 #pragma unroll
       for (int t2 = 0; t2 < PSTEPS; ++t2) pk[jb][t2] = M::pack(s[jb], t2);
@@ -300,6 +328,9 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
   auto m_phase = [&](int t, int k) {
     const bool do_pv = t - 1 >= mlo && t - 1 <= mhi;
     const bool do_s = t >= mlo && t <= mhi;
+    if constexpr (kDrop) {
+      if (do_s) load_mask(t);
+    }
     const char* kt = kbuf0 + (k % NBUF) * TB;                 // K(t)
     const char* vt = vbuf0 + ((k + NBUF - 1) % NBUF) * TB;    // V(t-1)
     if constexpr (sizeof(T) == 2) {
@@ -411,23 +442,29 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, bool kDrop>
 static int launch_fwd_t(const FwdArgs& a, void* stream) {
   const int64_t nwg = (int64_t)a.n_items * a.num_heads;
   if (a.scale_log2 > 0.f)
-    hipLaunchKernelGGL((swa_fwd_kernel<T, D, true>), dim3((unsigned)nwg), dim3(512), 0,
+    hipLaunchKernelGGL((swa_fwd_kernel<T, D, true, kDrop>), dim3((unsigned)nwg), dim3(512), 0,
                        static_cast<hipStream_t>(stream), a);
   else
-    hipLaunchKernelGGL((swa_fwd_kernel<T, D, false>), dim3((unsigned)nwg), dim3(512), 0,
+    hipLaunchKernelGGL((swa_fwd_kernel<T, D, false, kDrop>), dim3((unsigned)nwg), dim3(512), 0,
                        static_cast<hipStream_t>(stream), a);
   return (int)hipGetLastError();
 }
 
+template <bool kDrop>
+static int launch_fwd_d(const FwdArgs& a, int dtype, int head_dim, void* stream) {
+  if (dtype == 1) return head_dim == 128 ? launch_fwd_t<bf16, 128, kDrop>(a, stream)
+                                         : launch_fwd_t<bf16, 64, kDrop>(a, stream);
+  return head_dim == 128 ? launch_fwd_t<float, 128, kDrop>(a, stream)
+                         : launch_fwd_t<float, 64, kDrop>(a, stream);
+}
+
 int launch_forward(const FwdArgs& a, int dtype, int head_dim, void* stream) {
-  if (dtype == 1) return head_dim == 128 ? launch_fwd_t<bf16, 128>(a, stream)
-                                         : launch_fwd_t<bf16, 64>(a, stream);
-  return head_dim == 128 ? launch_fwd_t<float, 128>(a, stream)
-                         : launch_fwd_t<float, 64>(a, stream);
+  return a.drop.words ? launch_fwd_d<true>(a, dtype, head_dim, stream)
+                      : launch_fwd_d<false>(a, dtype, head_dim, stream);
 }
 
 }  // namespace swa

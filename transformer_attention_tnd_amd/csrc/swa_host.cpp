@@ -34,6 +34,7 @@ swa_status fail(swa_status s, const std::string& msg) {
 struct Seq {
   int64_t q0, sq, k0, skv;
   int32_t b;
+  int64_t drop_base;  // first dropout-mask bit of this sequence (sum of N Sq Skv before it)
 };
 
 int64_t floor_div(int64_t a, int64_t b) {
@@ -101,7 +102,10 @@ swa_status parse_seqs(const Problem& p, std::vector<Seq>& seqs, int64_t* end_q,
     if (cq < prev_q || ck < prev_kv)
       return fail(SWA_ERR_INVALID, "cu_seqlens must be non-decreasing (batch " +
                                        std::to_string(b) + ")");
-    seqs.push_back(Seq{prev_q, cq - prev_q, prev_kv, ck - prev_kv, static_cast<int32_t>(b)});
+    const int64_t base = seqs.empty() ? 0
+                                      : seqs.back().drop_base +
+                                            p.num_heads * seqs.back().sq * seqs.back().skv;
+    seqs.push_back(Seq{prev_q, cq - prev_q, prev_kv, ck - prev_kv, static_cast<int32_t>(b), base});
     prev_q = cq;
     prev_kv = ck;
   }
@@ -119,6 +123,15 @@ swa_status parse_seqs(const Problem& p, std::vector<Seq>& seqs, int64_t* end_q,
                         std::to_string(s.b) + " has " + std::to_string(s.sq) + " and " +
                         std::to_string(s.skv));
   }
+  if (p.drop_mask) {  // the mask covers sum_b N Sq Skv bits, read as whole 32-bit words
+    int64_t bits = 0;
+    for (const Seq& s : seqs) bits += p.num_heads * s.sq * s.skv;
+    const int64_t need = (bits + 31) / 32 * 4;
+    if (static_cast<int64_t>(p.drop_mask_bytes) < need)
+      return fail(SWA_ERR_INVALID, "drop_mask has " + std::to_string(p.drop_mask_bytes) +
+                                       " bytes, needs " + std::to_string(need) +
+                                       " (the mask bits rounded up to whole 32-bit words)");
+  }
   *end_q = prev_q;
   *end_kv = prev_kv;
   return SWA_OK;
@@ -128,6 +141,13 @@ swa_status validate(const Problem& p, std::vector<Seq>& seqs, int64_t* end_q, in
   if (!p.cu_q || !p.cu_kv) return fail(SWA_ERR_NULLPTR, "cu_seqlens_q / cu_seqlens_kv is NULL");
   swa_status s = check_sizes(p.num_seqs, p.t_q, p.t_kv, p.num_heads, p.head_dim, p.dtype);
   if (s != SWA_OK) return s;
+  // dropout with a given mask (API doc, dropMaskOptional / keepProbOptional; explainer 6.3)
+  if (p.drop_mask) {
+    if (!std::isfinite(p.keep_prob) || !(p.keep_prob > 0.0 && p.keep_prob <= 1.0))
+      return fail(SWA_ERR_INVALID, "keep_prob must be in (0, 1], got " + std::to_string(p.keep_prob));
+    if (reinterpret_cast<uintptr_t>(p.drop_mask) % 4 != 0)
+      return fail(SWA_ERR_INVALID, "drop_mask must be 4-byte aligned");
+  }
   // explainer 6.2: the query head count is a whole multiple of the key/value head count
   if (p.num_kv_heads < 1 || p.num_kv_heads > p.num_heads || p.num_heads % p.num_kv_heads != 0)
     return fail(SWA_ERR_INVALID, "num_heads (" + std::to_string(p.num_heads) +
@@ -196,6 +216,7 @@ Item make_item(const Problem& p, const Seq& s, int64_t block) {
   it.seq = s.b;
   it.band[0] = clamp_window(bd.pre);
   it.band[1] = clamp_window(bd.next);
+  it.drop_base = s.drop_base;
   it.tiles[1] = pack_range(1, 0);
   it.full[1] = pack_range(1, 0);
   return it;
@@ -385,6 +406,9 @@ Problem make_problem(const int64_t* cu_q, const int64_t* cu_kv, int64_t num_seqs
   p.sparse_mode = mode;
   p.cu_q = cu_q;
   p.cu_kv = cu_kv;
+  p.drop_mask = nullptr;
+  p.drop_mask_bytes = 0;
+  p.keep_prob = 1.0;
   return p;
 }
 
@@ -440,6 +464,13 @@ int timed_launch(int kind, void* stream, F&& fn) {
   return e;
 }
 
+// Kernel operands of the dropout mask (words null: no dropout).
+DropArgs drop_args(const Problem& p) {
+  DropArgs d{static_cast<const uint32_t*>(p.drop_mask),
+             static_cast<int64_t>(p.drop_mask_bytes / 4), static_cast<float>(1.0 / p.keep_prob)};
+  return d;
+}
+
 }  // namespace
 }  // namespace swa
 
@@ -469,18 +500,22 @@ swa_status swa_backward_workspace_size(int64_t num_seqs, int64_t t_q, int64_t t_
   return SWA_OK;
 }
 
-swa_status swa_forward_gqa(const void* q, const void* k, const void* v,
-                           const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,
-                           int64_t num_seqs, int64_t t_q, int64_t t_kv, int64_t num_heads,
-                           int64_t num_kv_heads, int64_t head_dim, int32_t dtype, double scale,
-                           int64_t pre_tokens, int64_t next_tokens, int64_t sparse_mode,
-                           void* out, float* softmax_max, float* softmax_sum, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+swa_status swa_forward_ex(const void* q, const void* k, const void* v,
+                          const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,
+                          int64_t num_seqs, int64_t t_q, int64_t t_kv, int64_t num_heads,
+                          int64_t num_kv_heads, int64_t head_dim, int32_t dtype, double scale,
+                          int64_t pre_tokens, int64_t next_tokens, int64_t sparse_mode,
+                          const void* drop_mask, size_t drop_mask_bytes, double keep_prob,
+                          void* out, float* softmax_max, float* softmax_sum, void* workspace,
+                          size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !out || !softmax_max || !softmax_sum || !workspace)
     return fail(SWA_ERR_NULLPTR, "a required tensor or the workspace is NULL");
   Problem p = make_problem(cu_seqlens_q, cu_seqlens_kv, num_seqs, t_q, t_kv, num_heads,
                            num_kv_heads, head_dim, dtype, scale, pre_tokens, next_tokens,
                            sparse_mode);
+  p.drop_mask = drop_mask;
+  p.drop_mask_bytes = drop_mask_bytes;
+  p.keep_prob = keep_prob;
   std::vector<Seq> seqs;
   int64_t end_q = 0, end_kv = 0;
   swa_status s = validate(p, seqs, &end_q, &end_kv);
@@ -514,6 +549,7 @@ swa_status swa_forward_gqa(const void* q, const void* k, const void* v,
     a.num_kv_heads = static_cast<int32_t>(num_kv_heads);
     a.scale_log2 = static_cast<float>(scale * 1.4426950408889634);
     a.mode = static_cast<int32_t>(sparse_mode);
+    a.drop = drop_args(p);
     if ((e = timed_launch(K_FWD, stream, [&] {
            return launch_forward(a, dtype, static_cast<int>(head_dim), stream);
          })) != 0)
@@ -528,26 +564,30 @@ swa_status swa_forward(const void* q, const void* k, const void* v, const int64_
                        double scale, int64_t pre_tokens, int64_t next_tokens,
                        int64_t sparse_mode, void* out, float* softmax_max, float* softmax_sum,
                        void* workspace, size_t workspace_bytes, void* stream) {
-  return swa_forward_gqa(q, k, v, cu_seqlens_q, cu_seqlens_kv, num_seqs, t_q, t_kv, num_heads,
-                         num_heads, head_dim, dtype, scale, pre_tokens, next_tokens,
-                         sparse_mode, out, softmax_max, softmax_sum, workspace, workspace_bytes,
-                         stream);
+  return swa_forward_ex(q, k, v, cu_seqlens_q, cu_seqlens_kv, num_seqs, t_q, t_kv, num_heads,
+                        num_heads, head_dim, dtype, scale, pre_tokens, next_tokens, sparse_mode,
+                        nullptr, 0, 1.0, out, softmax_max, softmax_sum, workspace,
+                        workspace_bytes, stream);
 }
 
-swa_status swa_backward_gqa(const void* q, const void* k, const void* v, const void* dy,
-                            const void* out, const float* softmax_max,
-                            const float* softmax_sum, const int64_t* cu_seqlens_q,
-                            const int64_t* cu_seqlens_kv, int64_t num_seqs, int64_t t_q,
-                            int64_t t_kv, int64_t num_heads, int64_t num_kv_heads,
-                            int64_t head_dim, int32_t dtype, double scale, int64_t pre_tokens,
-                            int64_t next_tokens, int64_t sparse_mode, void* dq, void* dk,
-                            void* dv, void* workspace, size_t workspace_bytes, void* stream) {
+swa_status swa_backward_ex(const void* q, const void* k, const void* v, const void* dy,
+                           const void* out, const float* softmax_max, const float* softmax_sum,
+                           const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,
+                           int64_t num_seqs, int64_t t_q, int64_t t_kv, int64_t num_heads,
+                           int64_t num_kv_heads, int64_t head_dim, int32_t dtype, double scale,
+                           int64_t pre_tokens, int64_t next_tokens, int64_t sparse_mode,
+                           const void* drop_mask, size_t drop_mask_bytes, double keep_prob,
+                           void* dq, void* dk, void* dv, void* workspace,
+                           size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !dy || !out || !softmax_max || !softmax_sum || !dq || !dk || !dv ||
       !workspace)
     return fail(SWA_ERR_NULLPTR, "a required tensor or the workspace is NULL");
   Problem p = make_problem(cu_seqlens_q, cu_seqlens_kv, num_seqs, t_q, t_kv, num_heads,
                            num_kv_heads, head_dim, dtype, scale, pre_tokens, next_tokens,
                            sparse_mode);
+  p.drop_mask = drop_mask;
+  p.drop_mask_bytes = drop_mask_bytes;
+  p.keep_prob = keep_prob;
   std::vector<Seq> seqs;
   int64_t end_q = 0, end_kv = 0;
   swa_status s = validate(p, seqs, &end_q, &end_kv);
@@ -595,6 +635,7 @@ swa_status swa_backward_gqa(const void* q, const void* k, const void* v, const v
   a.num_heads = static_cast<int32_t>(num_heads);
   a.num_kv_heads = static_cast<int32_t>(num_kv_heads);
   a.t_q = static_cast<int32_t>(t_q);
+  a.drop = drop_args(p);
   a.scale = static_cast<float>(scale);
   a.scale_log2 = static_cast<float>(scale * 1.4426950408889634);
   a.mode = static_cast<int32_t>(sparse_mode);
@@ -644,10 +685,10 @@ swa_status swa_backward(const void* q, const void* k, const void* v, const void*
                         int64_t head_dim, int32_t dtype, double scale, int64_t pre_tokens,
                         int64_t next_tokens, int64_t sparse_mode, void* dq, void* dk, void* dv,
                         void* workspace, size_t workspace_bytes, void* stream) {
-  return swa_backward_gqa(q, k, v, dy, out, softmax_max, softmax_sum, cu_seqlens_q,
-                          cu_seqlens_kv, num_seqs, t_q, t_kv, num_heads, num_heads, head_dim,
-                          dtype, scale, pre_tokens, next_tokens, sparse_mode, dq, dk, dv,
-                          workspace, workspace_bytes, stream);
+  return swa_backward_ex(q, k, v, dy, out, softmax_max, softmax_sum, cu_seqlens_q,
+                         cu_seqlens_kv, num_seqs, t_q, t_kv, num_heads, num_heads, head_dim,
+                         dtype, scale, pre_tokens, next_tokens, sparse_mode, nullptr, 0, 1.0,
+                         dq, dk, dv, workspace, workspace_bytes, stream);
 }
 
 swa_status swa_debug_tile_schedule(const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,

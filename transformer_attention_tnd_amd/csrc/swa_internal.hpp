@@ -21,12 +21,14 @@ constexpr int DQ_BM = FWD_HALF;
 // query rows per backward tile: 64, or 32 for fp32 with head_dim 128 (LDS)
 constexpr int bwd_block_q(int dtype, int head_dim) { return (dtype == 0 && head_dim == 128) ? 32 : 64; }
 
-// One schedule entry (48 bytes, uploaded to the workspace).
+// One schedule entry (64 bytes, uploaded to the workspace).
 //   tiles[i] = lo | hi << 16 : visited tile range [lo, hi] (empty if lo > hi)
 //   full[i]  = flo | fhi << 16 : tiles in [flo, fhi] need no element mask
 //   band     = {pre, next} of the sequence's mask (key j allowed for query i
 //              iff -pre <= j - i <= next), clamped to +-2^30; unused when the
 //              kernel's mode is 0 (no mask)
+//   drop_base = first dropout-mask bit of the sequence (its head 0); head n
+//              starts n * sq * skv bits later
 // Forward items carry one range per FWD_HALF-row half (index 0, 1); backward
 // items (dK/dV and dQ) use index 0 only.
 struct Item {
@@ -39,8 +41,10 @@ struct Item {
   int32_t tiles[2];
   int32_t full[2];
   int32_t band[2];
+  int64_t drop_base;
+  int64_t pad;
 };
-static_assert(sizeof(Item) == 48, "Item layout");
+static_assert(sizeof(Item) == 64, "Item layout");
 
 inline int32_t pack_range(int64_t lo, int64_t hi) {
   if (lo > hi) { lo = 1; hi = 0; }
@@ -54,6 +58,17 @@ struct Problem {
   int64_t pre_tokens, next_tokens, sparse_mode;
   const int64_t* cu_q;
   const int64_t* cu_kv;
+  const void* drop_mask;   // packed keep bits (null: no dropout)
+  size_t drop_mask_bytes;
+  double keep_prob;
+};
+
+// Dropout operands of the kernels: the packed keep bits as 32-bit words
+// (null: no dropout), their count, and 1 / keep_prob.
+struct DropArgs {
+  const uint32_t* words;
+  int64_t n_words;
+  float rkp;
 };
 
 // Kernel arguments.  Element pointers are typeless; the kernels cast.
@@ -70,6 +85,7 @@ struct FwdArgs {
   int32_t num_kv_heads;  // key/value heads; query head n reads head n / (num_heads / num_kv_heads)
   float scale_log2;  // scale * log2(e)
   int32_t mode;      // 0: no mask; otherwise each item's band applies
+  DropArgs drop;
 };
 
 struct BwdPreArgs {
@@ -104,6 +120,7 @@ struct BwdArgs {
   float scale;
   float scale_log2;
   int32_t mode;  // 0: no mask; otherwise each item's band applies
+  DropArgs drop;
 };
 
 struct FinalizeArgs {

@@ -176,3 +176,27 @@ def make_custom(lengths_q, lengths_kv=None, num_heads=2, head_dim=64, dtype=torc
         scale = 1.0 / math.sqrt(head_dim)
     return Problem(q, k, v, dy, cu_q, cu_kv, scale, pre_tokens, next_tokens, sparse_mode,
                    name=name)
+
+
+def make_drop_mask(p: Problem, keep_prob: float, seed: int = 7) -> torch.Tensor:
+    """Seeded dropout keep mask for problem p: one bit per (participating batch,
+    query head, query row, key), each 1 with probability keep_prob, packed
+    eight to a byte least significant bit first in (batch, head, row, key)
+    order, and padded with zero bytes to whole 32-bit words (uint8 host tensor)."""
+    import numpy as np
+    g = torch.Generator("cpu").manual_seed(seed)
+    lens_q, lens_kv, prev_q, prev_kv = [], [], 0, 0
+    for cq, ck in zip(p.cu_seqlens_q, p.cu_seqlens_kv):
+        if cq == 0 and prev_q > 0:
+            break
+        lens_q.append(cq - prev_q)
+        lens_kv.append(ck - prev_kv)
+        prev_q, prev_kv = cq, ck
+    nbits = sum(p.num_heads * a * b for a, b in zip(lens_q, lens_kv))
+    keep = (torch.rand(nbits, generator=g) < keep_prob).numpy().astype(np.uint8)
+    packed = np.packbits(keep, bitorder="little")
+    words = (packed.size + 3) // 4
+    out = np.zeros(4 * max(words, 1), dtype=np.uint8)
+    out[:packed.size] = packed
+    return torch.from_numpy(out)
+
