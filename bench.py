@@ -134,6 +134,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--keep-prob", type=float, default=1.0,
+                    help="< 1: dropout with a seeded caller mask of this keep probability")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device-to-device copy of this many bytes "
                          "--steps times (calibrates the HBM byte counters)")
@@ -177,11 +179,14 @@ def main():
                        dtype=torch.uint8, device=dev)
     args_common = (p.cu_seqlens_q, p.cu_seqlens_kv, p.scale, p.pre_tokens, p.next_tokens,
                    p.sparse_mode)
+    drop = None
+    if args.keep_prob < 1.0:
+        drop = workloads.make_drop_mask(p, args.keep_prob).to(dev)
 
     def step():
-        swa.swa_forward_ex(q, k, v, *args_common, None, 1.0, out, smax, ssum, ws_f)
-        swa.swa_backward_ex(q, k, v, dy, out, smax, ssum, *args_common, None, 1.0, dq, dk, dv,
-                            ws_b)
+        swa.swa_forward_ex(q, k, v, *args_common, drop, args.keep_prob, out, smax, ssum, ws_f)
+        swa.swa_backward_ex(q, k, v, dy, out, smax, ssum, *args_common, drop, args.keep_prob, dq,
+                            dk, dv, ws_b)
 
     for _ in range(args.warmup):
         step()
@@ -238,11 +243,11 @@ def main():
     achieved = kern[dominant]["achieved"]
     roofline = {"kernel": dominant, "bound": bound, "achieved": achieved, "peak": peak,
                 "unit": unit, "frac": achieved / peak,
-                "traffic": traffic_record(dominant, name),
+                "traffic": traffic_record(dominant, name) if drop is None else None,
                 "avg_launch_ms": kern[dominant]["avg_ms"]}
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and drop is None:  # (the oracle leg runs without dropout)
         cpu = cpu_baseline(p, N, pairs)
 
     t_f = kern["forward"]["avg_ms"]
@@ -263,7 +268,7 @@ def main():
         "config": {"workload": name, "tokens": T, "num_heads": N,
                    "num_kv_heads": k.shape[1], "head_dim": D,
                    "sparse_mode": p.sparse_mode, "pre_tokens": p.pre_tokens,
-                   "next_tokens": p.next_tokens, "num_seqs": nseq,
+                   "next_tokens": p.next_tokens, "num_seqs": nseq, "keep_prob": args.keep_prob,
                    "cu_seqlens": p.cu_seqlens_q if nseq <= 16 else None},
         "pct_of_bf16_peak": 100.0 * value / PEAK_BF16_DERIVED,
         "fwd_tflops": f_fwd / (t_f * 1e-3) / 1e12,

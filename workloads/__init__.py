@@ -193,8 +193,14 @@ def make_drop_mask(p: Problem, keep_prob: float, seed: int = 7) -> torch.Tensor:
         lens_kv.append(ck - prev_kv)
         prev_q, prev_kv = cq, ck
     nbits = sum(p.num_heads * a * b for a, b in zip(lens_q, lens_kv))
-    keep = (torch.rand(nbits, generator=g) < keep_prob).numpy().astype(np.uint8)
-    packed = np.packbits(keep, bitorder="little")
+    if keep_prob == 0.5:  # every bit a fair coin: draw whole random bytes
+        packed = torch.randint(0, 256, ((nbits + 7) // 8,), generator=g,
+                               dtype=torch.uint8).numpy()
+        if nbits % 8:
+            packed[-1] &= (1 << (nbits % 8)) - 1
+    else:
+        keep = (torch.rand(nbits, generator=g) < keep_prob).numpy().astype(np.uint8)
+        packed = np.packbits(keep, bitorder="little")
     words = (packed.size + 3) // 4
     out = np.zeros(4 * max(words, 1), dtype=np.uint8)
     out[:packed.size] = packed
