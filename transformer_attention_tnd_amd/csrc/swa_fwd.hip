@@ -333,6 +333,9 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
     }
     const char* kt = kbuf0 + (k % NBUF) * TB;                 // K(t)
     const char* vt = vbuf0 + ((k + NBUF - 1) % NBUF) * TB;    // V(t-1)
+    // the matrix phase takes issue priority over the other group's softmax
+    // on the same SIMD (measured: about 2 % faster than equal priority)
+    __builtin_amdgcn_s_setprio(3);
     if constexpr (sizeof(T) == 2) {
       using Z = std::integral_constant<int, 0>;
       using P = std::integral_constant<int, PVN>;
@@ -353,6 +356,7 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
         scores(kt);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   };
   // vector phase V(t)
   auto v_phase = [&](int t) {
