@@ -26,6 +26,9 @@
 //   accumulator with atomics (non-deterministic summation order, as the
 //   explainer section 6.1 describes for the default backward);
 //   swa_dq_finalize_kernel then writes dq = scale * dq_acc in the output type.
+//   With grouped heads the workgroup of a key/value head walks the query
+//   heads of its group in turn; with dropout the keep bits of each query tile
+//   are staged in LDS next to lse2 and D.
 
 #include <hip/hip_runtime.h>
 

@@ -25,9 +25,16 @@
 //
 // Data movement: K and V tiles of 64 keys go from HBM straight into
 // swizzled row-major LDS tiles (buffer loads with the LDS destination, rows
-// past the sequence read as zero), double-buffered and issued one tile
-// ahead.  V^T operands come from the row-major V tile through transposing
-// LDS reads.
+// past the sequence read as zero).  They rotate through three buffers each
+// (two when three do not fit), so the copy of a tile is issued two steps
+// before its first use.  V^T operands come from the row-major V tile through
+// transposing LDS reads.  The matrix phase (bf16) is one software pipeline of
+// its products with the LDS operands read a few products ahead; it runs at
+// raised wave priority.
+//
+// Dropout (a kDrop instantiation): the keep bits of a lane's row for the
+// tile are read as three 32-bit words in the matrix phase that forms the
+// tile's scores and applied in its softmax, after the row sum.
 //
 // Rescaling: the exponent reference of a row is only moved when the running
 // max exceeds it by more than 2^8 (in exp2 units); exp values then stay below
