@@ -328,6 +328,25 @@ def invariants_check(p, g):
         assert e1 <= 1e-2 and e2 <= 1e-2
 
 
+def test_maximum_sizes(dev):
+    """The largest sizes the interface takes (explainer 6.3: T up to 1M tokens,
+    N up to 256 heads): one 1,048,576-token sequence with a narrow band
+    (sampled rows and keys at the start, the middle and the end), and 256
+    heads (full parity).  Exercises the 64-bit offsets of every kernel."""
+    T = 1 << 20
+    p = workloads.make_custom([T], num_heads=1, head_dim=128, sparse_mode=4, pre_tokens=192,
+                              next_tokens=64, name="max_tokens")
+    note(f"[parity] max_tokens T={T}")
+    g = run_hip(p, dev)
+    for key in ("out", "dq", "dk", "dv"):
+        assert torch.isfinite(g[key].float()).all(), key
+    sampled_check(p, g, [(0, 0, 0, 64), (0, 0, T // 2 + 37, 64), (0, 0, 10**9, 64)])
+    del g
+    p = workloads.make_custom([300, 77], num_heads=256, head_dim=64, name="max_heads")
+    note("[parity] max_heads N=256")
+    compare_full(p, run_hip(p, dev), run_oracle(p, chunk=None))
+
+
 LARGE = [
     ("varlen_bf16_n16_d128_8seq_256to4096", [(0, 0, 0, 64), (3, 7, 1000, 64), (7, 15, 10**9, 48)]),
     ("swa_bf16_b1_n16_s16384_d128_pre2048_next0",
