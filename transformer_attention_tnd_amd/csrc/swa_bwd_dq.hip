@@ -39,6 +39,7 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_dq_kernel(BwdArgs a) {
   constexpr int NS = 2 * DSTEPS, NQ = 2 * NDB;
   constexpr int G_S1 = NS, G_Q0 = 2 * NS, G_Q1 = G_Q0 + NQ, NOPS = G_Q1 + NQ;
   constexpr int AHEAD = SWA_BWD_AHEAD, RING = AHEAD + 1;
+  constexpr int COPY_EVERY = 4;  // pipeline slots between copy instructions
   static_assert(D == 64 || D == 128, "head_dim 64 or 128");
   // Slot of the first softmax stage of register r of key block jb (spread as
   // in the dK/dV kernel, before the dQ products that use it).
@@ -133,16 +134,22 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db) tr_offsets<RB>(lane, db, otr[db][0], otr[db][1]);
 
-  auto load_tile = [&](int tile, int b) {
-    const int nvalid = it.skv - tile * BN;
+  // copies of the next tile's K and V into its slab, issued part by part from
+  // the pipeline of the current tile; a tile past the band copies zeros (no
+  // memory read) into the free slab
+  using Dma = TileDma<bf16, D, BN>;
+  Dma cp_k, cp_v;
+  auto start_copy = [&](int tile, int b) {
+    const int nvalid = tile <= hi ? it.skv - tile * BN : 0;
     char* slab = lds + b * SLAB;
-    tile_load_lds<bf16, D, BN>(kg + (int64_t)tile * BN * ldkv, ldkv, nvalid, slab, tid);
-    tile_load_lds<bf16, D, BN>(vg + (int64_t)tile * BN * ldkv, ldkv, nvalid, slab + KTB, tid);
+    cp_k.init(kg + (int64_t)tile * BN * ldkv, ldkv, nvalid, slab, tid);
+    cp_v.init(vg + (int64_t)tile * BN * ldkv, ldkv, nvalid, slab + KTB, tid);
   };
   auto rd128 = [&](int off) { return *reinterpret_cast<const op_t*>(lds + off); };
 
-  // One key tile: S^T, dP^T, P, dS, dQ^T += K^T dS^T.
-  auto step = [&](auto mask_tag, int tile) {
+  // One key tile (slab b): S^T, dP^T, P, dS, dQ^T += K^T dS^T; also issues
+  // the copies of tile + 1 into slab b ^ 1.
+  auto step = [&](auto mask_tag, int tile, int b) {
     constexpr bool kMask = decltype(mask_tag)::value;
     // key 32 jb + 8 g + 4 h + e of the tile is allowed iff 32 jb + 8 g + e is in [rel_lo, rel_hi]
     int rel_lo = 0, rel_hi = 0;
@@ -222,8 +229,17 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_dq_kernel(BwdArgs a) {
       }
     };
 
+    start_copy(tile + 1, b ^ 1);
     static_for<NOPS + AHEAD>([&](auto sc) {
       constexpr int sl = decltype(sc)::value;
+      // one copy instruction every COPY_EVERY slots from slot 1
+      if constexpr (sl % COPY_EVERY == 1 && sl / COPY_EVERY < 2 * Dma::PARTS) {
+        constexpr int pt = sl / COPY_EVERY;
+        if constexpr (pt % 2 == 0)
+          cp_k.template issue<pt / 2>();
+        else
+          cp_v.template issue<pt / 2>();
+      }
       if constexpr (sl < NOPS) read(std::integral_constant<int, sl>{});
       if constexpr (sl >= AHEAD) {
         mfma(std::integral_constant<int, sl - AHEAD>{});
@@ -234,11 +250,14 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_dq_kernel(BwdArgs a) {
   };
 
   if (lo <= hi) {
-    load_tile(lo, 0);
+    start_copy(lo, 0);
+    static_for<Dma::PARTS>([&](auto pc) {
+      cp_k.template issue<decltype(pc)::value>();
+      cp_v.template issue<decltype(pc)::value>();
+    });
     load_mask(lo);
     wait_vmem();
     __syncthreads();
-    if (lo < hi) load_tile(lo + 1, 1);
   }
   auto flip = [&](int b) {  // move the lane offsets to the other slab
     const int dr = b ? -SLAB : SLAB;
@@ -263,10 +282,9 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_dq_kernel(BwdArgs a) {
         msh = mshnext;
         if (tile < hi) load_mask(tile + 1);
       }
-      step(mask_tag, tile);
+      step(mask_tag, tile, b);
       wait_vmem();
       __syncthreads();
-      if (tile + 2 <= hi) load_tile(tile + 2, b);
       flip(b);
     }
   };

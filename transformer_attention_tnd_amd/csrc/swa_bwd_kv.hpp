@@ -33,8 +33,10 @@ namespace swa {
 // of products ahead into a small register ring, and the vector work (the
 // softmax elements) is spread over the slots between products, with
 // scheduling fences keeping that order.  LDS holds two slabs (the tiles of
-// query/key tile t and t+1, loaded straight from HBM); the lane offsets into
-// them sit in registers and move to the other slab once per tile.
+// query/key tile t and t+1, copied straight from HBM by instructions that the
+// pipeline of tile t issues one every few slots, so that the copies do not
+// stall the waves in a burst); the lane offsets into them sit in registers
+// and move to the other slab once per tile.
 template <int D, bool kGroups, bool kDrop>
 __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
   using M = Mfma<bf16>;
@@ -51,6 +53,7 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
   constexpr int NS = 2 * DSTEPS, NV = 4 * NDB;
   constexpr int G_S1 = NS, G_V0 = 2 * NS, G_V1 = G_V0 + NV, NOPS = G_V1 + NV;
   constexpr int AHEAD = SWA_BWD_AHEAD, RING = AHEAD + 1;
+  constexpr int COPY_EVERY = 4;        // pipeline slots between copy instructions
   static_assert(BN == 128 && (D == 64 || D == 128), "4 waves x 32 keys, 64-row tiles");
   // Slot of the first softmax stage of register r of block qb: the 16
   // registers are spread evenly from the end of the block's S / dP products
@@ -144,11 +147,19 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
   // of its row for keys 32 word .. 32 word + 31 of the block (two words and a
   // shift, joined when they are stored)
   uint32_t mreg[2] = {0u, 0u}, msh = 0;
-  auto load_tile = [&](int tile, int b) {
-    const int nvalid = it.sq - tile * BM;
+  // copies of the next tile's Q and dY into its slab, issued part by part
+  // from the pipeline of the current tile; a tile past the band copies zeros
+  // (no memory read) into the free slab
+  using Dma = TileDma<bf16, D, BM>;
+  Dma cp_q, cp_dy;
+  auto start_copy = [&](int tile, int b) {
+    const int nvalid = tile <= hi ? it.sq - tile * BM : 0;
     char* slab = lds + b * SLAB;
-    tile_load_lds<bf16, D, BM>(qg + (int64_t)tile * BM * ld, ld, nvalid, slab, tid);
-    tile_load_lds<bf16, D, BM>(dyg + (int64_t)tile * BM * ld, ld, nvalid, slab + QTB, tid);
+    cp_q.init(qg + (int64_t)tile * BM * ld, ld, nvalid, slab, tid);
+    cp_dy.init(dyg + (int64_t)tile * BM * ld, ld, nvalid, slab + QTB, tid);
+  };
+  // lse2 / D (and keep bits) of the tile's rows into registers, for store_rows
+  auto load_rows = [&](int tile) {
     if (tid < 2 * BM) {
       const int row = tid & (BM - 1), i = tile * BM + row;
       if (tid < BM)
@@ -165,6 +176,12 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
       mreg[1] = (i < it.sq && wd + 1 < a.drop.n_words) ? a.drop.words[wd + 1] : 0u;
     }
   };
+  auto copy_all = [&]() {
+    static_for<Dma::PARTS>([&](auto pc) {
+      cp_q.template issue<decltype(pc)::value>();
+      cp_dy.template issue<decltype(pc)::value>();
+    });
+  };
   auto store_rows = [&](int b) {
     if (tid < BM)
       reinterpret_cast<float*>(lse_s[b])[tid] = sreg;
@@ -177,7 +194,8 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
   auto rd128 = [&](int off) { return *reinterpret_cast<const op_t*>(lds + off); };
 
   // One query tile: S, dP, P, dS, dV^T += dY^T P, dK^T += Q^T dS.
-  auto step = [&](auto mask_tag, int tile) {
+  // One query tile (slab b): also issues the copies of tile + 1 into slab b ^ 1
+  auto step = [&](auto mask_tag, int tile, int b) {
     constexpr bool kMask = decltype(mask_tag)::value;
     // row 32 qb + 8 g + 4 h + e is allowed iff 32 qb + 8 g + e is in [rel_lo, rel_hi]
     int rel_lo = 0, rel_hi = 0;
@@ -283,8 +301,18 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
       }
     };
 
+    start_copy(tile + 1, b ^ 1);
     static_for<NOPS + AHEAD>([&](auto sc) {
       constexpr int sl = decltype(sc)::value;
+      if constexpr (sl == 0) load_rows(tile + 1);
+      // one copy instruction every COPY_EVERY slots from slot 1
+      if constexpr (sl % COPY_EVERY == 1 && sl / COPY_EVERY < 2 * Dma::PARTS) {
+        constexpr int pt = sl / COPY_EVERY;
+        if constexpr (pt % 2 == 0)
+          cp_q.template issue<pt / 2>();
+        else
+          cp_dy.template issue<pt / 2>();
+      }
       if constexpr (sl < NOPS) read(std::integral_constant<int, sl>{});
       if constexpr (sl >= AHEAD) {
         mfma(std::integral_constant<int, sl - AHEAD>{});
@@ -318,22 +346,22 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
   auto run = [&](auto mask_tag, int from, int to) {
     for (int tile = from; tile <= to; ++tile) {
       const int b = (tile - lo) & 1;
-      step(mask_tag, tile);
+      step(mask_tag, tile, b);
       if (tile < hi) store_rows(b ^ 1);
       wait_vmem();
       __syncthreads();
-      if (tile + 2 <= hi) load_tile(tile + 2, b);
       flip(b);
     }
   };
   for (int gi = 0; gi < G; ++gi) {
     set_head(kvh * G + gi);
     if (lo <= hi) {
-      load_tile(lo, 0);
+      start_copy(lo, 0);
+      copy_all();
+      load_rows(lo);
       wait_vmem();
       store_rows(0);
       __syncthreads();
-      if (lo < hi) load_tile(lo + 1, 1);
     }
     if (flo <= fhi) {  // masked tiles before and after the mask-free range
       run(std::true_type{}, lo, flo - 1);

@@ -152,6 +152,36 @@ __device__ inline void tile_load_lds(const T* base, int64_t ld, int nvalid, char
   }
 }
 
+// The copy of tile_load_lds in its PARTS separate instructions, so that a
+// software pipeline can issue them one at a time between its other work (a
+// burst of them stalls the issuing waves while the address unit drains
+// them).  Part p covers rows p * NT / CPR .. of the tile; with NT / CPR a
+// multiple of 16 every part has the same swizzle, so the parts differ only by
+// a row-stride offset.
+template <typename T, int D, int ROWS, int NT = 256>
+struct TileDma {
+  static constexpr int RB = D * (int)sizeof(T);
+  static constexpr int CPR = RB / 16;
+  static constexpr int PARTS = ROWS * CPR / NT;
+  static_assert((ROWS * CPR) % NT == 0 && (NT / CPR) % 16 == 0, "tile load mapping");
+  u32x4 rsrc;
+  uint32_t voff, vstep, dst;
+  __device__ void init(const T* base, int64_t ld, int nvalid, char* tile, int tid) {
+    const int64_t row_bytes = ld * (int64_t)sizeof(T);
+    nvalid = nvalid < ROWS ? nvalid : ROWS;
+    rsrc = buffer_rsrc(base, nvalid > 0 ? (uint32_t)((nvalid - 1) * row_bytes + RB) : 0u);
+    const int row = tid / CPR, pc = tid % CPR;
+    voff = (uint32_t)(row * row_bytes) + (uint32_t)((pc ^ tile_swz<RB>(row)) << 4);
+    vstep = (uint32_t)((NT / CPR) * row_bytes);
+    dst = __builtin_amdgcn_readfirstlane(lds_addr(tile) + (tid & ~63) * 16);
+  }
+  template <int P>
+  __device__ void issue() const {
+    static_assert(P < PARTS, "part");
+    dma16(rsrc, voff + P * vstep, dst + P * NT * 16);
+  }
+};
+
 // Contiguous copy of `bytes` (a multiple of 16, at most 1024) into LDS by the
 // first bytes/16 lanes of wave 0; bytes past `valid_bytes` read as zero.
 __device__ inline void span_load_lds(const void* base, uint32_t valid_bytes, int bytes, char* dst,
