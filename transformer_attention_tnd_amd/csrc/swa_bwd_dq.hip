@@ -230,6 +230,7 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_dq_kernel(BwdArgs a) {
     };
 
     start_copy(tile + 1, b ^ 1);
+    static_assert(COPY_EVERY * (2 * Dma::PARTS - 1) + 1 < NOPS + AHEAD, "every copy has a slot");
     static_for<NOPS + AHEAD>([&](auto sc) {
       constexpr int sl = decltype(sc)::value;
       // one copy instruction every COPY_EVERY slots from slot 1
