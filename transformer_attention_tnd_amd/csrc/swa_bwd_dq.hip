@@ -151,13 +151,9 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_dq_kernel(BwdArgs a) {
   // the copies of tile + 1 into slab b ^ 1.
   auto step = [&](auto mask_tag, int tile, int b) {
     constexpr bool kMask = decltype(mask_tag)::value;
-    // key 32 jb + 8 g + 4 h + e of the tile is allowed iff 32 jb + 8 g + e is in [rel_lo, rel_hi]
-    int rel_lo = 0, rel_hi = 0;
-    if constexpr (kMask) {
-      rel_lo = j_min - tile * BN - 4 * h;
-      rel_hi = j_max - tile * BN - 4 * h;
-      asm volatile("" : "+v"(rel_lo), "+v"(rel_hi));
-    }
+    // key 32 jb + 8 g + 4 h + e of the tile is allowed iff 32 jb + 8 g + e lies in the lane's range rg
+    LaneRange rg{0, 0u};
+    if constexpr (kMask) rg = lane_range(j_min - tile * BN - 4 * h, j_max - tile * BN - 4 * h, BN);
     op_t ring[RING];
     floatx16 s[2], dp[2];
     op_t sk[2][2];
@@ -201,7 +197,7 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_dq_kernel(BwdArgs a) {
       float p = __builtin_amdgcn_exp2f(fmaf(s[jb][r], c2, -lse));
       if constexpr (kMask) {
         const int rel = 32 * jb + 8 * (r >> 2) + (r & 3);
-        p = (rel >= rel_lo && rel <= rel_hi) ? p : 0.f;
+        p = in_range(rel, rg) ? p : 0.f;
       }
       s[jb][r] = p;
     };

@@ -197,13 +197,9 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
   // One query tile (slab b): also issues the copies of tile + 1 into slab b ^ 1
   auto step = [&](auto mask_tag, int tile, int b) {
     constexpr bool kMask = decltype(mask_tag)::value;
-    // row 32 qb + 8 g + 4 h + e is allowed iff 32 qb + 8 g + e is in [rel_lo, rel_hi]
-    int rel_lo = 0, rel_hi = 0;
-    if constexpr (kMask) {
-      rel_lo = i_min - tile * BM - 4 * h;
-      rel_hi = i_max - tile * BM - 4 * h;
-      asm volatile("" : "+v"(rel_lo), "+v"(rel_hi));
-    }
+    // row 32 qb + 8 g + 4 h + e is allowed iff 32 qb + 8 g + e lies in the lane's range rg
+    LaneRange rg{0, 0u};
+    if constexpr (kMask) rg = lane_range(i_min - tile * BM - 4 * h, i_max - tile * BM - 4 * h, BM);
     op_t ring[RING];
     floatx16 s[2], dp[2];
     floatx4 lv[2][4], dv4[2][4];
@@ -249,7 +245,7 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
       float p = __builtin_amdgcn_exp2f(fmaf(s[qb][r], c2, -lv[qb][g][e]));
       if constexpr (kMask) {
         const int rel = 32 * qb + 8 * g + e;
-        p = (rel >= rel_lo && rel <= rel_hi) ? p : 0.f;
+        p = in_range(rel, rg) ? p : 0.f;
       }
       s[qb][r] = p;
     };

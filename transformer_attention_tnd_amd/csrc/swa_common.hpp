@@ -285,4 +285,25 @@ __device__ inline bool allowed(int i, int j, int sq, int skv, int mode, int pre,
   return d >= -pre && d <= next;
 }
 
+// A lane's allowed element offsets within one tile of n elements, as
+// [lo, lo + w]: one subtract and one unsigned compare per element, all on the
+// vector ALU (no scalar combine of two compare masks).  An empty range is
+// lo = n, w = 0, which no offset in [0, n) passes.
+struct LaneRange {
+  int lo;
+  unsigned w;
+};
+__device__ inline LaneRange lane_range(int lo, int hi, int n) {
+  lo = lo < 0 ? 0 : lo;
+  hi = hi > n - 1 ? n - 1 : hi;
+  LaneRange r;
+  r.lo = hi < lo ? n : lo;
+  r.w = hi < lo ? 0u : (unsigned)(hi - lo);
+  asm volatile("" : "+v"(r.lo), "+v"(r.w));  // keep the per-lane form
+  return r;
+}
+__device__ inline bool in_range(int rel, const LaneRange& r) {
+  return (unsigned)(rel - r.lo) <= r.w;
+}
+
 }  // namespace swa

@@ -127,6 +127,14 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
     }
   }
   const float cs = kPos ? a.scale_log2 : 1.f;  // raw score -> exp2 units
+  // Keys allowed for this lane's row: j in [j_min, j_max] (empty past the end)
+  int j_min = 0, j_max = it.skv - 1;
+  if (a.mode != 0) {  // 64-bit: pre / next may be near the int range
+    const int64_t lo64 = (int64_t)qrow - it.band[0], hi64 = (int64_t)qrow + it.band[1];
+    j_min = lo64 < 0 ? 0 : (lo64 > it.skv ? it.skv : (int)lo64);
+    j_max = hi64 < j_max ? (hi64 < -1 ? -1 : (int)hi64) : j_max;
+  }
+  if (qrow >= it.sq) j_max = -1;
 
   // Dropout keep bits of this lane's row for the 64 keys of a tile: three
   // 32-bit words loaded in the matrix phase that forms the tile's scores,
@@ -221,12 +229,15 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
       for (int jb = 0; jb < NJB; ++jb) s[jb] *= a.scale_log2;
     }
     if constexpr (kMask) {
+      // key 32 jb + c_row(r, h) of the tile is allowed iff 32 jb + 8 (r / 4) + r % 4
+      // lies in the lane's range (the 4 h of c_row moved into the bounds)
+      const LaneRange rg = lane_range(j_min - tile * BN - 4 * h, j_max - tile * BN - 4 * h, BN);
 #pragma unroll
       for (int jb = 0; jb < NJB; ++jb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int j = tile * BN + 32 * jb + c_row(r, h);
-          s[jb][r] = allowed(qrow, j, it.sq, it.skv, a.mode, it.band[0], it.band[1]) ? s[jb][r] : -INFINITY;
+          const int rel = 32 * jb + 8 * (r >> 2) + (r & 3);
+          s[jb][r] = in_range(rel, rg) ? s[jb][r] : -INFINITY;
         }
       }
     }
