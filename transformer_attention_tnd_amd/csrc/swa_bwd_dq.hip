@@ -8,7 +8,9 @@
 // lse2 and D are per-lane scalars) and its dQ^T accumulator, and walks the
 // key tiles (64 keys) of the band: P = exp2(S^T c - lse2), dS = P (dP - D),
 // dQ^T += K^T dS^T with K^T from the key tile through transposing LDS reads.
-// dq = scale dQ is written once, in the input type.  The products of a tile
+// dq = scale dQ is written once, in the input type.  It runs first: its
+// prologue also computes D = rowsum(dY o O) and lse2 of its rows (the
+// backward preprocess) and stores them for the dK/dV kernel.  The products of a tile
 // form one software pipeline (see swa_pipe.hpp); this file is compiled with
 // the matrix-core results in ordinary vector registers, so the softmax
 // reads them without copies.
@@ -70,20 +72,24 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_dq_kernel(BwdArgs a) {
   const int flo = it.full[0] & 0xffff, fhi = (it.full[0] >> 16) & 0xffff;
   const float c2 = a.scale_log2;
 
-  // B operands of S^T and dP^T: lane (column qrow) holds Q[qrow][16t + 8h + e], dY likewise
-  op_t qf[DSTEPS], yf[DSTEPS];
+  // B operands of S^T and dP^T: lane (column qrow) holds Q[qrow][16t + 8h + e], dY likewise;
+  // O likewise, and the row's statistics, for D and lse2 (row_stats)
+  op_t qf[DSTEPS], yf[DSTEPS], of[DSTEPS];
   float lse = INFINITY, drow = 0.f;  // this row's lse2 and D (rows past the end: P = 0)
+  float smx, ssm;
+  const bool row_ok = qrow < it.sq;
   {
-    const bool ok = qrow < it.sq;
-    const int64_t off = (int64_t)(ok ? qrow : 0) * ld + 8 * h;
+    const int64_t row = (int64_t)(row_ok ? qrow : 0);
+    const int64_t off = row * ld + 8 * h;
+    const bf16* og = static_cast<const bf16*>(a.out) + (int64_t)it.q_base * ld + head * D;
+    const int64_t so = (((int64_t)it.q_base + row) * a.num_heads + head) * 8;
+    smx = a.smax[so];
+    ssm = a.ssum[so];
 #pragma unroll
     for (int t = 0; t < DSTEPS; ++t) {
-      qf[t] = ok ? M::load(qg + off + 16 * t) : op_t{};
-      yf[t] = ok ? M::load(dyg + off + 16 * t) : op_t{};
-    }
-    if (ok) {
-      lse = a.lse2[(int64_t)head * a.t_q + it.q_base + qrow];
-      drow = a.drow[(int64_t)head * a.t_q + it.q_base + qrow];
+      qf[t] = row_ok ? M::load(qg + off + 16 * t) : op_t{};
+      yf[t] = row_ok ? M::load(dyg + off + 16 * t) : op_t{};
+      of[t] = row_ok ? M::load(og + off + 16 * t) : op_t{};
     }
   }
   // Keys allowed for this lane's row: j in [j_min, j_max] (empty past the end)
@@ -99,8 +105,30 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_dq_kernel(BwdArgs a) {
   // dP - D and dS = P (dP - D) is one multiply (with dropout, dS = P (Z dP / kp
   // - D) needs dP alone: the chains start from zero)
   floatx16 ndrow;
+  // D = rowsum(dY o O) (fp32 products; this lane's half of the row plus the
+  // other half from lane l ^ 32, which holds the same row) and lse2 of this
+  // lane's row, stored for the dK/dV kernel (the backward preprocess)
+  auto row_stats = [&]() {
+    float dpart = 0.f;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) ndrow[r] = kDrop ? 0.f : -drow;
+    for (int t = 0; t < DSTEPS; ++t) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dpart += static_cast<float>(yf[t][e]) * static_cast<float>(of[t][e]);
+    }
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(dpart), __float_as_uint(dpart),
+                                                     false, false);
+    if (row_ok) {
+      drow = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      lse = (ssm > 0.f && smx > -INFINITY) ? smx * 1.4426950408889634f + log2f(ssm) : INFINITY;
+      if (h == 0) {
+        const int64_t at = (int64_t)head * a.t_q + it.q_base + qrow;
+        a.drow[at] = drow;
+        a.lse2[at] = lse;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ndrow[r] = kDrop ? 0.f : -drow;
+  };
 
   // Dropout keep bits of this lane's row for the 64 keys of a tile (three
   // 32-bit words, funnel-shifted in the softmax; bit k = key 64 t + k).  The
@@ -246,6 +274,7 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_dq_kernel(BwdArgs a) {
     });
   };
 
+  // the first tile's copies go out before the row statistics wait for their loads
   if (lo <= hi) {
     start_copy(lo, 0);
     static_for<Dma::PARTS>([&](auto pc) {
@@ -253,6 +282,9 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_dq_kernel(BwdArgs a) {
       cp_v.template issue<decltype(pc)::value>();
     });
     load_mask(lo);
+  }
+  row_stats();
+  if (lo <= hi) {
     wait_vmem();
     __syncthreads();
   }

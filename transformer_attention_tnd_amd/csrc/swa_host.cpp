@@ -613,12 +613,14 @@ swa_status swa_backward_ex(const void* q, const void* k, const void* v, const vo
   float* lse2 = reinterpret_cast<float*>(ws + L.lse2);
   float* dq_acc = two_pass ? nullptr : reinterpret_cast<float*>(ws + L.dq_acc);
   int e = 0;
-  BwdPreArgs pa{dy, out, softmax_max, softmax_sum, drow, lse2, dq_acc, t_q * num_heads,
-                static_cast<int32_t>(num_heads), static_cast<int32_t>(t_q)};
-  if ((e = timed_launch(K_BWD_PRE, stream, [&] {
-         return launch_bwd_pre(pa, dtype, static_cast<int>(head_dim), stream);
-       })) != 0)
-    return fail(SWA_ERR_HIP, hip_error_string(e));
+  if (!two_pass) {  // fp32: D, lse2 and the zeroed dq accumulator from the preprocess kernel
+    BwdPreArgs pa{dy, out, softmax_max, softmax_sum, drow, lse2, dq_acc, t_q * num_heads,
+                  static_cast<int32_t>(num_heads), static_cast<int32_t>(t_q)};
+    if ((e = timed_launch(K_BWD_PRE, stream, [&] {
+           return launch_bwd_pre(pa, dtype, static_cast<int>(head_dim), stream);
+         })) != 0)
+      return fail(SWA_ERR_HIP, hip_error_string(e));
+  }
   BwdArgs a;
   a.q = q;
   a.k = k;
@@ -626,6 +628,9 @@ swa_status swa_backward_ex(const void* q, const void* k, const void* v, const vo
   a.dy = dy;
   a.drow = drow;
   a.lse2 = lse2;
+  a.out = out;
+  a.smax = softmax_max;
+  a.ssum = softmax_sum;
   a.dq_acc = dq_acc;
   a.dq = dq;
   a.dk = dk;
@@ -639,6 +644,18 @@ swa_status swa_backward_ex(const void* q, const void* k, const void* v, const vo
   a.scale = static_cast<float>(scale);
   a.scale_log2 = static_cast<float>(scale * 1.4426950408889634);
   a.mode = static_cast<int32_t>(sparse_mode);
+  // bf16: the dQ kernel first (it also writes D and lse2 of every row of every
+  // sequence: one item per block of query rows, even when the block attends
+  // no key), then the dK/dV kernel, which reads them
+  if (two_pass && !dq_items.empty()) {
+    BwdArgs b = a;
+    b.items = reinterpret_cast<const Item*>(ws + L.items) + n_kv_items;
+    b.n_items = static_cast<int32_t>(dq_items.size());
+    if ((e = timed_launch(K_BWD_DQ, stream, [&] {
+           return launch_bwd_dq(b, static_cast<int>(head_dim), stream);
+         })) != 0)
+      return fail(SWA_ERR_HIP, hip_error_string(e));
+  }
   if (n_kv_items > 0) {
     if ((e = timed_launch(K_BWD, stream, [&] {
            return launch_backward(a, dtype, static_cast<int>(head_dim), stream);
@@ -646,15 +663,6 @@ swa_status swa_backward_ex(const void* q, const void* k, const void* v, const vo
       return fail(SWA_ERR_HIP, hip_error_string(e));
   }
   if (two_pass) {
-    if (!dq_items.empty()) {
-      BwdArgs b = a;
-      b.items = reinterpret_cast<const Item*>(ws + L.items) + n_kv_items;
-      b.n_items = static_cast<int32_t>(dq_items.size());
-      if ((e = timed_launch(K_BWD_DQ, stream, [&] {
-             return launch_bwd_dq(b, static_cast<int>(head_dim), stream);
-           })) != 0)
-        return fail(SWA_ERR_HIP, hip_error_string(e));
-    }
     if (end_q < t_q) {  // tokens after the last sequence
       FillArgs f{dq, static_cast<int64_t>(elem_bytes(dtype)), num_heads * head_dim, end_q, t_q,
                  nullptr, nullptr, 0};

@@ -106,8 +106,13 @@ struct BwdArgs {
   const void* k;
   const void* v;
   const void* dy;
-  const float* drow;  // [N, t_q]
-  const float* lse2;  // [N, t_q]
+  float* drow;        // [N, t_q]: D = rowsum(dY o O)
+  float* lse2;        // [N, t_q]: softmax_max log2(e) + log2(softmax_sum)
+  // bf16 two-pass: the dQ kernel (launched first) computes D and lse2 of its
+  // rows from out and the statistics and stores them for the dK/dV kernel
+  const void* out;    // [t_q, N, D]
+  const float* smax;  // [t_q, N, 8]
+  const float* ssum;  // [t_q, N, 8]
   float* dq_acc;      // fp32 one-pass backward only
   void* dq;           // bf16 dQ kernel only
   void* dk;
