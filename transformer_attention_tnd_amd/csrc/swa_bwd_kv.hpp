@@ -142,7 +142,6 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db) tr_offsets<RB>(lane, db, otr[db][0], otr[db][1]);
 
-  float sreg = 0.f;
   // dropout: thread (row = tid % 64, word = tid / 64) fetches the 32 keep bits
   // of its row for keys 32 word .. 32 word + 31 of the block (two words and a
   // shift, joined when they are stored)
@@ -158,14 +157,18 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
     cp_q.init(qg + (int64_t)tile * BM * ld, ld, nvalid, slab, tid);
     cp_dy.init(dyg + (int64_t)tile * BM * ld, ld, nvalid, slab + QTB, tid);
   };
-  // lse2 / D (and keep bits) of the tile's rows into registers, for store_rows
-  auto load_rows = [&](int tile) {
-    if (tid < 2 * BM) {
-      const int row = tid & (BM - 1), i = tile * BM + row;
-      if (tid < BM)
-        sreg = i < it.sq ? lse_g[i] : INFINITY;
-      else
-        sreg = i < it.sq ? drow_g[i] : 0.f;
+  // lse2 / D of the tile's rows go straight into LDS slot b (wave 0: lse2,
+  // wave 1: D; one 64-lane dword copy each, rows past the sequence read as
+  // zero: the tiles that hold such rows are masked tiles, where their P is
+  // zero whatever lse2 holds), waited for with the tile copies; with dropout
+  // the keep bits of the rows go through registers (store_rows)
+  auto load_rows = [&](int tile, int b) {
+    if (w < 2) {
+      const int nv = it.sq - tile * BM;
+      const uint32_t nrec = nv <= 0 ? 0u : (uint32_t)(nv < BM ? nv : BM) * 4u;
+      const float* src = (w == 0 ? lse_g : drow_g) + (int64_t)tile * BM;
+      const uint32_t dst = lds_addr(w == 0 ? (const void*)lse_s[b] : (const void*)drow_s[b]);
+      dma4(buffer_rsrc(src, nrec), (uint32_t)lane * 4u, __builtin_amdgcn_readfirstlane(dst));
     }
     if constexpr (kDrop) {
       const int row = tid & (BM - 1), i = tile * BM + row;
@@ -183,10 +186,6 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
     });
   };
   auto store_rows = [&](int b) {
-    if (tid < BM)
-      reinterpret_cast<float*>(lse_s[b])[tid] = sreg;
-    else if (tid < 2 * BM)
-      reinterpret_cast<float*>(drow_s[b])[tid - BM] = sreg;
     if constexpr (kDrop)
       mask_s[b * 4 * BM + (tid / BM) * BM + (tid & (BM - 1))] =
           __builtin_amdgcn_alignbit(mreg[1], mreg[0], msh);
@@ -301,7 +300,7 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
     static_assert(COPY_EVERY * (2 * Dma::PARTS - 1) + 1 < NOPS + AHEAD, "every copy has a slot");
     static_for<NOPS + AHEAD>([&](auto sc) {
       constexpr int sl = decltype(sc)::value;
-      if constexpr (sl == 0) load_rows(tile + 1);
+      if constexpr (sl == 0) load_rows(tile + 1, b ^ 1);
       // one copy instruction every COPY_EVERY slots from slot 1
       if constexpr (sl % COPY_EVERY == 1 && sl / COPY_EVERY < 2 * Dma::PARTS) {
         constexpr int pt = sl / COPY_EVERY;
@@ -355,8 +354,18 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
     if (lo <= hi) {
       start_copy(lo, 0);
       copy_all();
-      load_rows(lo);
-      wait_vmem();
+      load_rows(lo, 0);
+    }
+    wait_vmem();
+    // the K / V row loads are complete: an empty use of each register lets
+    // the compiler's wait tracking know it too, so that it does not count
+    // them as outstanding (and wait for the tile copies with them) in the
+    // first products of every tile
+    if constexpr (!kGroups) {
+#pragma unroll
+      for (int t = 0; t < DSTEPS; ++t) asm volatile("" : : "a"(kr[t]), "a"(vr[t]));
+    }
+    if (lo <= hi) {
       store_rows(0);
       __syncthreads();
     }

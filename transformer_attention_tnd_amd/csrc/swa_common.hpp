@@ -128,6 +128,15 @@ __device__ inline void dma16(u32x4 rsrc, uint32_t voff, uint32_t lds_base) {
                : "memory", "m0");
 }
 
+// 4 bytes per lane from rsrc + voff into LDS at lds_base + 4 * lane (the
+// same asynchronous global->LDS copy, one dword per lane).
+__device__ inline void dma4(u32x4 rsrc, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(lds_base), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
 // Copy rows [0, ROWS) of a row-major [rows, ld] slice starting at `base`
 // into a swizzled LDS tile (no registers involved).  Rows >= nvalid read as
 // zero.  All NT threads of the workgroup take part.
