@@ -303,8 +303,23 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
       otr[db][1] = tile_off<RB>(4 * h + (s16 >> 2) + 8, col2);
     }
   }
+  // bf16 with three buffers and no dropout: each group copies one tile per
+  // step, part by part from the slots of its matrix phase (a burst of copy
+  // instructions holds the issuing waves while the address unit drains it):
+  // group 0 the K tile two steps ahead, group 1 the V tile one step ahead.
+  // Past the range the copy reads nothing and writes zeros into the free
+  // buffer, so every wave issues the same number of copies in every step.
+  constexpr bool kSpread = sizeof(T) == 2 && NBUF == 3 && !kDrop;
+  using Dma = TileDma<bf16, D, BN, 256>;  // (used by the bf16 instantiations only)
+  constexpr int COPY_EVERY = 4;  // pipeline slots between copy instructions
+  Dma cp;
+  auto copy_burst = [&]() {
+    static_for<Dma::PARTS>([&](auto pc) { cp.template issue<decltype(pc)::value>(); });
+  };
   auto pipeline = [&](auto first_c, auto last_c, const char* kt, const char* vt) {
     constexpr int FIRST = decltype(first_c)::value, LAST = decltype(last_c)::value;
+    static_assert(!kSpread || COPY_EVERY * (Dma::PARTS - 1) + 1 < LAST - FIRST + AHEAD,
+                  "every copy has a slot");
     op_t ring[RING];
     auto read = [&](auto ic) {
       constexpr int i = decltype(ic)::value;
@@ -336,6 +351,8 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
     };
     static_for<LAST - FIRST + AHEAD>([&](auto sc) {
       constexpr int sl = decltype(sc)::value;
+      if constexpr (kSpread && sl % COPY_EVERY == 1 && sl / COPY_EVERY < Dma::PARTS)
+        cp.template issue<sl / COPY_EVERY>();
       if constexpr (sl < LAST - FIRST) read(std::integral_constant<int, FIRST + sl>{});
       if constexpr (sl >= AHEAD) mfma(std::integral_constant<int, FIRST + sl - AHEAD>{});
       __builtin_amdgcn_sched_barrier(0);
@@ -364,6 +381,8 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
         pipeline(Z{}, P{}, kt, vt);
       else if (do_s)
         pipeline(P{}, E{}, kt, vt);
+      else if constexpr (kSpread)
+        copy_burst();
     } else {
       if (do_pv && do_s) {
         pv(vt);
@@ -403,8 +422,15 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
       // two buffers: K(t+1), V(t) (used in the next step)
       const bool ck = NBUF == 3 ? t + 2 <= hi : t + 1 <= hi;
       const bool cv = NBUF == 3 ? t + 1 <= hi : t <= hi;
-      if (ck) load_k(NBUF == 3 ? t + 2 : t + 1, (k + (NBUF == 3 ? 2 : 1)) % NBUF);
-      if (cv) load_v(NBUF == 3 ? t + 1 : t, (k + (NBUF == 3 ? 1 : 0)) % NBUF);
+      if constexpr (kSpread) {
+        const int tt = g == 0 ? t + 2 : t + 1;
+        const bf16* src = reinterpret_cast<const bf16*>(g == 0 ? kg : vg) + (int64_t)tt * BN * ldkv;
+        char* dst = g == 0 ? kbuf0 + ((k + 2) % NBUF) * TB : vbuf0 + ((k + 1) % NBUF) * TB;
+        cp.init(src, ldkv, tt <= hi ? it.skv - tt * BN : 0, dst, tid & 255);
+      } else {
+        if (ck) load_k(NBUF == 3 ? t + 2 : t + 1, (k + (NBUF == 3 ? 2 : 1)) % NBUF);
+        if (cv) load_v(NBUF == 3 ? t + 1 : t, (k + (NBUF == 3 ? 1 : 0)) % NBUF);
+      }
       // half A
       if (g == 0)
         m_phase(t, k);
@@ -418,7 +444,9 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
         m_phase(t, k);
       // the tiles of the next step have landed (with three buffers, the
       // copies issued in this step may still be in flight)
-      if (NBUF == 2 || (!ck && !cv))
+      if constexpr (kSpread)  // this step's copies (one tile per wave) stay in flight
+        __builtin_amdgcn_s_waitcnt(0x0F70 | Dma::PARTS);
+      else if (NBUF == 2 || (!ck && !cv))
         wait_vmem();
       else if (ck && cv)
         __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * NC));
@@ -426,6 +454,7 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
         __builtin_amdgcn_s_waitcnt(0x0F70 | NC);
       __syncthreads();
     }
+    if constexpr (kSpread) wait_vmem();  // the last step's copies (into free buffers)
   }
 
   // epilogue: normalise, store out and the statistics of this lane's row
