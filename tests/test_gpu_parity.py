@@ -53,6 +53,9 @@ CUSTOM = {
                                            sparse_mode=4, pre_tokens=40, next_tokens=8,
                                            trailing=2, extra_tokens=5),
     "bf16_zero_length_sequences": dict(lengths_q=[0, 64, 0, 100], num_heads=2, head_dim=64),
+    # a sequence with query rows but no keys: its rows attend nothing (out = 0, dq = 0)
+    "bf16_d128_no_keys_for_a_sequence": dict(lengths_q=[140, 100], lengths_kv=[0, 120],
+                                             num_heads=2, head_dim=128),
     "bf16_empty_rows_negative_next": dict(lengths_q=[150, 90], num_heads=2, head_dim=128,
                                           sparse_mode=4, pre_tokens=70, next_tokens=-5),
     "bf16_narrow_band_negative_pre": dict(lengths_q=[260], num_heads=1, head_dim=128,
