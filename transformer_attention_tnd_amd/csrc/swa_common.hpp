@@ -83,14 +83,16 @@ __device__ __host__ constexpr inline int row_of_slot(int p) {
 
 // Swizzled row-major LDS tiles.  Rows are stored back to back with no
 // padding; the 16-byte chunk c of row r sits at chunk c ^ tile_swz<RB>(r).
-// Rows of 256 bytes or more use a 4-bit permutation, so that 16 consecutive
-// rows reading one logical chunk (a 128-bit operand read) land on 16
-// distinct bank groups; 128-byte rows (8 chunks) use a 3-bit one.  Both keep
-// the 4 rows of a transposing 64-bit read (an aligned 32-byte pair per row)
-// on distinct bank groups.
+// Rows of 256 bytes or more use s(r) = 4 (r mod 4) + (r / 4 mod 4): a
+// permutation of 16 consecutive rows, so that 16 rows reading one logical
+// chunk (a 128-bit operand read) land on 16 distinct bank groups, and one
+// that puts the 4 rows of each half-wave of a transposing 64-bit read (two
+// aligned 32-byte pairs per row, from two 16-lane groups) in 4 different
+// aligned groups of 4 chunks, so the half-wave covers all 64 banks once.
+// 128-byte rows (8 chunks) use a 3-bit permutation.
 template <int RB>
 __device__ __host__ constexpr inline int tile_swz(int r) {
-  return RB >= 256 ? (((r & 7) << 1) | ((r >> 3) & 1)) : (((r & 3) << 1) | ((r >> 2) & 1));
+  return RB >= 256 ? (((r & 3) << 2) | ((r >> 2) & 3)) : (((r & 3) << 1) | ((r >> 2) & 1));
 }
 template <int RB>
 __device__ __host__ constexpr inline int tile_off(int r, int byte) {
