@@ -122,7 +122,7 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_dq_kernel(BwdArgs a) {
       lse = (ssm > 0.f && smx > -INFINITY) ? smx * 1.4426950408889634f + log2f(ssm) : INFINITY;
       if (h == 0) {
         const int64_t at = (int64_t)head * a.t_q + it.q_base + qrow;
-        a.drow[at] = drow;
+        a.drow[at] = -drow;  // the dK/dV kernel starts its dP chains from -D
         a.lse2[at] = lse;
       }
     }

@@ -69,7 +69,7 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
 
   __shared__ __attribute__((aligned(1024))) char lds[2 * SLAB];
   __shared__ floatx4 lse_s[2][BM / 4];   // lse2 of the tile's rows
-  __shared__ floatx4 drow_s[2][BM / 4];  // D of the tile's rows
+  __shared__ floatx4 drow_s[2][BM / 4];  // -D of the tile's rows
   // dropout keep bits of the tile: [slot][key word kw / 32 of the block][row],
   // bit c of a word = key 32 * word + c
   __shared__ uint32_t mask_s[kDrop ? 2 * 4 * BM : 1];
@@ -201,7 +201,12 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
     if constexpr (kMask) rg = lane_range(i_min - tile * BM - 4 * h, i_max - tile * BM - 4 * h, BM);
     op_t ring[RING];
     floatx16 s[2], dp[2];
-    floatx4 lv[2][4], dv4[2][4];
+    floatx4 lv[2][4], dv4[2][4];  // lse2 and -D of 4 rows (dv4: dropout only)
+    floatx16 nd[2];  // -D of the rows of accumulator registers 0..15 of block qb
+    // Without dropout (and with one query head per workgroup: the grouped
+    // build keeps its accumulators apart) the dP chain starts from -D, so
+    // that the accumulator ends as dP - D and dS = P (dP - D) is one multiply
+    constexpr bool kNegD = !kDrop && !kGroups;
     uint32_t mk[2][4][4];  // keep words of rows 32 qb + 8 g + 4 h + e (this wave's keys)
     op_t pk[2][2], sk[2][2];
 
@@ -225,7 +230,7 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
         if constexpr (i % 2 == 0)
           s[qb] = M::mma(x, kr[t], t == 0 ? floatx16{} : s[qb]);
         else
-          dp[qb] = M::mma(x, vr[t], t == 0 ? floatx16{} : dp[qb]);
+          dp[qb] = M::mma(x, vr[t], t == 0 ? (kNegD ? nd[qb] : floatx16{}) : dp[qb]);
       } else {
         constexpr int j = i - G_V0, qb = j / NV, jj = j % NV;
         constexpr int t2 = jj / (2 * NDB), db = (jj / 2) % NDB;
@@ -237,7 +242,8 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
     };
     // Softmax of accumulator register r of block qb in two stages one slot
     // apart (so no instruction waits on the one before it):
-    //   A: P = exp2(s c - lse2), masked;   B: dS = P (dP - D), and each
+    //   A: P = exp2(s c - lse2), masked;   B: dS = P (dP - D) (with kNegD the
+    //   accumulator already holds dP - D), and each
     //   completed pair of P and dS is rounded into the dV / dK operands.
     auto soft_a = [&](int qb, int r) {
       const int g = r >> 2, e = r & 3;
@@ -252,10 +258,12 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
       if constexpr (kDrop) {
         // dV takes P Z / kp, dS = P (Z dP / kp - D)
         const bool kept = (mk[qb][r >> 2][r & 3] >> c) & 1u;
-        dp[qb][r] = s[qb][r] * ((kept ? dp[qb][r] * a.drop.rkp : 0.f) - dv4[qb][r >> 2][r & 3]);
+        dp[qb][r] = s[qb][r] * ((kept ? dp[qb][r] * a.drop.rkp : 0.f) + dv4[qb][r >> 2][r & 3]);
         s[qb][r] = kept ? s[qb][r] * a.drop.rkp : 0.f;
+      } else if constexpr (kNegD) {
+        dp[qb][r] = s[qb][r] * dp[qb][r];
       } else {
-        dp[qb][r] = s[qb][r] * (dp[qb][r] - dv4[qb][r >> 2][r & 3]);
+        dp[qb][r] = s[qb][r] * (dp[qb][r] + dv4[qb][r >> 2][r & 3]);
       }
       if (r & 1) {
         pk[qb][r >> 3][(r & 7) - 1] = static_cast<bf16>(s[qb][r - 1]);
@@ -275,7 +283,8 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
           if (m == kv_soft_slot(qb, 4 * g) - 2) {
             const int off = olr + (32 * qb + 8 * g) * 4;
             lv[qb][g] = *reinterpret_cast<const floatx4*>(reinterpret_cast<const char*>(lse_s) + off);
-            dv4[qb][g] = *reinterpret_cast<const floatx4*>(reinterpret_cast<const char*>(drow_s) + off);
+            if constexpr (!kNegD)
+              dv4[qb][g] = *reinterpret_cast<const floatx4*>(reinterpret_cast<const char*>(drow_s) + off);
             if constexpr (kDrop) {
               typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
               const u32x4_t m4 = *reinterpret_cast<const u32x4_t*>(
@@ -301,6 +310,18 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
     static_for<NOPS + AHEAD>([&](auto sc) {
       constexpr int sl = decltype(sc)::value;
       if constexpr (sl == 0) load_rows(tile + 1, b ^ 1);
+      // -D of block qb's rows, three slots before its first dP product
+      // (product NS qb + 1, issued at slot NS qb + 1 + AHEAD)
+      if constexpr (kNegD && (sl == AHEAD - 2 || sl == NS + AHEAD - 2)) {
+        constexpr int qb = sl < NS ? 0 : 1;
+        const char* base = reinterpret_cast<const char*>(drow_s) + olr + 32 * qb * 4;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const floatx4 f = *reinterpret_cast<const floatx4*>(base + 8 * g * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) nd[qb][4 * g + e] = f[e];
+        }
+      }
       // one copy instruction every COPY_EVERY slots from slot 1
       if constexpr (sl % COPY_EVERY == 1 && sl / COPY_EVERY < 2 * Dma::PARTS) {
         constexpr int pt = sl / COPY_EVERY;

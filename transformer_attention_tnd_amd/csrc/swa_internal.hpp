@@ -106,7 +106,8 @@ struct BwdArgs {
   const void* k;
   const void* v;
   const void* dy;
-  float* drow;        // [N, t_q]: D = rowsum(dY o O)
+  float* drow;        // [N, t_q]: D = rowsum(dY o O) (fp32 one-pass); -D (bf16
+                      // two-pass: written by the dQ kernel, read by the dK/dV kernel)
   float* lse2;        // [N, t_q]: softmax_max log2(e) + log2(softmax_sum)
   // bf16 two-pass: the dQ kernel (launched first) computes D and lse2 of its
   // rows from out and the statistics and stores them for the dK/dV kernel
