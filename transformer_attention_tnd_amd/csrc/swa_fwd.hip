@@ -25,9 +25,10 @@
 //
 // Data movement: K and V tiles of 64 keys go from HBM straight into
 // swizzled row-major LDS tiles (buffer loads with the LDS destination, rows
-// past the sequence read as zero).  They rotate through three buffers each
-// (two when three do not fit), so the copy of a tile is issued two steps
-// before its first use.  V^T operands come from the row-major V tile through
+// past the sequence read as zero).  They rotate through four buffers each in
+// the bf16 kernels without dropout, whose copies go out part by part from the
+// matrix phases, so a tile's copy has two steps to land; otherwise three
+// (two when three do not fit).  V^T operands come from the row-major V tile through
 // transposing LDS reads.  The matrix phase (bf16) is one software pipeline of
 // its products with the LDS operands read a few products ahead; it runs at
 // raised wave priority.
@@ -88,9 +89,12 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
   constexpr float kRescale = 8.f;         // exp2-domain slack before moving the reference
   static_assert(HALF == 128 && BN == 64, "two groups of 4 waves x 32 rows; 64-key tiles");
 
-  // K and V tiles rotate through NBUF buffers each (three when they fit:
-  // the copy of a tile then lands a full step before its first use)
-  constexpr int NBUF = 6 * TB <= 160 * 1024 ? 3 : 2;
+  // K and V tiles rotate through NBUF buffers each: four for the bf16
+  // kernels without dropout, whose copies are issued from the matrix phases
+  // (the copy of a tile then has two steps to land), else three when they
+  // fit (one step), else two
+  constexpr bool kSpreadable = sizeof(T) == 2 && !kDrop;
+  constexpr int NBUF = kSpreadable && 8 * TB <= 160 * 1024 ? 4 : 6 * TB <= 160 * 1024 ? 3 : 2;
   __shared__ __attribute__((aligned(1024))) char lds[2 * NBUF * TB];  // K[NBUF] V[NBUF]
   char* const kbuf0 = lds;
   char* const vbuf0 = lds + NBUF * TB;
@@ -303,13 +307,13 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
       otr[db][1] = tile_off<RB>(4 * h + (s16 >> 2) + 8, col2);
     }
   }
-  // bf16 with three buffers and no dropout: each group copies one tile per
-  // step, part by part from the slots of its matrix phase (a burst of copy
-  // instructions holds the issuing waves while the address unit drains it):
-  // group 0 the K tile two steps ahead, group 1 the V tile one step ahead.
+  // bf16 without dropout: each group copies one tile per step, part by part
+  // from the slots of its matrix phase (a burst of copy instructions holds
+  // the issuing waves while the address unit drains it): group 0 the K tile
+  // NBUF - 1 steps ahead, group 1 the V tile NBUF - 2 steps ahead.
   // Past the range the copy reads nothing and writes zeros into the free
   // buffer, so every wave issues the same number of copies in every step.
-  constexpr bool kSpread = sizeof(T) == 2 && NBUF == 3 && !kDrop;
+  constexpr bool kSpread = kSpreadable && NBUF >= 3;
   using Dma = TileDma<bf16, D, BN, 256>;  // (used by the bf16 instantiations only)
   constexpr int COPY_EVERY = 4;  // pipeline slots between copy instructions
   Dma cp;
@@ -407,11 +411,14 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
   // copy instructions per thread for one K or V tile
   constexpr int NC = BN * (RB / 16) / NT;
   static_assert(2 * NC <= 15, "copy batch fits the wait immediate");
+  static_assert(!kSpread || (NBUF - 2) * Dma::PARTS <= 15, "copies in flight fit the wait immediate");
   if (lo <= hi) {
     load_k(lo, 0);
-    if (NBUF == 3) {
-      if (lo + 1 <= hi) load_k(lo + 1, 1);
-      load_v(lo, 0);
+    if (NBUF >= 3) {  // K(lo .. lo + NBUF - 2), V(lo .. lo + NBUF - 3)
+      for (int j = 1; j <= NBUF - 2; ++j)
+        if (lo + j <= hi) load_k(lo + j, j);
+      for (int j = 0; j <= NBUF - 3; ++j)
+        if (lo + j <= hi) load_v(lo + j, j);
     }
     wait_vmem();
     __syncthreads();
@@ -423,9 +430,11 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
       const bool ck = NBUF == 3 ? t + 2 <= hi : t + 1 <= hi;
       const bool cv = NBUF == 3 ? t + 1 <= hi : t <= hi;
       if constexpr (kSpread) {
-        const int tt = g == 0 ? t + 2 : t + 1;
+        // K(t + NBUF - 1) into the buffer of K(t - 1), V(t + NBUF - 2) into
+        // that of V(t - 2): both last read in the previous step
+        const int tt = g == 0 ? t + NBUF - 1 : t + NBUF - 2;
         const bf16* src = reinterpret_cast<const bf16*>(g == 0 ? kg : vg) + (int64_t)tt * BN * ldkv;
-        char* dst = g == 0 ? kbuf0 + ((k + 2) % NBUF) * TB : vbuf0 + ((k + 1) % NBUF) * TB;
+        char* dst = g == 0 ? kbuf0 + ((k + NBUF - 1) % NBUF) * TB : vbuf0 + ((k + NBUF - 2) % NBUF) * TB;
         cp.init(src, ldkv, tt <= hi ? it.skv - tt * BN : 0, dst, tid & 255);
       } else {
         if (ck) load_k(NBUF == 3 ? t + 2 : t + 1, (k + (NBUF == 3 ? 2 : 1)) % NBUF);
@@ -444,8 +453,8 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
         m_phase(t, k);
       // the tiles of the next step have landed (with three buffers, the
       // copies issued in this step may still be in flight)
-      if constexpr (kSpread)  // this step's copies (one tile per wave) stay in flight
-        __builtin_amdgcn_s_waitcnt(0x0F70 | Dma::PARTS);
+      if constexpr (kSpread)  // the copies of the last NBUF - 2 steps (one tile per wave each) stay in flight
+        __builtin_amdgcn_s_waitcnt(0x0F70 | ((NBUF - 2) * Dma::PARTS));
       else if (NBUF == 2 || (!ck && !cv))
         wait_vmem();
       else if (ck && cv)
