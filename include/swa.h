@@ -106,8 +106,8 @@ swa_status swa_forward_workspace_size(int64_t num_seqs, int64_t t_q, int64_t t_k
                                       size_t* bytes);
 
 /* Device workspace bytes that swa_backward needs: the tile schedules, the
- * row terms D = rowsum(dY * out) and lse2, and the fp32 dq accumulator
- * [t_q, num_heads, head_dim] (used by fp32 inputs only). */
+ * row terms D = rowsum(dY * out) (stored negated for bf16) and lse2, and the
+ * fp32 dq accumulator [t_q, num_heads, head_dim] (used by fp32 inputs only). */
 swa_status swa_backward_workspace_size(int64_t num_seqs, int64_t t_q, int64_t t_kv,
                                        int64_t num_heads, int64_t head_dim, int32_t dtype,
                                        size_t* bytes);
@@ -132,7 +132,9 @@ swa_status swa_forward(const void* q, const void* k, const void* v,
  * FlashAttentionScoreGrad article (两趟循环结构): one kernel for dK/dV over
  * key blocks and one for dQ over query blocks, each recomputing P and dS, with
  * no atomics, so every output is bitwise reproducible (the deterministic mode
- * of the explainer, section 6.1).  fp32 inputs run one pass and accumulate dq
+ * of the explainer, section 6.1); the dQ kernel runs first and also forms the
+ * row terms D and lse2 that the dK/dV kernel reads.  fp32 inputs run a
+ * preprocess kernel for those terms, then one pass that accumulates dq
  * with fp32 atomics, so its last bits may differ from run to run (the pages'
  * default, explainer section 6.1). */
 swa_status swa_backward(const void* q, const void* k, const void* v, const void* dy,
@@ -214,9 +216,9 @@ swa_status swa_debug_tile_schedule(const int64_t* cu_seqlens_q, const int64_t* c
  * kernel the library launches is bracketed by two HIP events recorded on its
  * stream.  swa_profile_read waits for the recorded launches of one kernel
  * kind, returns their summed duration (ms) and count, and forgets them.
- * Kernel kinds: 0 forward, 1 backward preprocess, 2 backward main (dK/dV for
- * bf16, one pass for fp32), 3 dq finalize (fp32), 4 zero fill, 5 backward dQ
- * (bf16).  Not thread-safe across concurrent streams
+ * Kernel kinds: 0 forward, 1 backward preprocess (fp32), 2 backward main
+ * (dK/dV for bf16, one pass for fp32), 3 dq finalize (fp32), 4 zero fill,
+ * 5 backward dQ with the row terms (bf16).  Not thread-safe across concurrent streams
  * (launches from all threads are pooled). */
 swa_status swa_profile_enable(int32_t enable);
 swa_status swa_profile_read(int32_t kernel, double* total_ms, int64_t* launches);
