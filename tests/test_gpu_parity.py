@@ -142,20 +142,20 @@ def test_dropout_cases_full_parity(dev, case):
 
 
 def test_dropout_keep_all_equals_no_dropout(dev):
-    """An all-ones mask with keep_prob 1 reproduces the call without dropout:
-    out, the statistics and dv bit for bit (the dropout kernels apply the same
-    products); dk and dq up to rounding, since without dropout the dP chains
-    start from -D (dS = P (dP - D) in one multiply) and with dropout D is
-    subtracted after the chain."""
+    """An all-ones mask with keep_prob 1 reproduces the call without dropout up
+    to rounding: the bf16 forward without dropout walks 128-key tiles where the
+    dropout one walks the scheduler's 64-key tiles (another summation order),
+    and without dropout the backward's dP chains start from -D (dS = P (dP - D)
+    in one multiply) where with dropout D is subtracted after the chain."""
     p = workloads.make_custom([300, 77], num_heads=2, head_dim=128, sparse_mode=4,
                               pre_tokens=100, next_tokens=0)
     mask = workloads.make_drop_mask(p, 1.0)
     a = run_hip(p, dev)
     b = run_hip(p, dev, drop_mask=mask, keep_prob=1.0)
-    for n in ("out", "smax", "ssum", "dv"):
-        assert torch.equal(a[n], b[n]), n
-    for n in ("dk", "dq"):
+    for n in ("out", "dq", "dk", "dv"):
         assert (a[n].float() - b[n].float()).abs().max() <= 1e-2, n
+    assert (a["smax"] - b["smax"]).abs().max() <= 1e-5
+    assert ((a["ssum"] - b["ssum"]).abs() / b["ssum"].abs().clamp_min(1e-30)).max() <= 1e-4
 
 
 # ------------------------------------------------------------ exact cases

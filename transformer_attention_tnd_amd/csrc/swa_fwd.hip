@@ -79,7 +79,12 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
   using M = Mfma<T>;
   using op_t = typename M::op_t;
   constexpr int KPL = M::KPL, KSTEP = M::KSTEP;
-  constexpr int HALF = FWD_HALF, BN = FWD_BN, NT = 512;
+  // bf16 without dropout walks 128-key tiles (two of the scheduler's 64-key
+  // tiles per step: half the barriers, rescale checks and lane swaps per
+  // key); the other instantiations walk the scheduler's tiles
+  constexpr bool kWide = sizeof(T) == 2 && !kDrop;
+  constexpr int HALF = FWD_HALF, BN = kWide ? 2 * FWD_BN : FWD_BN, NT = 512;
+  constexpr int SUB = BN / FWD_BN;  // scheduler tiles per kernel tile
   constexpr int RB = D * (int)sizeof(T);  // tile row bytes
   constexpr int TB = BN * RB;             // tile bytes
   constexpr int NDB = D / 32;             // 32-wide head-dim blocks
@@ -87,14 +92,17 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
   constexpr int QSTEPS = D / KSTEP;       // contraction steps over d
   constexpr int PSTEPS = 32 / KSTEP;      // contraction steps per 32 keys
   constexpr float kRescale = 8.f;         // exp2-domain slack before moving the reference
-  static_assert(HALF == 128 && BN == 64, "two groups of 4 waves x 32 rows; 64-key tiles");
+  static_assert(HALF == 128 && FWD_BN == 64, "two groups of 4 waves x 32 rows; 64-key scheduler tiles");
 
   // K and V tiles rotate through NBUF buffers each: four for the bf16
   // kernels without dropout, whose copies are issued from the matrix phases
   // (the copy of a tile then has two steps to land), else three when they
   // fit (one step), else two
   constexpr bool kSpreadable = sizeof(T) == 2 && !kDrop;
-  constexpr int NBUF = kSpreadable && 8 * TB <= 160 * 1024 ? 4 : 6 * TB <= 160 * 1024 ? 3 : 2;
+  constexpr int NBUF = kSpreadable && 8 * TB <= 160 * 1024   ? 4
+                      : kSpreadable && 6 * TB <= 160 * 1024 ? 3
+                      : 6 * TB <= 160 * 1024 && !kWide      ? 3
+                                                            : 2;
   __shared__ __attribute__((aligned(1024))) char lds[2 * NBUF * TB];  // K[NBUF] V[NBUF]
   char* const kbuf0 = lds;
   char* const vbuf0 = lds + NBUF * TB;
@@ -111,14 +119,28 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
   const T* kg = static_cast<const T*>(a.k) + (int64_t)it.kv_base * ldkv + kvh * D;
   const T* vg = static_cast<const T*>(a.v) + (int64_t)it.kv_base * ldkv + kvh * D;
   const int qrow = it.block * 2 * HALF + HALF * g + 32 * (w & 3) + c;  // sequence-local
-  // this group's tile range, and the union over both groups (the loop range)
-  const int32_t mtiles = g ? it.tiles[1] : it.tiles[0], mfull = g ? it.full[1] : it.full[0];
-  const int mlo = mtiles & 0xffff, mhi = (mtiles >> 16) & 0xffff;
-  const int mflo = mfull & 0xffff, mfhi = (mfull >> 16) & 0xffff;
+  // this group's tile range, and the union over both groups (the loop range),
+  // in kernel tiles: a kernel tile is visited if one of its scheduler tiles
+  // is, and mask-free only if all of them are (keys of a visited kernel tile
+  // that the schedule skips are outside the band: the mask removes them)
+  auto vis = [](int32_t r, int& l, int& u) {
+    const int l0 = r & 0xffff, u0 = (r >> 16) & 0xffff;
+    l = l0 > u0 ? 1 : l0 / SUB;
+    u = l0 > u0 ? 0 : u0 / SUB;
+  };
+  auto full = [](int32_t r, int& l, int& u) {
+    const int l0 = r & 0xffff, u0 = (r >> 16) & 0xffff;
+    l = l0 > u0 ? 1 : (l0 + SUB - 1) / SUB;
+    u = l0 > u0 ? 0 : (u0 + 1) / SUB - 1;
+  };
+  int mlo, mhi, mflo, mfhi;
+  vis(g ? it.tiles[1] : it.tiles[0], mlo, mhi);
+  full(g ? it.full[1] : it.full[0], mflo, mfhi);
   int lo, hi;
   {
-    const int lo0 = it.tiles[0] & 0xffff, hi0 = (it.tiles[0] >> 16) & 0xffff;
-    const int lo1 = it.tiles[1] & 0xffff, hi1 = (it.tiles[1] >> 16) & 0xffff;
+    int lo0, hi0, lo1, hi1;
+    vis(it.tiles[0], lo0, hi0);
+    vis(it.tiles[1], lo1, hi1);
     if (lo0 > hi0) {
       lo = lo1;
       hi = hi1;
@@ -131,14 +153,22 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
     }
   }
   const float cs = kPos ? a.scale_log2 : 1.f;  // raw score -> exp2 units
-  // Keys allowed for this lane's row: j in [j_min, j_max] (empty past the end)
-  int j_min = 0, j_max = it.skv - 1;
-  if (a.mode != 0) {  // 64-bit: pre / next may be near the int range
-    const int64_t lo64 = (int64_t)qrow - it.band[0], hi64 = (int64_t)qrow + it.band[1];
-    j_min = lo64 < 0 ? 0 : (lo64 > it.skv ? it.skv : (int)lo64);
-    j_max = hi64 < j_max ? (hi64 < -1 ? -1 : (int)hi64) : j_max;
-  }
-  if (qrow >= it.sq) j_max = -1;
+  // Keys allowed for this lane's row: j in [j_min, j_max] (empty past the
+  // end).  Formed where a masked tile needs it (the row index passes an
+  // empty asm so the compiler does not keep the two bounds live, in
+  // registers, across the whole loop).
+  auto key_range = [&](int& j_min, int& j_max) {
+    int q = qrow;
+    asm volatile("" : "+v"(q));
+    j_min = 0;
+    j_max = it.skv - 1;
+    if (a.mode != 0) {  // 64-bit: pre / next may be near the int range
+      const int64_t lo64 = (int64_t)q - it.band[0], hi64 = (int64_t)q + it.band[1];
+      j_min = lo64 < 0 ? 0 : (lo64 > it.skv ? it.skv : (int)lo64);
+      j_max = hi64 < j_max ? (hi64 < -1 ? -1 : (int)hi64) : j_max;
+    }
+    if (q >= it.sq) j_max = -1;
+  };
 
   // Dropout keep bits of this lane's row for the 64 keys of a tile: three
   // 32-bit words loaded in the matrix phase that forms the tile's scores,
@@ -235,6 +265,8 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
     if constexpr (kMask) {
       // key 32 jb + c_row(r, h) of the tile is allowed iff 32 jb + 8 (r / 4) + r % 4
       // lies in the lane's range (the 4 h of c_row moved into the bounds)
+      int j_min, j_max;
+      key_range(j_min, j_max);
       const LaneRange rg = lane_range(j_min - tile * BN - 4 * h, j_max - tile * BN - 4 * h, BN);
 #pragma unroll
       for (int jb = 0; jb < NJB; ++jb) {
@@ -313,7 +345,7 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
   // NBUF - 1 steps ahead, group 1 the V tile NBUF - 2 steps ahead.
   // Past the range the copy reads nothing and writes zeros into the free
   // buffer, so every wave issues the same number of copies in every step.
-  constexpr bool kSpread = kSpreadable && NBUF >= 3;
+  constexpr bool kSpread = kSpreadable;
   using Dma = TileDma<bf16, D, BN, 256>;  // (used by the bf16 instantiations only)
   constexpr int COPY_EVERY = 4;  // pipeline slots between copy instructions
   Dma cp;
