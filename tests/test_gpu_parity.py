@@ -190,6 +190,51 @@ def test_query_zero_counts_are_exact(dev):
         assert (out - expect).abs().max() <= 1e-6
 
 
+ZERO_Q_BF16 = {
+    "d128_band": dict(lengths_q=[300, 77, 513], head_dim=128, sparse_mode=4, pre=70, nxt=9),
+    "d128_wide_band": dict(lengths_q=[700, 129], head_dim=128, sparse_mode=4, pre=200, nxt=130),
+    "d64_left_up_causal": dict(lengths_q=[300, 513], lengths_kv=[700, 260], head_dim=64,
+                               sparse_mode=2, pre=0, nxt=0),
+    "d128_right_down_causal": dict(lengths_q=[513, 77], lengths_kv=[260, 300], head_dim=128,
+                                   sparse_mode=3, pre=0, nxt=0),
+}
+
+
+@pytest.mark.parametrize("case", sorted(ZERO_Q_BF16))
+def test_query_zero_counts_are_exact_bf16(dev, case):
+    """The same count check on the bf16 forward (128-key tiles, each visited
+    or mask-free by the classification of its two scheduler tiles): with q = 0
+    every allowed probability is exactly 1, so softmax_sum equals the number of
+    allowed keys and softmax_max is 0, bit for bit; out (the fraction of
+    allowed keys j = c mod D) is zero exactly where no allowed key falls in
+    class c, and otherwise within the bf16 rounding of the fraction."""
+    kw = dict(ZERO_Q_BF16[case])
+    D, mode, pre, nxt = kw.pop("head_dim"), kw.pop("sparse_mode"), kw.pop("pre"), kw.pop("nxt")
+    p = workloads.make_custom(kw["lengths_q"], kw.get("lengths_kv"), num_heads=1, head_dim=D,
+                              dtype=torch.bfloat16, sparse_mode=mode, pre_tokens=pre,
+                              next_tokens=nxt)
+    p.q.zero_()
+    p.v.zero_()
+    for s0, L in oracle.sequences(p.cu_seqlens_kv):
+        for j in range(L):
+            p.v[s0 + j, 0, j % D] = 1.0
+    note(f"[zero-q bf16] {case} cu_q={p.cu_seqlens_q} cu_kv={p.cu_seqlens_kv}")
+    g = run_hip(p, dev, with_backward=False)
+    for (q0, Lq), (_, Lk) in zip(oracle.sequences(p.cu_seqlens_q), oracle.sequences(p.cu_seqlens_kv)):
+        M = oracle.allowed_mask(torch.arange(Lq), torch.arange(Lk), mode, pre, nxt, Lq, Lk)
+        counts = M.sum(1)
+        assert torch.equal(g["ssum"][q0:q0 + Lq, 0, 0], counts.float()), "row counts differ"
+        has = counts > 0
+        assert torch.equal(g["smax"][q0:q0 + Lq, 0, 0][has], torch.zeros(int(has.sum())))
+        per_c = torch.zeros(Lq, D)
+        for c in range(D):
+            per_c[:, c] = M[:, c::D].sum(1).float()
+        expect = per_c / counts.clamp_min(1)[:, None].float()
+        out = g["out"][q0:q0 + Lq, 0].float()
+        assert torch.equal(out != 0, expect != 0), "mask pattern differs"
+        assert ((out - expect).abs() <= expect.abs() * 2.0 ** -8 + 1e-7).all()
+
+
 def test_forward_example_constant_inputs(dev):
     """VarLenScore API doc call example (T=256, N=1, D=128, scale 0.088388,
     pre/next 65536, mode 0) with q = k = v = 1: out = 1, softmax_max =
