@@ -109,12 +109,18 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_dq_kernel(BwdArgs a) {
   // other half from lane l ^ 32, which holds the same row) and lse2 of this
   // lane's row, stored for the dK/dV kernel (the backward preprocess)
   auto row_stats = [&]() {
-    float dpart = 0.f;
+    // two bf16 products per instruction (exact in fp32) added in fp32, four chains
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    float dp4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < DSTEPS; ++t) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) dpart += static_cast<float>(yf[t][e]) * static_cast<float>(of[t][e]);
+      for (int e = 0; e < 4; ++e) {
+        const bf16x2 y2 = {yf[t][2 * e], yf[t][2 * e + 1]}, o2 = {of[t][2 * e], of[t][2 * e + 1]};
+        dp4[e] = __builtin_amdgcn_fdot2_f32_bf16(y2, o2, dp4[e], false);
+      }
     }
+    const float dpart = (dp4[0] + dp4[1]) + (dp4[2] + dp4[3]);
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(dpart), __float_as_uint(dpart),
                                                      false, false);
     if (row_ok) {
