@@ -222,7 +222,7 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
 
   // S^T block jb: rows = keys 32*jb + c_row(r, h), column = this lane's query
   // (the two key blocks alternate so that consecutive MFMAs are independent)
-  auto scores = [&](const char* kt) {
+  auto scores = [&](const char* kt) __attribute__((always_inline)) {
 #pragma unroll
     for (int jb = 0; jb < NJB; ++jb) s[jb] = floatx16{};
 #pragma unroll
@@ -236,7 +236,7 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
     }
   };
   // O^T[db] += V^T P^T with the probabilities of the previous tile
-  auto pv = [&](const char* vt) {
+  auto pv = [&](const char* vt) __attribute__((always_inline)) {
 #pragma unroll
     for (int jb = 0; jb < NJB; ++jb) {
 #pragma unroll
@@ -256,7 +256,7 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
     }
   };
   // Softmax of the current tile: scores -> probabilities (packed), running stats.
-  auto softmax = [&](auto mask_tag, int tile) {
+  auto softmax = [&](auto mask_tag, int tile) __attribute__((always_inline)) {
     constexpr bool kMask = decltype(mask_tag)::value;
     if constexpr (!kPos) {  // non-positive scale: work on scaled scores (scale before masking)
 #pragma unroll
@@ -396,7 +396,7 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
   };
 
   // matrix phase M(t): P(t-1) V(t-1) and S(t), for the tiles of this group
-  auto m_phase = [&](int t, int k) {
+  auto m_phase = [&](int t, int k) __attribute__((always_inline)) {
     const bool do_pv = t - 1 >= mlo && t - 1 <= mhi;
     const bool do_s = t >= mlo && t <= mhi;
     if constexpr (kDrop) {
@@ -432,7 +432,7 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
     __builtin_amdgcn_s_setprio(0);
   };
   // vector phase V(t)
-  auto v_phase = [&](int t) {
+  auto v_phase = [&](int t) __attribute__((always_inline)) {
     if (t < mlo || t > mhi) return;
     if (t < mflo || t > mfhi)
       softmax(std::true_type{}, t);
