@@ -27,7 +27,9 @@ namespace swa {
 //     of S^T = K Q^T and dP^T = V dY^T) and its dQ^T accumulator, and walks the
 //     key tiles (64 keys) of the band; dQ^T += K^T dS^T takes K^T from the
 //     key tile through transposing LDS reads.  dq is written once, in the
-//     input type.
+//     input type.  It runs first and also forms D = rowsum(dY o O) and lse2
+//     of its rows, which this kernel reads (D stored negated: without dropout
+//     the dP chains here start from -D).
 // Both are organised for one wave per SIMD.  The products of a tile form one
 // software pipeline in a fixed order; each LDS operand is read a fixed number
 // of products ahead into a small register ring, and the vector work (the
@@ -157,8 +159,8 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
     cp_q.init(qg + (int64_t)tile * BM * ld, ld, nvalid, slab, tid);
     cp_dy.init(dyg + (int64_t)tile * BM * ld, ld, nvalid, slab + QTB, tid);
   };
-  // lse2 / D of the tile's rows go straight into LDS slot b (wave 0: lse2,
-  // wave 1: D; one 64-lane dword copy each, rows past the sequence read as
+  // lse2 / -D of the tile's rows go straight into LDS slot b (wave 0: lse2,
+  // wave 1: -D; one 64-lane dword copy each, rows past the sequence read as
   // zero: the tiles that hold such rows are masked tiles, where their P is
   // zero whatever lse2 holds), waited for with the tile copies; with dropout
   // the keep bits of the rows go through registers (store_rows)

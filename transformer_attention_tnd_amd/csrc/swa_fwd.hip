@@ -23,12 +23,17 @@
 // Each SIMD holds one wave of each group, so its matrix core always has one
 // wave feeding it while the other wave's softmax runs on the vector ALUs.
 //
-// Data movement: K and V tiles of 64 keys go from HBM straight into
-// swizzled row-major LDS tiles (buffer loads with the LDS destination, rows
-// past the sequence read as zero).  They rotate through four buffers each in
-// the bf16 kernels without dropout, whose copies go out part by part from the
-// matrix phases, so a tile's copy has two steps to land; otherwise three
-// (two when three do not fit).  V^T operands come from the row-major V tile through
+// Tiles: the bf16 kernels without dropout walk 128-key tiles (two of the
+// scheduler's 64-key tiles per step, which halves the barriers, rescale
+// checks and lane swaps per key); the dropout and fp32 kernels walk 64-key
+// tiles.
+//
+// Data movement: K and V tiles go from HBM straight into swizzled row-major
+// LDS tiles (buffer loads with the LDS destination, rows past the sequence
+// read as zero).  In the bf16 kernels without dropout the copies go out part
+// by part from the matrix phases, into two buffers each at D = 128 (four at
+// D = 64); otherwise they rotate through three buffers (two when three do
+// not fit).  V^T operands come from the row-major V tile through
 // transposing LDS reads.  The matrix phase (bf16) is one software pipeline of
 // its products with the LDS operands read a few products ahead; it runs at
 // raised wave priority.
