@@ -176,10 +176,12 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
   };
 
   // Dropout keep bits of this lane's row for the 64 keys of a tile: three
-  // 32-bit words loaded in the matrix phase that forms the tile's scores,
-  // funnel-shifted into the window in its softmax (bit k = key 64 t + k).
-  uint32_t mw[3] = {0u, 0u, 0u};
-  uint32_t msh = 0;
+  // 32-bit words, funnel-shifted into the window in the tile's softmax (bit
+  // k = key 64 t + k).  The words of tile t + 1 are loaded (into mwn) in the
+  // matrix phase of tile t and move into mw at the start of the next matrix
+  // phase, so a load has a full step to land.
+  uint32_t mw[3] = {0u, 0u, 0u}, mwn[3] = {0u, 0u, 0u};
+  uint32_t msh = 0, mshn = 0;
   const int64_t drop_row = kDrop ? it.drop_base + (int64_t)head * it.sq * it.skv +
                                        (int64_t)(qrow < it.sq ? qrow : 0) * it.skv
                                  : 0;
@@ -187,10 +189,10 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
     if constexpr (kDrop) {
       const int64_t bit = drop_row + (int64_t)tile * BN;
       const int64_t w = bit >> 5;
-      msh = (uint32_t)(bit & 31);
+      mshn = (uint32_t)(bit & 31);
 #pragma unroll
       for (int e = 0; e < 3; ++e)
-        mw[e] = (qrow < it.sq && w + e < a.drop.n_words) ? a.drop.words[w + e] : 0u;
+        mwn[e] = (qrow < it.sq && w + e < a.drop.n_words) ? a.drop.words[w + e] : 0u;
     }
   };
 
@@ -404,8 +406,11 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
   auto m_phase = [&](int t, int k) __attribute__((always_inline)) {
     const bool do_pv = t - 1 >= mlo && t - 1 <= mhi;
     const bool do_s = t >= mlo && t <= mhi;
-    if constexpr (kDrop) {
-      if (do_s) load_mask(t);
+    if constexpr (kDrop) {  // this tile's words in, the next tile's requested
+#pragma unroll
+      for (int e = 0; e < 3; ++e) mw[e] = mwn[e];
+      msh = mshn;
+      load_mask(t + 1);
     }
     const char* kt = kbuf0 + (k % NBUF) * TB;                 // K(t)
     const char* vt = vbuf0 + ((k + NBUF - 1) % NBUF) * TB;    // V(t-1)
@@ -457,6 +462,7 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
       for (int j = 0; j <= NBUF - 3; ++j)
         if (lo + j <= hi) load_v(lo + j, j);
     }
+    if constexpr (kDrop) load_mask(lo);
     wait_vmem();
     __syncthreads();
     const int nk = hi - lo + 2;
@@ -492,12 +498,13 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
       // copies issued in this step may still be in flight)
       if constexpr (kSpread)  // the copies of the last NBUF - 2 steps (one tile per wave each) stay in flight
         __builtin_amdgcn_s_waitcnt(0x0F70 | ((NBUF - 2) * Dma::PARTS));
-      else if (NBUF == 2 || (!ck && !cv))
+      else if (NBUF == 2 || (!ck && !cv) || kDrop)  // dropout: the next tile's keep words too
         wait_vmem();
       else if (ck && cv)
         __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * NC));
       else
         __builtin_amdgcn_s_waitcnt(0x0F70 | NC);
+      if constexpr (kDrop) asm volatile("" : : "v"(mwn[0]), "v"(mwn[1]), "v"(mwn[2]), "v"(mshn));
       __syncthreads();
     }
     if constexpr (kSpread) wait_vmem();  // the last step's copies (into free buffers)
