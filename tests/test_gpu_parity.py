@@ -121,6 +121,9 @@ DROPOUT = {
     "bf16_d128_gqa_causal_dropout": (dict(lengths_q=[257, 130], lengths_kv=[300, 100],
                                           num_heads=4, num_kv_heads=2, head_dim=128,
                                           sparse_mode=3, std=0.5), 0.9),
+    "bf16_d64_gqa_band_dropout": (dict(lengths_q=[200, 333], num_heads=6, num_kv_heads=2,
+                                       head_dim=64, sparse_mode=4, pre_tokens=100,
+                                       next_tokens=20), 0.75),
     "fp32_d128_band_dropout": (dict(lengths_q=[300, 45], num_heads=2, head_dim=128,
                                     sparse_mode=4, pre_tokens=90, next_tokens=20,
                                     dtype=torch.float32), 0.7),
