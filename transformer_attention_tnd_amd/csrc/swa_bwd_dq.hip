@@ -331,19 +331,16 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_dq_kernel(BwdArgs a) {
     run(std::true_type{}, lo, hi);
   }
 
-  // dq = scale dQ for this lane's row (zero when the row attends no key)
-  if (qrow < it.sq) {
-    bf16* dqp = static_cast<bf16*>(a.dq) + ((int64_t)it.q_base + qrow) * ld + head * D;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 v4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v4[e] = static_cast<bf16>(acc[db][4 * g + e] * a.scale);
-        *reinterpret_cast<bf16x4*>(dqp + 32 * db + 8 * g + 4 * h) = v4;
-      }
-    }
+  // dq = scale dQ (zero for a row that attends no key), as whole rows
+  // through the wave's own LDS slice (the slabs are free: every copy has
+  // landed and the last tile is done)
+  static_assert(4 * 32 * RB <= 2 * SLAB, "the staging slices fit in the slabs");
+  __syncthreads();
+  {
+    const int row0 = it.block * BQ + 32 * w;  // sequence-local row of the wave's slice
+    store_rows_via_lds<NDB>(acc, a.scale, lds + w * 32 * RB,
+                            static_cast<bf16*>(a.dq) + ((int64_t)it.q_base + row0) * ld + head * D, ld,
+                            it.sq - row0);
   }
 }
 

@@ -403,26 +403,17 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
     if (lo <= hi && ((hi - lo + 1) & 1)) flip(1);
   }
 
-  // this lane's key column of dK^T / dV^T
-  if (kw < it.skv) {
-    const int64_t tok = (int64_t)it.kv_base + kw;
-    bf16* dkp = static_cast<bf16*>(a.dk) + tok * ldkv + kvh * D;
-    bf16* dvp = static_cast<bf16*>(a.dv) + tok * ldkv + kvh * D;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * db + 8 * g + 4 * h;
-        bf16x4 k4, v4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          k4[e] = static_cast<bf16>(dk[db][4 * g + e] * a.scale);
-          v4[e] = static_cast<bf16>(dv[db][4 * g + e]);
-        }
-        *reinterpret_cast<bf16x4*>(dkp + d0) = k4;
-        *reinterpret_cast<bf16x4*>(dvp + d0) = v4;
-      }
-    }
+  // dK = scale dK^T and dV^T, as whole rows through two LDS slices per wave
+  // (the slabs are free: every copy has landed and the last tile is done)
+  static_assert(2 * 4 * 32 * RB <= 2 * SLAB, "the staging slices fit in the slabs");
+  __syncthreads();
+  {
+    const int row0 = it.block * BN + 32 * w;  // sequence-local key of the wave's slice
+    const int64_t off = ((int64_t)it.kv_base + row0) * ldkv + kvh * D;
+    store_rows_via_lds<NDB>(dk, a.scale, lds + w * 32 * RB, static_cast<bf16*>(a.dk) + off, ldkv,
+                            it.skv - row0);
+    store_rows_via_lds<NDB>(dv, 1.f, lds + (4 + w) * 32 * RB, static_cast<bf16*>(a.dv) + off, ldkv,
+                            it.skv - row0);
   }
 }
 

@@ -286,6 +286,49 @@ __device__ inline int xcd_remap(int wg, int nwg) {
   return x * q + (x < r ? x : r) + idx;
 }
 
+// Store a wave's 32 rows of 32 NDB values held in transposed accumulators
+// (lane l: row l % 32, value 32 db + 8 g + 4 (l / 32) + e in acc[db][4 g + e]),
+// each value times mul and rounded to bf16, as whole rows.  Stored directly,
+// a lane would write half of its row in 8-byte pieces and every store
+// instruction would scatter over 64 rows, ld elements apart; here the rows go
+// through the wave's own LDS slice st (32 swizzled rows of 64 NDB bytes,
+// which no other wave may touch meanwhile) and each store instruction
+// writes 16 bytes per lane, 64 / (4 NDB) complete rows.  Rows r >= nrows of
+// dst are not written.
+template <int NDB>
+__device__ __attribute__((always_inline)) inline void store_rows_via_lds(const floatx16 (&acc)[NDB], float mul,
+                                                                          char* st, bf16* dst, int64_t ld,
+                                                                          int nrows) {
+  constexpr int RB = 64 * NDB;  // row bytes
+  // lane indices formed here (an empty asm keeps the compiler from sharing
+  // these offsets with values computed before the caller's tile loop, which
+  // would keep them live, in registers, across it)
+  int ln = threadIdx.x;
+  asm volatile("" : "+v"(ln));
+  ln &= 63;
+  const int c = ln & 31, h = ln >> 5;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      bf16x4 v4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v4[e] = static_cast<bf16>(acc[db][4 * g + e] * mul);
+      *reinterpret_cast<bf16x4*>(st + tile_off<RB>(c, 2 * (32 * db + 8 * g + 4 * h))) = v4;
+    }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave reads what its other lanes wrote
+  constexpr int CPR = RB / 16, RPI = 64 / CPR;           // 16-byte chunks per row, rows per instruction
+  const int ch = ln % CPR, rr = ln / CPR;
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = RPI * i + rr;
+    const u32x4 val = *reinterpret_cast<const u32x4*>(st + tile_off<RB>(r, 16 * ch));
+    if (r < nrows) *reinterpret_cast<u32x4*>(dst + (int64_t)r * ld + 8 * ch) = val;
+  }
+  asm volatile("" ::: "memory");  // the reads stay ahead of any later write to st
+}
+
 // Element mask: inside the sequence and, unless mode is 0, inside the band
 // -pre <= j - i <= next (the item's band: sparse modes 2, 3 and 4 all reach the
 // kernels in this form).

@@ -515,43 +515,15 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
   const float inv = l_ref > 0.f ? 1.f / l_ref : 0.f;
   const int64_t tok = (int64_t)it.q_base + qrow;
   if constexpr (sizeof(T) == 2) {
-    // A lane holds half of its row (8-byte pieces, one every 16 bytes), and
-    // the rows of a wave lie ld elements apart in memory: stored directly,
-    // every store instruction would scatter over 64 rows.  The wave's 32 rows
-    // go through LDS instead (its own 32-row slice of the K / V area, free
-    // once every wave has left the loop and the last copies have landed) and
-    // are stored as whole rows, CPR lanes of 16 bytes per row.
+    // the wave's 32 rows as whole rows, through its own 32-row slice of the
+    // K / V area (free once every wave has left the loop and the last
+    // copies have landed)
     static_assert(8 * 32 * RB <= 2 * NBUF * TB, "the staging slices fit in the K / V area");
     __syncthreads();
-    // lane indices formed here (an empty asm keeps the compiler from sharing
-    // these offsets with values computed before the loop, which would keep
-    // them live, in registers, across it)
-    int ln = threadIdx.x;
-    asm volatile("" : "+v"(ln));
-    ln &= 63;
-    const int ec = ln & 31, eh = ln >> 5;
-    char* const st = lds + w * 32 * RB;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        bf16x4 v4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v4[e] = static_cast<bf16>(o[db][4 * gq + e] * inv);
-        *reinterpret_cast<bf16x4*>(st + tile_off<RB>(ec, 2 * (32 * db + 8 * gq + 4 * eh))) = v4;
-      }
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave reads what its other lanes wrote
-    constexpr int CPR = RB / 16, RPI = 64 / CPR;  // 16-byte chunks per row, rows per instruction
-    const int ch = ln % CPR, rr = ln / CPR;
     const int row0 = it.block * 2 * HALF + 32 * w;  // sequence-local row of the wave's slice
-    T* const ob = static_cast<T*>(a.out) + ((int64_t)it.q_base + row0) * ld + head * D + 8 * ch;
-#pragma unroll
-    for (int i = 0; i < 32 / RPI; ++i) {
-      const int r = RPI * i + rr;
-      const u32x4 val = *reinterpret_cast<const u32x4*>(st + tile_off<RB>(r, 16 * ch));
-      if (row0 + r < it.sq) *reinterpret_cast<u32x4*>(ob + (int64_t)r * ld) = val;
-    }
+    store_rows_via_lds<NDB>(o, inv, lds + w * 32 * RB,
+                            static_cast<bf16*>(a.out) + ((int64_t)it.q_base + row0) * ld + head * D, ld,
+                            it.sq - row0);
   } else if (qrow < it.sq) {
     T* op = static_cast<T*>(a.out) + tok * ld + head * D;
 #pragma unroll
