@@ -36,7 +36,8 @@
 // not fit).  V^T operands come from the row-major V tile through
 // transposing LDS reads.  The matrix phase (bf16) is one software pipeline of
 // its products with the LDS operands read a few products ahead; it runs at
-// raised wave priority.
+// raised wave priority.  At the end (bf16) each wave stages its 32 output
+// rows in LDS and stores them as whole rows.
 //
 // Dropout (a kDrop instantiation): the keep bits of a lane's row for the
 // tile are read as three 32-bit words in the matrix phase that forms the
