@@ -82,7 +82,7 @@ def assert_close(name, g, o, dtype):
         assert mean <= TOL_BF16_MEAN, f"{name}: mean abs error {mean:.3e} > {TOL_BF16_MEAN}"
 
 
-def assert_stats(smax_g, ssum_g, smax_o, ssum_o, dtype):
+def assert_stats(smax_g, ssum_g, smax_o, ssum_o, dtype, quiet=False):
     """Statistics [.., 8] from the GPU against oracle [..]; all 8 copies equal."""
     assert torch.equal(smax_g, smax_g[..., :1].expand_as(smax_g)), "softmax_max copies differ"
     assert torch.equal(ssum_g, ssum_g[..., :1].expand_as(ssum_g)), "softmax_sum copies differ"
@@ -95,7 +95,8 @@ def assert_stats(smax_g, ssum_g, smax_o, ssum_o, dtype):
     if fin.any():
         dm = float((gm[fin] - om[fin]).abs().max())
         ds = float(((gs[fin] - os_[fin]).abs() / os_[fin].abs()).max())
-        note(f"  softmax_max: max_abs={dm:.3e}  softmax_sum: max_rel={ds:.3e}")
+        if not quiet:
+            note(f"  softmax_max: max_abs={dm:.3e}  softmax_sum: max_rel={ds:.3e}")
         if dtype == torch.float32:
             ref = float(om[fin].abs().max())
             assert dm <= TOL_FP32_REL * max(ref, 1.0)
@@ -112,3 +113,79 @@ def compare_full(p, g, o):
     for n in ("dq", "dk", "dv"):
         if n in g:
             assert_close(n, g[n], o[n], dt)
+
+
+class StreamedErrors:
+    """Running whole-tensor error figures, fed one (sequence, head group) at a
+    time: max |g - o|, sum |g - o|, element count and max |o| per tensor, and
+    the worst statistic errors.  Checks against the same tolerances as
+    ``assert_close`` / ``assert_stats``."""
+
+    def __init__(self, dtype):
+        self.dtype = dtype
+        self.t = {}
+        self.stat_max_abs = 0.0
+        self.stat_sum_rel = 0.0
+
+    def add(self, name, g, o):
+        d = (g.double() - o.double()).abs()
+        mx, s, n, ref = self.t.get(name, (0.0, 0.0, 0, 0.0))
+        self.t[name] = (max(mx, float(d.max()) if d.numel() else 0.0), s + float(d.sum()),
+                        n + d.numel(), max(ref, float(o.abs().max()) if o.numel() else 0.0))
+
+    def add_stats(self, smax_g, ssum_g, smax_o, ssum_o):
+        assert_stats(smax_g, ssum_g, smax_o, ssum_o, self.dtype, quiet=True)
+        gm, gs = smax_g[..., 0].double(), ssum_g[..., 0].double()
+        fin = torch.isfinite(smax_o)
+        if fin.any():
+            self.stat_max_abs = max(self.stat_max_abs,
+                                    float((gm[fin] - smax_o[fin]).abs().max()))
+            self.stat_sum_rel = max(self.stat_sum_rel, float(
+                ((gs[fin] - ssum_o[fin]).abs() / ssum_o[fin].abs()).max()))
+
+    def merge(self, other):
+        for name, (mx, s, n, ref) in other.t.items():
+            a = self.t.get(name, (0.0, 0.0, 0, 0.0))
+            self.t[name] = (max(a[0], mx), a[1] + s, a[2] + n, max(a[3], ref))
+        self.stat_max_abs = max(self.stat_max_abs, other.stat_max_abs)
+        self.stat_sum_rel = max(self.stat_sum_rel, other.stat_sum_rel)
+
+    def check(self, label):
+        for name, (mx, s, n, ref) in self.t.items():
+            mean = s / max(n, 1)
+            if self.dtype == torch.float32:
+                rel = mx / max(ref, 1e-30)
+                note(f"  {label} {name}: max_rel={rel:.3e} over {n} elements")
+                assert rel <= TOL_FP32_REL, f"{name}: max relative error {rel:.3e}"
+            else:
+                note(f"  {label} {name}: max_abs={mx:.3e} mean_abs={mean:.3e} over {n} "
+                     f"elements (|ref|max={ref:.3e})")
+                assert mx <= TOL_BF16_MAX, f"{name}: max abs error {mx:.3e} > {TOL_BF16_MAX}"
+                assert mean <= TOL_BF16_MEAN, f"{name}: mean abs error {mean:.3e}"
+        note(f"  {label} softmax_max: max_abs={self.stat_max_abs:.3e}  softmax_sum: "
+             f"max_rel={self.stat_sum_rel:.3e}")
+
+
+def compare_streamed(p, g, kv_heads, acc, chunk=512):
+    """Compare every row and key of the given key/value heads (with their
+    query heads) of problem p against the oracle, one (sequence, key/value
+    head) at a time on contiguous slices, so that no fp64 copy of the whole
+    problem is held.  The oracle gives a varlen batch the results of separate
+    per-sequence calls, so each slice is its own one-sequence problem."""
+    G = p.q.shape[1] // p.k.shape[1]
+    kw = dict(pre_tokens=p.pre_tokens, next_tokens=p.next_tokens,
+              sparse_mode=p.sparse_mode, chunk=chunk)
+    for (q0, lq), (k0, lk) in zip(oracle.sequences(p.cu_seqlens_q),
+                                  oracle.sequences(p.cu_seqlens_kv)):
+        tq, tk = slice(q0, q0 + lq), slice(k0, k0 + lk)
+        for h in kv_heads:
+            hq, hk = slice(h * G, (h + 1) * G), slice(h, h + 1)
+            Q, dY = (x[tq, hq].contiguous() for x in (p.q, p.dy))
+            K, V = (x[tk, hk].contiguous() for x in (p.k, p.v))
+            out, sm, ss = oracle.forward(Q, K, V, [lq], [lk], p.scale, **kw)
+            dq, dk, dv = oracle.backward(Q, K, V, dY, out, sm, ss, [lq], [lk], p.scale, **kw)
+            acc.add("out", g["out"][tq, hq], out)
+            acc.add("dq", g["dq"][tq, hq], dq)
+            acc.add("dk", g["dk"][tk, hk], dk)
+            acc.add("dv", g["dv"][tk, hk], dv)
+            acc.add_stats(g["smax"][tq, hq], g["ssum"][tq, hq], sm, ss)

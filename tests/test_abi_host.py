@@ -227,3 +227,33 @@ def test_schedule_orders_longest_item_first():
             last = (seq, blk)
         counts[-1] += 1
     assert counts == sorted(counts, reverse=True)
+
+
+I64_MAX, I64_MIN = 2**63 - 1, -2**63
+
+
+@pytest.mark.parametrize("direction", [0, 1, 2])
+@pytest.mark.parametrize("pre,nxt,same_as", [
+    (I64_MAX, 0, (INT_MAX, 0)),
+    (0, I64_MAX, (0, INT_MAX)),
+    (I64_MAX, I64_MAX, (INT_MAX, INT_MAX)),
+    (I64_MAX, -5, (INT_MAX, -5)),
+    (-7, I64_MAX, (-7, INT_MAX)),
+    # -pre = I64_MAX: every row is empty, as with -pre = INT_MAX
+    (I64_MIN + 1, I64_MAX, (-INT_MAX, INT_MAX)),
+])
+def test_band_reach_beyond_int32_equals_widest_band(pre, nxt, same_as, direction):
+    """pre_tokens / next_tokens are int64 in the interface: a reach of 2^63 - 1
+    must schedule exactly what a reach of 2^31 - 1 does (both exceed any
+    sequence), with no overflow in the schedule's index arithmetic."""
+    cu = [300, 1000]
+    got = swa.swa_debug_tile_schedule(cu, cu, 1000, 1000, 128, 1, pre, nxt, 4, direction)
+    ref = swa.swa_debug_tile_schedule(cu, cu, 1000, 1000, 128, 1, *same_as, 4, direction)
+    assert got == ref
+
+
+@pytest.mark.parametrize("pre,nxt", [(I64_MAX, I64_MIN), (I64_MIN, I64_MAX), (I64_MIN, 0)])
+def test_band_sum_below_zero_is_rejected_without_overflow(pre, nxt):
+    # pre + next = -1 (or far below) in exact arithmetic: every row is empty
+    assert raw_forward(mode=4, pre=pre, nxt=nxt) == swa.SWA_ERR_INVALID
+    assert "pre_tokens + next_tokens" in swa.swa_last_error()

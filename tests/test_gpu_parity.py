@@ -2,9 +2,10 @@
 
 Small problems (the two small workloads and hand-made varlen/band cases that
 span several tiles and ragged tails) are compared element by element.  The
-three large workloads run in full on the GPU, in the launch configuration the
-benchmark times, and are compared on sampled rows and keys that the oracle
-evaluates one at a time, plus invariants that hold at any size.
+large workloads run in full on the GPU, in the launch configuration the
+benchmark times, and are compared element by element too, streamed one
+(sequence, key/value head) at a time through the oracle, after a fast
+pre-check on sampled rows and keys and on invariants that hold at any size.
 """
 import math
 
@@ -14,8 +15,8 @@ import torch
 import oracle
 import transformer_attention_tnd_amd as swa
 import workloads
-from parity_utils import (assert_close, assert_stats, compare_full, note, require_gpu,
-                          run_hip, run_oracle)
+from parity_utils import (StreamedErrors, assert_close, assert_stats, compare_full,
+                          compare_streamed, note, require_gpu, run_hip, run_oracle)
 
 pytestmark = pytest.mark.gpu
 INT_MAX = 2147483647
@@ -386,8 +387,8 @@ def invariants_check(p, g):
 def test_maximum_sizes(dev):
     """The largest sizes the interface takes (explainer 6.3: T up to 1M tokens,
     N up to 256 heads): one 1,048,576-token sequence with a narrow band
-    (sampled rows and keys at the start, the middle and the end), and 256
-    heads (full parity).  Exercises the 64-bit offsets of every kernel."""
+    (every row and key against the oracle), and 256 heads (full parity).
+    Exercises the 64-bit offsets of every kernel."""
     T = 1 << 20
     p = workloads.make_custom([T], num_heads=1, head_dim=128, sparse_mode=4, pre_tokens=192,
                               next_tokens=64, name="max_tokens")
@@ -395,33 +396,70 @@ def test_maximum_sizes(dev):
     g = run_hip(p, dev)
     for key in ("out", "dq", "dk", "dv"):
         assert torch.isfinite(g[key].float()).all(), key
-    sampled_check(p, g, [(0, 0, 0, 64), (0, 0, T // 2 + 37, 64), (0, 0, 10**9, 64)])
+    acc = StreamedErrors(p.dtype)
+    compare_streamed(p, g, range(p.k.shape[1]), acc)
+    acc.check("max_tokens whole tensors")
     del g
     p = workloads.make_custom([300, 77], num_heads=256, head_dim=64, name="max_heads")
     note("[parity] max_heads N=256")
     compare_full(p, run_hip(p, dev), run_oracle(p, chunk=None))
 
 
-LARGE = [
-    ("varlen_bf16_n16_d128_8seq_256to4096", [(0, 0, 0, 64), (3, 7, 1000, 64), (7, 15, 10**9, 48)]),
-    ("swa_bf16_b1_n16_s16384_d128_pre2048_next0",
-     [(0, 0, 0, 64), (0, 5, 2000, 96), (0, 11, 9000, 64), (0, 15, 10**9, 64)]),
-    ("varlen_swa_bf16_n32_d128_4seq_16kto32k_pre4096_next512",
-     [(0, 0, 0, 64), (1, 13, 4500, 64), (2, 31, 20000, 64), (3, 20, 10**9, 64)]),
+# Each large workload runs once on the GPU, in the launch configuration the
+# benchmark times (part 0: sampled rows and keys plus invariants, a fast
+# pre-check), then every row and key of every head is compared with the
+# oracle, a group of key/value heads per part; the last part checks the
+# whole-tensor figures (max and mean |g - o| per output tensor over all
+# elements, the worst statistic errors).
+LARGE = {
+    "varlen_bf16_n16_d128_8seq_256to4096":
+        ([(0, 0, 0, 64), (3, 7, 1000, 64), (7, 15, 10**9, 48)], 2),
+    "swa_bf16_b1_n16_s16384_d128_pre2048_next0":
+        ([(0, 0, 0, 64), (0, 5, 2000, 96), (0, 11, 9000, 64), (0, 15, 10**9, 64)], 2),
+    "varlen_swa_bf16_n32_d128_4seq_16kto32k_pre4096_next512":
+        ([(0, 0, 0, 64), (1, 13, 4500, 64), (2, 31, 20000, 64), (3, 20, 10**9, 64)], 8),
     # causal: keys near the end (few rows attend them, so the oracle's
     # key-side check stays cheap); the row-side check covers each sample too
-    ("causal_bf16_b1_n16_s16384_d128", [(0, 0, 16000, 64), (0, 9, 15000, 32), (0, 15, 10**9, 32)]),
-    ("gqa_swa_bf16_b1_n16kv4_s16384_d128_pre2048_next0",
-     [(0, 0, 0, 64), (0, 6, 5000, 64), (0, 15, 10**9, 64)]),
-]
+    "causal_bf16_b1_n16_s16384_d128":
+        ([(0, 0, 16000, 64), (0, 9, 15000, 32), (0, 15, 10**9, 32)], 4),
+    "gqa_swa_bf16_b1_n16kv4_s16384_d128_pre2048_next0":
+        ([(0, 0, 0, 64), (0, 6, 5000, 64), (0, 15, 10**9, 64)], 2),
+}
+LARGE_CASES = [(n, part) for n, (_, parts) in LARGE.items() for part in range(parts + 1)]
+_large = {}
 
 
-@pytest.mark.parametrize("name,samples", LARGE, ids=[n for n, _ in LARGE])
-def test_large_workloads_sampled_parity(dev, name, samples):
-    p = workloads.make_problem(name)
-    note(f"[parity] {name} T={p.q.shape[0]} cu={p.cu_seqlens_q}")
-    g = run_hip(p, dev)
-    for key in ("out", "dq", "dk", "dv"):
-        assert torch.isfinite(g[key].float()).all(), key
-    sampled_check(p, g, samples)
-    invariants_check(p, g)
+def large_state(dev, name):
+    """(problem, GPU results, per-part error accumulators) of one workload;
+    only the most recent workload is kept."""
+    if name not in _large:
+        _large.clear()
+        p = workloads.make_problem(name)
+        note(f"[parity] {name} T={p.q.shape[0]} cu={p.cu_seqlens_q}")
+        g = run_hip(p, dev)
+        for key in ("out", "dq", "dk", "dv"):
+            assert torch.isfinite(g[key].float()).all(), key
+        _large[name] = (p, g, {})
+    return _large[name]
+
+
+@pytest.mark.parametrize("name,part", LARGE_CASES, ids=[f"{n}-{i}" for n, i in LARGE_CASES])
+def test_large_workloads_parity(dev, name, part):
+    samples, parts = LARGE[name]
+    p, g, accs = large_state(dev, name)
+    if part == 0:
+        sampled_check(p, g, samples)
+        invariants_check(p, g)
+        return
+    nkv = p.k.shape[1]
+    heads = range((part - 1) * nkv // parts, part * nkv // parts)
+    acc = StreamedErrors(p.dtype)
+    compare_streamed(p, g, heads, acc)
+    acc.check(f"key/value heads {heads.start}..{heads.stop - 1}:")
+    accs[part] = acc
+    if part == parts:
+        assert sorted(accs) == list(range(1, parts + 1)), "a part of the workload was not run"
+        whole = StreamedErrors(p.dtype)
+        for a in accs.values():
+            whole.merge(a)
+        whole.check(f"{name} whole tensors:")

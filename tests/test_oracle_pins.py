@@ -371,3 +371,98 @@ def test_pins_catch_planted_mistakes(name):
     fwd_ok = torch.allclose(out, ref, atol=1e-12)
     bwd_ok = all(torch.allclose(a, b, atol=1e-12) for a, b in zip(grads, ref_grads))
     assert not (band_ok and fwd_ok and bwd_ok), name
+
+
+# ---------------------------------------------------------------- tile enumerator
+
+# Tile tables derived by hand from the band rule -pre <= j - i <= next with 64 x 64
+# tiles (P = partial, F = full, unlisted tiles skipped).  A tile is full only if
+# all of its 64 x 64 elements lie inside the sequence and inside the band.
+from oracle.tiles import FULL as F_, PARTIAL as P_  # noqa: E402
+HAND_TILES = [
+    # one 200-token sequence, pre 130, next 64: rows 192..199 form a ragged
+    # query block and keys 192..199 a ragged key tile.  Per query block (rows
+    # r..r+63) the offsets j - i of key tile t span [64 (t - b) - 63, 64 (t - b) + 63]
+    # with b the block index: inside [-130, 64] for t - b in {-1, 0} (full if
+    # complete), partly for t - b in {-2, 1}, never beyond.
+    dict(lengths=[200], mode=4, pre=130, nxt=64, direction="fwd", expect={
+        (0, 0): [(0, F_), (1, P_)],
+        (0, 1): [(0, F_), (1, F_), (2, P_)],
+        (0, 2): [(0, P_), (1, F_), (2, F_), (3, P_)],
+        # ragged rows 192..199: tile 2 would be full if rows past the end counted
+        (0, 3): [(0, P_), (1, P_), (2, P_), (3, P_)],
+    }),
+    # the same tiles seen from the key side (items = key blocks, tiles = query
+    # blocks): the transpose of the table above
+    dict(lengths=[200], mode=4, pre=130, nxt=64, direction="bwd", expect={
+        (0, 0): [(0, F_), (1, F_), (2, P_), (3, P_)],
+        (0, 1): [(0, P_), (1, F_), (2, F_), (3, P_)],
+        (0, 2): [(1, P_), (2, F_), (3, P_)],
+        (0, 3): [(2, P_), (3, P_)],
+    }),
+    # 130 tokens, pre 64, next 0 (the diagonal tile always misses j > i)
+    dict(lengths=[130], mode=4, pre=64, nxt=0, direction="fwd", expect={
+        (0, 0): [(0, P_)],
+        (0, 1): [(0, P_), (1, P_)],
+        (0, 2): [(1, P_), (2, P_)],
+    }),
+    # no mask, 130 queries over 70 keys (a second batch after a zero-length
+    # one): only the complete 64 x 64 tiles are full
+    dict(lengths=[0, 130], lengths_kv=[0, 70], mode=0, pre=0, nxt=0, direction="fwd", expect={
+        (1, 0): [(0, F_), (1, P_)],
+        (1, 1): [(0, F_), (1, P_)],
+        (1, 2): [(0, P_), (1, P_)],
+    }),
+    # the same from the key side: key blocks 0..63 and 64..69 over query blocks
+    dict(lengths=[0, 130], lengths_kv=[0, 70], mode=0, pre=0, nxt=0, direction="bwd", expect={
+        (1, 0): [(0, F_), (1, F_), (2, P_)],
+        (1, 1): [(0, P_), (1, P_), (2, P_)],
+    }),
+]
+
+
+@pytest.mark.parametrize("case", range(len(HAND_TILES)))
+def test_tile_enumerator_hand_tables(case):
+    c = HAND_TILES[case]
+    cu_q = workloads.cumulative(c["lengths"])
+    cu_kv = workloads.cumulative(c.get("lengths_kv", c["lengths"]))
+    got = oracle.enumerate_tiles(cu_q, cu_kv, c["mode"], c["pre"], c["nxt"], 64, 64,
+                                 c["direction"])
+    expect = dict(c["expect"])
+    for key in got:          # items of zero-length sequences are absent from both
+        expect.setdefault(key, [])
+    assert got == expect
+
+
+TILE_MUTATIONS = {
+    "rows_past_the_end_count": ("m &= (rows < sq)[:, None] & (cols < skv)[None, :]",
+                                "m &= (cols < skv)[None, :]"),
+    "keys_past_the_end_count": ("m &= (rows < sq)[:, None] & (cols < skv)[None, :]",
+                                "m &= (rows < sq)[:, None]"),
+    "full_if_any": ("return FULL if mask_block.all() else PARTIAL",
+                    "return FULL if mask_block.any() else PARTIAL"),
+    "bwd_counts_from_query_length": ("-(-skv // block_item), -(-sq // block_tile)",
+                                     "-(-sq // block_item), -(-skv // block_tile)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(TILE_MUTATIONS))
+def test_tile_pins_catch_planted_mistakes(name):
+    import types
+
+    from oracle import tiles as T
+    src = open(T.__file__).read()
+    old, new = TILE_MUTATIONS[name]
+    assert old in src
+    src = src.replace(old, new).replace("from .attention import", "from oracle.attention import")
+    mod = types.ModuleType("tiles_mutant")
+    exec(compile(src, "tiles_mutant", "exec"), mod.__dict__)
+    caught = False
+    for c in HAND_TILES:
+        cu_q = workloads.cumulative(c["lengths"])
+        cu_kv = workloads.cumulative(c.get("lengths_kv", c["lengths"]))
+        got = mod.enumerate_tiles(cu_q, cu_kv, c["mode"], c["pre"], c["nxt"], 64, 64,
+                                  c["direction"])
+        got = {k: v for k, v in got.items() if v}
+        caught |= got != c["expect"]
+    assert caught, name

@@ -157,7 +157,8 @@ swa_status validate(const Problem& p, std::vector<Seq>& seqs, int64_t* end_q, in
     return fail(SWA_ERR_INVALID, "The sparse_mode value should be 0, 2, 3 or 4, but got " +
                                      std::to_string(p.sparse_mode));
   if (!std::isfinite(p.scale)) return fail(SWA_ERR_INVALID, "scale must be finite");
-  if (p.sparse_mode == 4 && p.pre_tokens + p.next_tokens < 0)
+  // the sum of two int64 values, taken without overflow
+  if (p.sparse_mode == 4 && static_cast<__int128>(p.pre_tokens) + p.next_tokens < 0)
     return fail(SWA_ERR_INVALID, "pre_tokens + next_tokens must be >= 0 in sparse_mode 4 "
                                  "(otherwise every row is empty)");
   return parse_seqs(p, seqs, end_q, end_kv);
@@ -194,7 +195,10 @@ Band seq_band(const Problem& p, const Seq& s) {
   switch (p.sparse_mode) {
     case 2: return Band{true, kWide, 0};                 // j <= i
     case 3: return Band{true, kWide, s.skv - s.sq};      // j - i <= Skv - Sq
-    case 4: return Band{true, p.pre_tokens, p.next_tokens};
+    // a band reach beyond kWide covers every key of any sequence (T <= 2^20);
+    // clamping it keeps the schedules' index arithmetic free of overflow
+    case 4: return Band{true, std::max(-kWide, std::min(kWide, p.pre_tokens)),
+                        std::max(-kWide, std::min(kWide, p.next_tokens))};
     default: return Band{false, kWide, kWide};
   }
 }
