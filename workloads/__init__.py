@@ -73,9 +73,12 @@ WORKLOADS = {
         # takes: causal (sparse_mode 2) and 4:1 grouped key/value heads
         Workload("causal_bf16_b1_n16_s16384_d128", torch.bfloat16, 16, 128, 2,
                  1.0 / math.sqrt(128), batch=1, seqlen=16384),
+        # (std 0.5: dK / dV sum four query heads, and at std 1 they reach ~10,
+        # where one bf16 rounding step of the output alone (1/16) exceeds the
+        # absolute tolerance; at 0.5 they stay near unit scale)
         Workload("gqa_swa_bf16_b1_n16kv4_s16384_d128_pre2048_next0", torch.bfloat16, 16, 128, 4,
-                 1.0 / math.sqrt(128), pre_tokens=2048, next_tokens=0, batch=1, seqlen=16384,
-                 num_kv_heads=4),
+                 1.0 / math.sqrt(128), pre_tokens=2048, next_tokens=0, std=0.5, batch=1,
+                 seqlen=16384, num_kv_heads=4),
     ]
 }
 
