@@ -106,8 +106,8 @@ swa_status swa_forward_workspace_size(int64_t num_seqs, int64_t t_q, int64_t t_k
                                       size_t* bytes);
 
 /* Device workspace bytes that swa_backward needs: the tile schedules, the
- * row terms D = rowsum(dY * out) (stored negated for bf16) and lse2, and the
- * fp32 dq accumulator [t_q, num_heads, head_dim] (used by fp32 inputs only). */
+ * row terms D = rowsum(dY * out) (stored negated for bf16) and lse2, and, for
+ * fp32 inputs only, the fp32 dq accumulator [t_q, num_heads, head_dim]. */
 swa_status swa_backward_workspace_size(int64_t num_seqs, int64_t t_q, int64_t t_kv,
                                        int64_t num_heads, int64_t head_dim, int32_t dtype,
                                        size_t* bytes);
@@ -189,6 +189,31 @@ swa_status swa_backward_ex(const void* q, const void* k, const void* v, const vo
                            const void* drop_mask, size_t drop_mask_bytes, double keep_prob,
                            void* dq, void* dk, void* dv, void* workspace,
                            size_t workspace_bytes, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * backward of swa_backward_ex with no workspace argument.  It calls no
+ * hipMalloc, hipFree or other allocating routine; its schedule tables and
+ * row terms live in a fixed scratch array of SWA_NOALLOC_SCRATCH_BYTES
+ * (32 MiB) that the library holds on each device it runs on until the
+ * process ends.  A problem whose backward workspace (swa_backward_workspace_size)
+ * exceeds that size returns SWA_ERR_WORKSPACE and writes nothing.  All calls
+ * on one device share its scratch, which keeps the last call's contents:
+ * calls that overlap in time on one device (on different streams, or from
+ * several threads) race and must not be issued.  The schedule table is
+ * copied from host memory with a synchronous copy, skipped when the device's
+ * scratch already holds the same table.  Arguments, layouts, results and
+ * every other status as in swa_backward_ex. */
+#define SWA_NOALLOC_SCRATCH_BYTES (32u << 20)
+swa_status swa_backward_noalloc(const void* q, const void* k, const void* v, const void* dy,
+                                const void* out, const float* softmax_max,
+                                const float* softmax_sum, const int64_t* cu_seqlens_q,
+                                const int64_t* cu_seqlens_kv, int64_t num_seqs, int64_t t_q,
+                                int64_t t_kv, int64_t num_heads, int64_t num_kv_heads,
+                                int64_t head_dim, int32_t dtype, double scale,
+                                int64_t pre_tokens, int64_t next_tokens, int64_t sparse_mode,
+                                const void* drop_mask, size_t drop_mask_bytes, double keep_prob,
+                                void* dq, void* dk, void* dv, void* stream);
 
 /* Message for the last non-OK status returned on this thread ("" if none).
  * The pointer stays valid until the next call on the same thread. */

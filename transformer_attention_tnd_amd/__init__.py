@@ -19,7 +19,7 @@ import os
 __all__ = [
     "INT_MAX", "SwaError", "load_library", "library_path",
     "swa_forward_workspace_size", "swa_backward_workspace_size",
-    "swa_forward", "swa_backward", "swa_forward_ex", "swa_backward_ex",
+    "swa_forward", "swa_backward", "swa_forward_ex", "swa_backward_ex", "swa_backward_noalloc",
     "swa_last_error", "swa_debug_tile_schedule",
     "swa_profile_enable", "swa_profile_read",
     "forward", "backward", "DTYPE_FP32", "DTYPE_BF16", "DTYPE_FP16",
@@ -56,6 +56,9 @@ _SIGNATURES = {
                         _i64, _i64, _i64, _i32, ctypes.c_double, _i64, _i64, _i64, _vp,
                         ctypes.c_size_t, ctypes.c_double, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                         _vp],
+    "swa_backward_noalloc": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64p, _i64p, _i64, _i64, _i64,
+                             _i64, _i64, _i64, _i32, ctypes.c_double, _i64, _i64, _i64, _vp,
+                             ctypes.c_size_t, ctypes.c_double, _vp, _vp, _vp, _vp],
     "swa_last_error": [],
     "swa_debug_tile_schedule": [_i64p, _i64p, _i64, _i64, _i64, _i64, _i32, _i64, _i64, _i64,
                                 _i32, _i32p, _i64, _i64p, _i32p, _i32p],
@@ -260,6 +263,25 @@ def swa_backward_ex(q, k, v, dy, out, softmax_max, softmax_sum, cu_seqlens_q, cu
         float(scale), int(pre_tokens), int(next_tokens), int(sparse_mode), mp, mb, kp, _ptr(dq),
         _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(q, stream)))
+
+
+def swa_backward_noalloc(q, k, v, dy, out, softmax_max, softmax_sum, cu_seqlens_q,
+                         cu_seqlens_kv, scale, pre_tokens, next_tokens, sparse_mode, drop_mask,
+                         keep_prob, dq, dk, dv, stream=None):
+    """Marshal to swa_backward_noalloc: swa_backward_ex without a workspace
+    (the library's fixed per-device scratch is used; nothing is allocated)."""
+    _shape_checks(q, k, v, extra_q=(dy, out, dq), extra_kv=(dk, dv), grouped=True)
+    _stats_check(q, softmax_max, softmax_sum)
+    cq, nq = _cu_array(cu_seqlens_q)
+    ck, nk = _cu_array(cu_seqlens_kv)
+    if nq != nk:
+        raise ValueError("cu_seqlens_q and cu_seqlens_kv must have the same length")
+    mp, mb, kp = _mask_args(drop_mask, keep_prob, q.device)
+    _check(load_library().swa_backward_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(dy), _ptr(out), _ptr(softmax_max), _ptr(softmax_sum),
+        cq, ck, nq, q.shape[0], k.shape[0], q.shape[1], k.shape[1], q.shape[2], _dtype_code(q),
+        float(scale), int(pre_tokens), int(next_tokens), int(sparse_mode), mp, mb, kp, _ptr(dq),
+        _ptr(dk), _ptr(dv), _stream(q, stream)))
 
 
 def swa_debug_tile_schedule(cu_seqlens_q, cu_seqlens_kv, t_q, t_kv, head_dim, dtype,

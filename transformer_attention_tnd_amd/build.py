@@ -22,6 +22,7 @@ SOURCES = {
     "swa_bwd_kv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "swa_bwd_kv_gqa.hip": [],
     "swa_bwd_dq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "swa_noalloc.hip": [],
 }
 ARCH = os.environ.get("SWA_OFFLOAD_ARCH", "gfx950")
 

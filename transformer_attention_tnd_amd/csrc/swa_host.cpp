@@ -176,18 +176,20 @@ int64_t max_items_dq(int64_t num_seqs, int64_t t_q) {
   return ceil_div(t_q, DQ_BM) + num_seqs;
 }
 
-// Backward workspace: dK/dV items, then dQ items | D | lse2 | dq accumulator.
+// Backward workspace: dK/dV items, then dQ items | D | lse2 | dq accumulator
+// (fp32 inputs only).
 struct BwdLayout {
   size_t items, drow, lse2, dq_acc, total;
 };
 
-BwdLayout bwd_layout(int64_t num_seqs, int64_t t_q, int64_t t_kv, int64_t n, int64_t d) {
+BwdLayout bwd_layout(int64_t num_seqs, int64_t t_q, int64_t t_kv, int64_t n, int64_t d,
+                     int32_t dtype) {
   BwdLayout l;
   l.items = 0;
   l.drow = align256(sizeof(Item) * (max_items_bwd(num_seqs, t_kv) + max_items_dq(num_seqs, t_q)));
   l.lse2 = l.drow + align256(sizeof(float) * t_q * n);
   l.dq_acc = l.lse2 + align256(sizeof(float) * t_q * n);
-  l.total = l.dq_acc + align256(sizeof(float) * t_q * n * d);
+  l.total = l.dq_acc + (dtype == SWA_DTYPE_FP32 ? align256(sizeof(float) * t_q * n * d) : 0);
   return l;
 }
 
@@ -392,6 +394,30 @@ swa_status upload(const std::vector<Item>& items, void* dst, void* stream) {
   return SWA_OK;
 }
 
+// Upload for the entry point that allocates nothing: the table goes straight
+// from host memory into the device's scratch (a copy from pageable memory,
+// which the HIP runtime completes before returning, so no staging buffer is
+// kept); it is skipped when the last table written to that device's scratch
+// is the same, since only this entry point writes the table there.
+struct NoAllocTables {
+  std::mutex mu;
+  std::vector<Item> last[64];
+};
+NoAllocTables g_noalloc;
+
+swa_status upload_noalloc(const std::vector<Item>& items, void* dst, int device, void* stream) {
+  const size_t bytes = sizeof(Item) * items.size();
+  if (bytes == 0) return SWA_OK;
+  std::lock_guard<std::mutex> lock(g_noalloc.mu);
+  std::vector<Item>& last = g_noalloc.last[device];
+  if (last.size() == items.size() && std::memcmp(last.data(), items.data(), bytes) == 0)
+    return SWA_OK;
+  last.clear();  // unknown contents until the copy has succeeded
+  const int e = hip_memcpy_h2d_async(dst, items.data(), bytes, stream);
+  if (e != 0) return fail(SWA_ERR_HIP, hip_error_string(e));
+  last = items;
+  return SWA_OK;
+}
 
 Problem make_problem(const int64_t* cu_q, const int64_t* cu_kv, int64_t num_seqs, int64_t t_q,
                      int64_t t_kv, int64_t n, int64_t nkv, int64_t d, int32_t dtype,
@@ -500,7 +526,7 @@ swa_status swa_backward_workspace_size(int64_t num_seqs, int64_t t_q, int64_t t_
   if (!bytes) return fail(SWA_ERR_NULLPTR, "bytes is NULL");
   swa_status s = check_sizes(num_seqs, t_q, t_kv, num_heads, head_dim, dtype);
   if (s != SWA_OK) return s;
-  *bytes = bwd_layout(num_seqs, t_q, t_kv, num_heads, head_dim).total;
+  *bytes = bwd_layout(num_seqs, t_q, t_kv, num_heads, head_dim, dtype).total;
   return SWA_OK;
 }
 
@@ -574,32 +600,33 @@ swa_status swa_forward(const void* q, const void* k, const void* v, const int64_
                         workspace_bytes, stream);
 }
 
-swa_status swa_backward_ex(const void* q, const void* k, const void* v, const void* dy,
-                           const void* out, const float* softmax_max, const float* softmax_sum,
-                           const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,
-                           int64_t num_seqs, int64_t t_q, int64_t t_kv, int64_t num_heads,
-                           int64_t num_kv_heads, int64_t head_dim, int32_t dtype, double scale,
-                           int64_t pre_tokens, int64_t next_tokens, int64_t sparse_mode,
-                           const void* drop_mask, size_t drop_mask_bytes, double keep_prob,
-                           void* dq, void* dk, void* dv, void* workspace,
-                           size_t workspace_bytes, void* stream) {
-  if (!q || !k || !v || !dy || !out || !softmax_max || !softmax_sum || !dq || !dk || !dv ||
-      !workspace)
-    return fail(SWA_ERR_NULLPTR, "a required tensor or the workspace is NULL");
-  Problem p = make_problem(cu_seqlens_q, cu_seqlens_kv, num_seqs, t_q, t_kv, num_heads,
-                           num_kv_heads, head_dim, dtype, scale, pre_tokens, next_tokens,
-                           sparse_mode);
-  p.drop_mask = drop_mask;
-  p.drop_mask_bytes = drop_mask_bytes;
-  p.keep_prob = keep_prob;
-  std::vector<Seq> seqs;
-  int64_t end_q = 0, end_kv = 0;
-  swa_status s = validate(p, seqs, &end_q, &end_kv);
-  if (s != SWA_OK) return s;
-  const BwdLayout L = bwd_layout(num_seqs, t_q, t_kv, num_heads, head_dim);
-  if (workspace_bytes < L.total)
-    return fail(SWA_ERR_WORKSPACE, "workspace has " + std::to_string(workspace_bytes) +
-                                       " bytes, needs " + std::to_string(L.total));
+}  // extern "C"
+
+namespace swa {
+namespace {
+
+// Backward device arguments (the caller's buffers).
+struct BwdBuffers {
+  const void *q, *k, *v, *dy, *out;
+  const float *smax, *ssum;
+  void *dq, *dk, *dv;
+};
+
+// The backward after validation, over a workspace laid out by L.
+// noalloc_device >= 0: the workspace is that device's fixed scratch, and the
+// schedule is uploaded without staging (upload_noalloc).
+swa_status run_backward(const Problem& p, const std::vector<Seq>& seqs, int64_t end_q,
+                        int64_t end_kv, const BwdBuffers& B, char* ws, const BwdLayout& L,
+                        int noalloc_device, void* stream) {
+  const int64_t t_q = p.t_q, t_kv = p.t_kv, num_heads = p.num_heads;
+  const int64_t num_kv_heads = p.num_kv_heads, head_dim = p.head_dim;
+  const int32_t dtype = p.dtype;
+  const double scale = p.scale;
+  const void *q = B.q, *k = B.k, *v = B.v, *dy = B.dy, *out = B.out;
+  const float *softmax_max = B.smax, *softmax_sum = B.ssum;
+  void *dq = B.dq, *dk = B.dk, *dv = B.dv;
+  const int64_t sparse_mode = p.sparse_mode;
+  swa_status s = SWA_OK;
   // bf16: dK/dV kernel + dQ kernel (no atomics); fp32: one pass with a dq accumulator
   const bool two_pass = dtype == SWA_DTYPE_BF16;
   std::vector<Item> items, dq_items;
@@ -611,8 +638,9 @@ swa_status swa_backward_ex(const void* q, const void* k, const void* v, const vo
   }
   const size_t n_kv_items = items.size();
   items.insert(items.end(), dq_items.begin(), dq_items.end());
-  char* ws = static_cast<char*>(workspace);
-  if ((s = upload(items, ws + L.items, stream)) != SWA_OK) return s;
+  s = noalloc_device >= 0 ? upload_noalloc(items, ws + L.items, noalloc_device, stream)
+                          : upload(items, ws + L.items, stream);
+  if (s != SWA_OK) return s;
   float* drow = reinterpret_cast<float*>(ws + L.drow);
   float* lse2 = reinterpret_cast<float*>(ws + L.lse2);
   float* dq_acc = two_pass ? nullptr : reinterpret_cast<float*>(ws + L.dq_acc);
@@ -688,6 +716,92 @@ swa_status swa_backward_ex(const void* q, const void* k, const void* v, const vo
       return fail(SWA_ERR_HIP, hip_error_string(e));
   }
   return SWA_OK;
+}
+
+// Validation shared by the backward entry points.
+swa_status backward_problem(const void* q, const void* k, const void* v, const void* dy,
+                            const void* out, const float* softmax_max, const float* softmax_sum,
+                            const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,
+                            int64_t num_seqs, int64_t t_q, int64_t t_kv, int64_t num_heads,
+                            int64_t num_kv_heads, int64_t head_dim, int32_t dtype, double scale,
+                            int64_t pre_tokens, int64_t next_tokens, int64_t sparse_mode,
+                            const void* drop_mask, size_t drop_mask_bytes, double keep_prob,
+                            void* dq, void* dk, void* dv, Problem* p, std::vector<Seq>* seqs,
+                            int64_t* end_q, int64_t* end_kv, BwdBuffers* B) {
+  if (!q || !k || !v || !dy || !out || !softmax_max || !softmax_sum || !dq || !dk || !dv)
+    return fail(SWA_ERR_NULLPTR, "a required tensor is NULL");
+  *p = make_problem(cu_seqlens_q, cu_seqlens_kv, num_seqs, t_q, t_kv, num_heads, num_kv_heads,
+                    head_dim, dtype, scale, pre_tokens, next_tokens, sparse_mode);
+  p->drop_mask = drop_mask;
+  p->drop_mask_bytes = drop_mask_bytes;
+  p->keep_prob = keep_prob;
+  *B = BwdBuffers{q, k, v, dy, out, softmax_max, softmax_sum, dq, dk, dv};
+  return validate(*p, *seqs, end_q, end_kv);
+}
+
+}  // namespace
+}  // namespace swa
+
+extern "C" {
+
+swa_status swa_backward_ex(const void* q, const void* k, const void* v, const void* dy,
+                           const void* out, const float* softmax_max, const float* softmax_sum,
+                           const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,
+                           int64_t num_seqs, int64_t t_q, int64_t t_kv, int64_t num_heads,
+                           int64_t num_kv_heads, int64_t head_dim, int32_t dtype, double scale,
+                           int64_t pre_tokens, int64_t next_tokens, int64_t sparse_mode,
+                           const void* drop_mask, size_t drop_mask_bytes, double keep_prob,
+                           void* dq, void* dk, void* dv, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (!workspace) return fail(SWA_ERR_NULLPTR, "the workspace is NULL");
+  Problem p;
+  std::vector<Seq> seqs;
+  int64_t end_q = 0, end_kv = 0;
+  BwdBuffers B;
+  swa_status s = backward_problem(q, k, v, dy, out, softmax_max, softmax_sum, cu_seqlens_q,
+                                  cu_seqlens_kv, num_seqs, t_q, t_kv, num_heads, num_kv_heads,
+                                  head_dim, dtype, scale, pre_tokens, next_tokens, sparse_mode,
+                                  drop_mask, drop_mask_bytes, keep_prob, dq, dk, dv, &p, &seqs,
+                                  &end_q, &end_kv, &B);
+  if (s != SWA_OK) return s;
+  const BwdLayout L = bwd_layout(num_seqs, t_q, t_kv, num_heads, head_dim, dtype);
+  if (workspace_bytes < L.total)
+    return fail(SWA_ERR_WORKSPACE, "workspace has " + std::to_string(workspace_bytes) +
+                                       " bytes, needs " + std::to_string(L.total));
+  return run_backward(p, seqs, end_q, end_kv, B, static_cast<char*>(workspace), L, -1, stream);
+}
+
+swa_status swa_backward_noalloc(const void* q, const void* k, const void* v, const void* dy,
+                                const void* out, const float* softmax_max,
+                                const float* softmax_sum, const int64_t* cu_seqlens_q,
+                                const int64_t* cu_seqlens_kv, int64_t num_seqs, int64_t t_q,
+                                int64_t t_kv, int64_t num_heads, int64_t num_kv_heads,
+                                int64_t head_dim, int32_t dtype, double scale,
+                                int64_t pre_tokens, int64_t next_tokens, int64_t sparse_mode,
+                                const void* drop_mask, size_t drop_mask_bytes, double keep_prob,
+                                void* dq, void* dk, void* dv, void* stream) {
+  Problem p;
+  std::vector<Seq> seqs;
+  int64_t end_q = 0, end_kv = 0;
+  BwdBuffers B;
+  swa_status s = backward_problem(q, k, v, dy, out, softmax_max, softmax_sum, cu_seqlens_q,
+                                  cu_seqlens_kv, num_seqs, t_q, t_kv, num_heads, num_kv_heads,
+                                  head_dim, dtype, scale, pre_tokens, next_tokens, sparse_mode,
+                                  drop_mask, drop_mask_bytes, keep_prob, dq, dk, dv, &p, &seqs,
+                                  &end_q, &end_kv, &B);
+  if (s != SWA_OK) return s;
+  const BwdLayout L = bwd_layout(num_seqs, t_q, t_kv, num_heads, head_dim, dtype);
+  if (L.total > kNoAllocScratchBytes)
+    return fail(SWA_ERR_WORKSPACE,
+                "this problem needs " + std::to_string(L.total) + " bytes of scratch; "
+                "swa_backward_noalloc has a fixed " + std::to_string(kNoAllocScratchBytes) +
+                " bytes per device (call swa_backward_ex with a workspace instead)");
+  void* scratch = nullptr;
+  int device = 0;
+  const int e = noalloc_scratch(stream, &scratch, &device);
+  if (e != 0) return fail(SWA_ERR_HIP, hip_error_string(e));
+  return run_backward(p, seqs, end_q, end_kv, B, static_cast<char*>(scratch), L, device,
+                      stream);
 }
 
 swa_status swa_backward(const void* q, const void* k, const void* v, const void* dy,

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/swa.h"
+
 namespace swa {
 
 // Block sizes.  Forward: a work item is one block of FWD_BM = 2 x FWD_HALF
@@ -161,6 +163,11 @@ int launch_bwd_kv_grouped(const BwdArgs& a, int head_dim, void* stream);
 int launch_bwd_dq(const BwdArgs& a, int head_dim, void* stream);
 int launch_dq_finalize(const FinalizeArgs& a, int dtype, void* stream);
 int launch_fill(const FillArgs& a, void* stream);
+// Size of the fixed device scratch used by swa_backward_noalloc, and the
+// device address of the copy of it on the device of `stream` (null: the
+// current device); looked up once per device (swa_noalloc.hip).
+constexpr size_t kNoAllocScratchBytes = SWA_NOALLOC_SCRATCH_BYTES;
+int noalloc_scratch(void* stream, void** ptr, int* device);
 const char* hip_error_string(int err);
 int hip_memcpy_h2d_async(void* dst, const void* src, size_t bytes, void* stream);
 int hip_pinned_alloc(void** p, size_t bytes);
