@@ -32,6 +32,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <type_traits>
 #include <utility>
 
@@ -507,5 +508,22 @@ int hip_event_elapsed_ms(float* ms, void* start, void* stop) {
   return (int)hipEventElapsedTime(ms, static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(stop));
 }
 int hip_event_destroy(void* ev) { return (int)hipEventDestroy(static_cast<hipEvent_t>(ev)); }
+
+int hip_cu_count(void* stream, int* n) {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  hipError_t e = stream ? hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev)
+                        : hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev < 0 || dev >= 64) return (int)hipErrorInvalidDevice;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v <= 0) {
+    if ((e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+      return (int)e;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  *n = v;
+  return 0;
+}
 
 }  // namespace swa

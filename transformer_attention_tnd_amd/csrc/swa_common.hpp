@@ -130,6 +130,14 @@ __device__ inline void dma16(u32x4 rsrc, uint32_t voff, uint32_t lds_base) {
                : "memory", "m0");
 }
 
+// dma16 with an extra scalar byte offset added to the source address.
+__device__ inline void dma16_so(u32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds_base), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory", "m0");
+}
+
 // 4 bytes per lane from rsrc + voff into LDS at lds_base + 4 * lane (the
 // same asynchronous global->LDS copy, one dword per lane).
 __device__ inline void dma4(u32x4 rsrc, uint32_t voff, uint32_t lds_base) {
@@ -205,6 +213,11 @@ __device__ inline void span_load_lds(const void* base, uint32_t valid_bytes, int
 
 // Wait for this wave's outstanding vector-memory operations (vmcnt = 0).
 __device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// s_waitcnt immediate that waits until at most n (< 64) vector-memory
+// operations are outstanding (vmcnt bits 3:0 and 15:14; expcnt and lgkmcnt
+// left at their maxima).
+constexpr int vmcnt_imm(int n) { return ((n >> 4) << 14) | 0x0F70 | (n & 15); }
 
 // Transposing 64-bit LDS read (ds_read_b64_tr_b16): within each group of 16
 // lanes, lane j receives element (j & 3) of the 4-element chunks addressed by

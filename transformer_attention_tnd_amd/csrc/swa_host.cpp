@@ -186,7 +186,10 @@ BwdLayout bwd_layout(int64_t num_seqs, int64_t t_q, int64_t t_kv, int64_t n, int
                      int32_t dtype) {
   BwdLayout l;
   l.items = 0;
-  l.drow = align256(sizeof(Item) * (max_items_bwd(num_seqs, t_kv) + max_items_dq(num_seqs, t_q)));
+  // schedule: the items of both kernels, their work lists (a code per
+  // (item, head) unit) and the work-list offsets
+  const int64_t n_it = max_items_bwd(num_seqs, t_kv) + max_items_dq(num_seqs, t_q);
+  l.drow = align256(sizeof(Item) * n_it + sizeof(int32_t) * (n_it * n + 2 * (kMaxGrid + 1)));
   l.lse2 = l.drow + align256(sizeof(float) * t_q * n);
   l.dq_acc = l.lse2 + align256(sizeof(float) * t_q * n);
   l.total = l.dq_acc + (dtype == SWA_DTYPE_FP32 ? align256(sizeof(float) * t_q * n * d) : 0);
@@ -352,6 +355,88 @@ void order_items(std::vector<Item>& items) {
                    [](const Item& a, const Item& b) { return cost(a) > cost(b); });
 }
 
+// Static work lists of the persistent kernels: one workgroup per compute
+// unit, each running a list of (item, head) units.  The units, head-major
+// (heads, then the items longest first, so neighbouring blocks of a head are
+// neighbours), are cut into 8 contiguous ranges of equal cost, one per XCD
+// (workgroups are dispatched round-robin over the 8 XCDs, so workgroup w
+// runs on XCD w % 8 and keeps the key/value tiles its range shares in that
+// XCD's L2).  Within a range the units are taken longest first and each goes
+// to the XCD's least loaded workgroup (longest-processing-time-first).
+struct WorkList {
+  std::vector<int32_t> code;  // units grouped by workgroup
+  std::vector<int32_t> off;   // grid + 1 offsets into code
+  int grid = 0;
+};
+
+// Cost of a unit in tile units (x10): masked tiles take about 1.4 times a
+// mask-free one, and each unit adds a switch of about 1.5 tiles.
+int64_t unit_cost(const Item& it, int halves) {
+  int64_t c = 15;
+  for (int h = 0; h < halves; ++h) {
+    const int64_t n = range_len(it.tiles[h]), f = range_len(it.full[h]);
+    c = std::max(c, 15 + 10 * n + 4 * (n - f));
+  }
+  return c;
+}
+
+void build_worklist(const std::vector<Item>& items, int64_t heads, int n_cu, int halves,
+                    WorkList& wl) {
+  const int64_t n_units = static_cast<int64_t>(items.size()) * heads;
+  wl.grid = static_cast<int>(std::min<int64_t>(std::min(n_cu, kMaxGrid), n_units));
+  wl.code.clear();
+  wl.off.assign(wl.grid + 1, 0);
+  if (wl.grid == 0) return;
+  std::vector<int64_t> cost(items.size());
+  for (size_t i = 0; i < items.size(); ++i) cost[i] = unit_cost(items[i], halves);
+  // XCD ranges (all workgroups form one range unless the grid is a multiple of 8)
+  const int nx = wl.grid % 8 == 0 ? 8 : 1;
+  int64_t total = 0;
+  for (int64_t c : cost) total += c * heads;
+  std::vector<std::vector<int32_t>> per_wg(wl.grid);
+  int64_t u = 0, acc = 0;
+  for (int x = 0; x < nx; ++x) {
+    // units [u, end) of the head-major order: cumulative cost up to (x + 1) / nx of the total
+    const int64_t target = total * (x + 1) / nx;
+    std::vector<std::pair<int64_t, int32_t>> range;  // (cost, code)
+    while (u < n_units && (acc < target || x == nx - 1)) {
+      const int64_t head = u / static_cast<int64_t>(items.size());
+      const int64_t item = u - head * static_cast<int64_t>(items.size());
+      range.emplace_back(cost[item], work_code(item, head));
+      acc += cost[item];
+      ++u;
+    }
+    std::stable_sort(range.begin(), range.end(),
+                     [](const std::pair<int64_t, int32_t>& a, const std::pair<int64_t, int32_t>& b) {
+                       return a.first > b.first;
+                     });
+    // least loaded workgroup of this XCD (ties: lowest index)
+    std::vector<std::pair<int64_t, int>> load;  // (load, wg)
+    for (int w = x; w < wl.grid; w += nx) load.emplace_back(0, w);
+    auto cmp = [](const std::pair<int64_t, int>& a, const std::pair<int64_t, int>& b) {
+      return a.first != b.first ? a.first > b.first : a.second > b.second;
+    };
+    std::make_heap(load.begin(), load.end(), cmp);
+    for (const auto& r : range) {
+      std::pop_heap(load.begin(), load.end(), cmp);
+      load.back().first += r.first;
+      per_wg[load.back().second].push_back(r.second);
+      std::push_heap(load.begin(), load.end(), cmp);
+    }
+  }
+  // Each workgroup runs its units shortest first: the workgroups of an XCD
+  // then reach their unit switches (where the next unit's rows are loaded) at
+  // different times instead of all together after equal-length units.
+  for (int w = 0; w < wl.grid; ++w) {
+    std::stable_sort(per_wg[w].begin(), per_wg[w].end(), [&](int32_t a, int32_t b) {
+      return cost[a & 0xffff] < cost[b & 0xffff];
+    });
+    wl.off[w] = static_cast<int32_t>(wl.code.size());
+    wl.code.insert(wl.code.end(), per_wg[w].begin(), per_wg[w].end());
+  }
+  wl.off[wl.grid] = static_cast<int32_t>(wl.code.size());
+}
+
 // Pinned staging buffers for uploading the schedule.  A slot is reused only
 // after the copy recorded behind it has completed.
 struct Staging {
@@ -366,8 +451,7 @@ struct Staging {
 };
 Staging g_staging;
 
-swa_status upload(const std::vector<Item>& items, void* dst, void* stream) {
-  const size_t bytes = sizeof(Item) * items.size();
+swa_status upload(const void* data, size_t bytes, void* dst, void* stream) {
   if (bytes == 0) return SWA_OK;
   std::lock_guard<std::mutex> lock(g_staging.mu);
   Staging::Slot& s = g_staging.slots[g_staging.next++ % 8];
@@ -386,7 +470,7 @@ swa_status upload(const std::vector<Item>& items, void* dst, void* stream) {
   }
   if (!s.event && (e = hip_event_create(&s.event)) != 0)
     return fail(SWA_ERR_HIP, hip_error_string(e));
-  std::memcpy(s.host, items.data(), bytes);
+  std::memcpy(s.host, data, bytes);
   if ((e = hip_memcpy_h2d_async(dst, s.host, bytes, stream)) != 0)
     return fail(SWA_ERR_HIP, hip_error_string(e));
   if ((e = hip_event_record(s.event, stream)) != 0) return fail(SWA_ERR_HIP, hip_error_string(e));
@@ -401,22 +485,29 @@ swa_status upload(const std::vector<Item>& items, void* dst, void* stream) {
 // is the same, since only this entry point writes the table there.
 struct NoAllocTables {
   std::mutex mu;
-  std::vector<Item> last[64];
+  std::vector<uint8_t> last[64];
 };
 NoAllocTables g_noalloc;
 
-swa_status upload_noalloc(const std::vector<Item>& items, void* dst, int device, void* stream) {
-  const size_t bytes = sizeof(Item) * items.size();
-  if (bytes == 0) return SWA_OK;
+swa_status upload_noalloc(const std::vector<uint8_t>& blob, void* dst, int device, void* stream) {
+  if (blob.empty()) return SWA_OK;
   std::lock_guard<std::mutex> lock(g_noalloc.mu);
-  std::vector<Item>& last = g_noalloc.last[device];
-  if (last.size() == items.size() && std::memcmp(last.data(), items.data(), bytes) == 0)
-    return SWA_OK;
+  std::vector<uint8_t>& last = g_noalloc.last[device];
+  if (last == blob) return SWA_OK;
   last.clear();  // unknown contents until the copy has succeeded
-  const int e = hip_memcpy_h2d_async(dst, items.data(), bytes, stream);
+  const int e = hip_memcpy_h2d_async(dst, blob.data(), blob.size(), stream);
   if (e != 0) return fail(SWA_ERR_HIP, hip_error_string(e));
-  last = items;
+  last = blob;
   return SWA_OK;
+}
+
+// Append the bytes of v to a schedule blob; returns the offset where they start.
+template <typename T>
+size_t append(std::vector<uint8_t>& blob, const std::vector<T>& v) {
+  const size_t at = blob.size();
+  blob.resize(at + sizeof(T) * v.size());
+  if (!v.empty()) std::memcpy(blob.data() + at, v.data(), sizeof(T) * v.size());
+  return at;
 }
 
 Problem make_problem(const int64_t* cu_q, const int64_t* cu_kv, int64_t num_seqs, int64_t t_q,
@@ -557,7 +648,8 @@ swa_status swa_forward_ex(const void* q, const void* k, const void* v,
   std::vector<Item> items;
   schedule_forward(p, seqs, items);
   order_items(items);
-  if ((s = upload(items, workspace, stream)) != SWA_OK) return s;
+  if ((s = upload(items.data(), sizeof(Item) * items.size(), workspace, stream)) != SWA_OK)
+    return s;
   int e = 0;
   if (end_q < t_q) {
     FillArgs f{out, static_cast<int64_t>(elem_bytes(dtype)), num_heads * head_dim, end_q, t_q,
@@ -637,14 +729,27 @@ swa_status run_backward(const Problem& p, const std::vector<Seq>& seqs, int64_t 
     order_items(dq_items);
   }
   const size_t n_kv_items = items.size();
-  items.insert(items.end(), dq_items.begin(), dq_items.end());
-  s = noalloc_device >= 0 ? upload_noalloc(items, ws + L.items, noalloc_device, stream)
-                          : upload(items, ws + L.items, stream);
+  // persistent bf16 kernels: work lists over one workgroup per compute unit
+  WorkList wl_kv, wl_dq;
+  int e = 0;
+  if (two_pass) {
+    int n_cu = 0;
+    if ((e = hip_cu_count(stream, &n_cu)) != 0) return fail(SWA_ERR_HIP, hip_error_string(e));
+    build_worklist(items, num_kv_heads, n_cu, 1, wl_kv);
+    build_worklist(dq_items, num_heads, n_cu, 1, wl_dq);
+  }
+  std::vector<uint8_t> blob;
+  append(blob, items);
+  const size_t at_dq_items = append(blob, dq_items);
+  const size_t at_code_kv = append(blob, wl_kv.code), at_code_dq = append(blob, wl_dq.code);
+  const size_t at_off_kv = append(blob, wl_kv.off), at_off_dq = append(blob, wl_dq.off);
+  s = noalloc_device >= 0 ? upload_noalloc(blob, ws + L.items, noalloc_device, stream)
+                          : upload(blob.data(), blob.size(), ws + L.items, stream);
   if (s != SWA_OK) return s;
+  const char* sched = ws + L.items;
   float* drow = reinterpret_cast<float*>(ws + L.drow);
   float* lse2 = reinterpret_cast<float*>(ws + L.lse2);
   float* dq_acc = two_pass ? nullptr : reinterpret_cast<float*>(ws + L.dq_acc);
-  int e = 0;
   if (!two_pass) {  // fp32: D, lse2 and the zeroed dq accumulator from the preprocess kernel
     BwdPreArgs pa{dy, out, softmax_max, softmax_sum, drow, lse2, dq_acc, t_q * num_heads,
                   static_cast<int32_t>(num_heads), static_cast<int32_t>(t_q)};
@@ -667,8 +772,11 @@ swa_status run_backward(const Problem& p, const std::vector<Seq>& seqs, int64_t 
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  a.items = reinterpret_cast<const Item*>(ws + L.items);
+  a.items = reinterpret_cast<const Item*>(sched);
   a.n_items = static_cast<int32_t>(n_kv_items);
+  a.work = reinterpret_cast<const int32_t*>(sched + at_code_kv);
+  a.work_off = reinterpret_cast<const int32_t*>(sched + at_off_kv);
+  a.n_wg = wl_kv.grid;
   a.num_heads = static_cast<int32_t>(num_heads);
   a.num_kv_heads = static_cast<int32_t>(num_kv_heads);
   a.t_q = static_cast<int32_t>(t_q);
@@ -681,8 +789,11 @@ swa_status run_backward(const Problem& p, const std::vector<Seq>& seqs, int64_t 
   // no key), then the dK/dV kernel, which reads them
   if (two_pass && !dq_items.empty()) {
     BwdArgs b = a;
-    b.items = reinterpret_cast<const Item*>(ws + L.items) + n_kv_items;
+    b.items = reinterpret_cast<const Item*>(sched + at_dq_items);
     b.n_items = static_cast<int32_t>(dq_items.size());
+    b.work = reinterpret_cast<const int32_t*>(sched + at_code_dq);
+    b.work_off = reinterpret_cast<const int32_t*>(sched + at_off_dq);
+    b.n_wg = wl_dq.grid;
     if ((e = timed_launch(K_BWD_DQ, stream, [&] {
            return launch_bwd_dq(b, static_cast<int>(head_dim), stream);
          })) != 0)

@@ -65,6 +65,13 @@ struct Problem {
   double keep_prob;
 };
 
+// Persistent kernels: at most this many workgroups (one per compute unit);
+// work list codes are item | head << 16.
+constexpr int kMaxGrid = 1024;
+inline int32_t work_code(int64_t item, int64_t head) {
+  return static_cast<int32_t>(item | (head << 16));
+}
+
 // Dropout operands of the kernels: the packed keep bits as 32-bit words
 // (null: no dropout), their count, and 1 / keep_prob.
 struct DropArgs {
@@ -122,6 +129,11 @@ struct BwdArgs {
   void* dv;
   const Item* items;
   int32_t n_items;
+  // persistent bf16 kernels: workgroup w runs the units
+  // work[work_off[w] .. work_off[w + 1]) (codes item | head << 16) in order
+  const int32_t* work;
+  const int32_t* work_off;
+  int32_t n_wg;          // persistent grid size
   int32_t num_heads;     // query heads (q, dy, dq, D, lse2)
   int32_t num_kv_heads;  // key/value heads (k, v, dk, dv); the dK/dV grid runs over these
   int32_t t_q;
@@ -178,5 +190,7 @@ int hip_event_sync(void* ev);
 int hip_event_create_timed(void** ev);
 int hip_event_elapsed_ms(float* ms, void* start, void* stop);
 int hip_event_destroy(void* ev);
+// compute units of the device of `stream` (null: the current device), cached per device
+int hip_cu_count(void* stream, int* n);
 
 }  // namespace swa
