@@ -9,7 +9,7 @@ namespace swa {
 
 template <bool kDrop>
 static int launch_bwd_kv_t(const BwdArgs& a, int head_dim, void* stream) {
-  const int64_t nwg = (int64_t)a.n_items * a.num_kv_heads;  // one workgroup per key block and head
+  const int64_t nwg = a.n_wg;  // persistent: one workgroup per compute unit
   if (head_dim == 128)
     hipLaunchKernelGGL((swa_bwd_kv_kernel<128, false, kDrop>), dim3((unsigned)nwg), dim3(256), 0,
                        static_cast<hipStream_t>(stream), a);

@@ -30,6 +30,8 @@ namespace swa {
 //     input type.  It runs first and also forms D = rowsum(dY o O) and lse2
 //     of its rows, which this kernel reads (D stored negated: without dropout
 //     the dP chains here start from -D).
+// Both are persistent: one workgroup per compute unit runs a list of
+// (item, head) units from the host (see swa_host.cpp, build_worklist).
 // Both are organised for one wave per SIMD.  The products of a tile form one
 // software pipeline in a fixed order; each LDS operand is read a fixed number
 // of products ahead into a small register ring, and the vector work (the
@@ -69,7 +71,12 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
                 kv_soft_slot(0, 15) + 1 < G_V0 + NV / 2 && kv_soft_slot(1, 15) + 1 < G_V1 + NV / 2,
                 "softmax stages finish before the products that use them");
 
-  __shared__ __attribute__((aligned(1024))) char lds[2 * SLAB];
+  // two slabs (Q | dY of tiles t and t + 1), then the epilogue area (the dK
+  // and dV rows of the 4 waves), so that the slabs can take the next unit's
+  // first tile while a unit's results leave
+  constexpr int EPI = 2 * 4 * 32 * RB;
+  __shared__ __attribute__((aligned(1024))) char lds[2 * SLAB + EPI];
+  char* const epi = lds + 2 * SLAB;
   __shared__ floatx4 lse_s[2][BM / 4];   // lse2 of the tile's rows
   __shared__ floatx4 drow_s[2][BM / 4];  // -D of the tile's rows
   // dropout keep bits of the tile: [slot][key word kw / 32 of the block][row],
@@ -78,15 +85,19 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, h = lane >> 5, c = lane & 31;
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int kvh = L / a.n_items;  // the grid runs over key/value heads
-  const Item it = a.items[L - kvh * a.n_items];
+  const int32_t* work = a.work + a.work_off[blockIdx.x];
+  const int n_units = a.work_off[blockIdx.x + 1] - a.work_off[blockIdx.x];
+  if (n_units <= 0) return;
   // query heads sharing this K / V (kGroups == false: exactly one)
   const int G = kGroups ? a.num_heads / a.num_kv_heads : 1;
   const int64_t ld = (int64_t)a.num_heads * D;       // q / dy row stride
   const int64_t ldkv = (int64_t)a.num_kv_heads * D;  // k / v / dk / dv row stride
-  const bf16* kg = static_cast<const bf16*>(a.k) + (int64_t)it.kv_base * ldkv + kvh * D;
-  const bf16* vg = static_cast<const bf16*>(a.v) + (int64_t)it.kv_base * ldkv + kvh * D;
+  const float c2 = a.scale_log2;
+
+  // the current unit (a block of BN keys of one key/value head)
+  UnitInfo it;
+  int kvh = 0;
+  int lo = 1, hi = 0, flo = 1, fhi = 0;
   // the query head being processed (the group's heads run one after another,
   // accumulating into the same dK / dV registers) and its tensors
   const bf16* qg = nullptr;
@@ -101,37 +112,50 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
     lse_g = a.lse2 + (int64_t)hq * a.t_q + it.q_base;
     drow_g = a.drow + (int64_t)hq * a.t_q + it.q_base;
   };
-  const int kw = it.block * BN + 32 * w + c;  // this lane's key (sequence-local)
-  const int lo = it.tiles[0] & 0xffff, hi = (it.tiles[0] >> 16) & 0xffff;
-  const int flo = it.full[0] & 0xffff, fhi = (it.full[0] >> 16) & 0xffff;
-  const float c2 = a.scale_log2;
+  auto set_unit = [&](const UnitInfo& u) {
+    it = u;
+    kvh = u.head;
+    lo = u.tiles0 & 0xffff;
+    hi = (u.tiles0 >> 16) & 0xffff;
+    flo = u.full0 & 0xffff;
+    fhi = (u.full0 >> 16) & 0xffff;
+  };
+  int kw = 0;  // this lane's key (sequence-local)
 
   floatx16 dk[NDB], dv[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    dk[db] = floatx16{};
-    dv[db] = floatx16{};
-  }
   // B operands of S and dP: lane (column kw) holds K[kw][16t + 8h + e], V likewise
   op_t kr[DSTEPS], vr[DSTEPS];
-  {
-    const bool ok = kw < it.skv;
-    const int64_t off = (int64_t)(ok ? kw : 0) * ldkv + 8 * h;
+  auto load_kv_rows = [&](const UnitInfo& u) {
+    const int key = u.block * BN + 32 * w + c;
+    const bool ok = key < u.skv;
+    const int64_t off = ((int64_t)u.kv_base + (ok ? key : 0)) * ldkv + u.head * D + 8 * h;
+    const bf16* kp = static_cast<const bf16*>(a.k) + off;
+    const bf16* vp = static_cast<const bf16*>(a.v) + off;
 #pragma unroll
     for (int t = 0; t < DSTEPS; ++t) {
-      kr[t] = ok ? M::load(kg + off + 16 * t) : op_t{};
-      vr[t] = ok ? M::load(vg + off + 16 * t) : op_t{};
+      kr[t] = ok ? M::load(kp + 16 * t) : op_t{};
+      vr[t] = ok ? M::load(vp + 16 * t) : op_t{};
     }
-  }
+  };
   // Rows allowed for this lane's key: i in [i_min, i_max] (empty if the key
   // is past the sequence), from the band rule -pre <= kw - i <= next.
-  int i_min = 0, i_max = it.sq - 1;
-  if (a.mode != 0) {  // 64-bit: pre / next may be near the int range
-    const int64_t lo64 = (int64_t)kw - it.band[1], hi64 = (int64_t)kw + it.band[0];
-    i_min = lo64 < 0 ? 0 : (lo64 > it.sq ? it.sq : (int)lo64);
-    i_max = hi64 < i_max ? (hi64 < -1 ? -1 : (int)hi64) : i_max;
-  }
-  if (kw >= it.skv) i_max = -1;
+  int i_min = 0, i_max = -1;
+  auto key_range = [&]() {
+    kw = it.block * BN + 32 * w + c;
+    i_min = 0;
+    i_max = it.sq - 1;
+    if (a.mode != 0) {  // 64-bit: pre / next may be near the int range
+      const int64_t lo64 = (int64_t)kw - it.next, hi64 = (int64_t)kw + it.pre;
+      i_min = lo64 < 0 ? 0 : (lo64 > it.sq ? it.sq : (int)lo64);
+      i_max = hi64 < i_max ? (hi64 < -1 ? -1 : (int)hi64) : i_max;
+    }
+    if (kw >= it.skv) i_max = -1;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      dk[db] = floatx16{};
+      dv[db] = floatx16{};
+    }
+  };
 
   // Lane offsets (slab of the current tile).  Rows 16 apart share a swizzle,
   // so the 32-row block, the 16-row step and Q vs dY are immediate offsets.
@@ -372,49 +396,96 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
       flip(b);
     }
   };
-  for (int gi = 0; gi < G; ++gi) {
-    set_head(kvh * G + gi);
+  // the first query tile of head hq of the current unit into slab 0, with
+  // its lse2 / -D rows (and keep bits); waited for by the caller
+  auto copy_first = [&]() {
     if (lo <= hi) {
       start_copy(lo, 0);
       copy_all();
       load_rows(lo, 0);
     }
-    wait_vmem();
-    // the K / V row loads are complete: an empty use of each register lets
-    // the compiler's wait tracking know it too, so that it does not count
-    // them as outstanding (and wait for the tile copies with them) in the
-    // first products of every tile
+  };
+  // the K / V row loads are complete (the caller waited): an empty use of
+  // each register lets the compiler's wait tracking know it too, so that it
+  // does not count them as outstanding (and wait for the tile copies with
+  // them) in the first products of every tile
+  auto settle_kv = [&]() {
     if constexpr (!kGroups) {
 #pragma unroll
       for (int t = 0; t < DSTEPS; ++t) asm volatile("" : : "a"(kr[t]), "a"(vr[t]));
     }
-    if (lo <= hi) {
-      store_rows(0);
-      __syncthreads();
-    }
-    if (flo <= fhi) {  // masked tiles before and after the mask-free range
-      run(std::true_type{}, lo, flo - 1);
-      run(std::false_type{}, flo, fhi);
-      run(std::true_type{}, fhi + 1, hi);
-    } else {
-      run(std::true_type{}, lo, hi);
-    }
-    // the next head starts on slab 0 again
-    if (lo <= hi && ((hi - lo + 1) & 1)) flip(1);
+  };
+
+  // ---- the first unit: its K / V rows and first tile
+  uint32_t iv_cur = load_unit(a.items, __builtin_amdgcn_readfirstlane(load_code(work, 0)), lane);
+  uint32_t iv_n1 = 0u;
+  if (n_units > 1) iv_n1 = load_unit(a.items, __builtin_amdgcn_readfirstlane(load_code(work, 1)), lane);
+  {
+    const UnitInfo u0 = unit_info(iv_cur);
+    set_unit(u0);
+    set_head(kvh * G);
+    load_kv_rows(u0);
+    copy_first();
+    wait_vmem();
+    settle_kv();
+    if (lo <= hi) store_rows(0);
+    __syncthreads();
   }
 
-  // dK = scale dK^T and dV^T, as whole rows through two LDS slices per wave
-  // (the slabs are free: every copy has landed and the last tile is done)
-  static_assert(2 * 4 * 32 * RB <= 2 * SLAB, "the staging slices fit in the slabs");
-  __syncthreads();
-  {
+  for (int k = 0; k < n_units; ++k) {
+    const bool has_nxt = k + 1 < n_units;
+    // the item of unit k + 2 lands during this unit
+    uint32_t iv_n2 = 0u;
+    if (k + 2 < n_units)
+      iv_n2 = load_unit(a.items, __builtin_amdgcn_readfirstlane(load_code(work, k + 2)), lane);
+    key_range();
+    for (int gi = 0; gi < G; ++gi) {
+      if (gi > 0) {  // the next query head of the group: its first tile
+        set_head(kvh * G + gi);
+        copy_first();
+        wait_vmem();
+        if (lo <= hi) store_rows(0);
+        __syncthreads();
+      }
+      if (flo <= fhi) {  // masked tiles before and after the mask-free range
+        run(std::true_type{}, lo, flo - 1);
+        run(std::false_type{}, flo, fhi);
+        run(std::true_type{}, fhi + 1, hi);
+      } else {
+        run(std::true_type{}, lo, hi);
+      }
+      // the next head (or unit) starts on slab 0 again
+      if (lo <= hi && ((hi - lo + 1) & 1)) flip(1);
+    }
+
+    // Switch: the next unit's K / V rows (the registers of this unit's are
+    // free) and first tile go out before this unit's dK = scale dK^T and dV^T
+    // leave, as whole rows through two LDS slices per wave of the epilogue
+    // area, so the loads' latency overlaps the stores.
     const int row0 = it.block * BN + 32 * w;  // sequence-local key of the wave's slice
-    const int64_t off = ((int64_t)it.kv_base + row0) * ldkv + kvh * D;
-    store_rows_via_lds<NDB>(dk, a.scale, lds + w * 32 * RB, static_cast<bf16*>(a.dk) + off, ldkv,
-                            it.skv - row0);
-    store_rows_via_lds<NDB>(dv, 1.f, lds + (4 + w) * 32 * RB, static_cast<bf16*>(a.dv) + off, ldkv,
-                            it.skv - row0);
+    bf16* const dk_dst = static_cast<bf16*>(a.dk) + ((int64_t)it.kv_base + row0) * ldkv + kvh * D;
+    bf16* const dv_dst = static_cast<bf16*>(a.dv) + ((int64_t)it.kv_base + row0) * ldkv + kvh * D;
+    const int nrows = it.skv - row0;
+    if (has_nxt) {
+      const UnitInfo n = unit_info(iv_n1);
+      load_kv_rows(n);
+      set_unit(n);
+      set_head(kvh * G);
+      copy_first();
+    }
+    static_assert(EPI >= 2 * 4 * 32 * RB, "the epilogue slices fit");
+    store_rows_via_lds<NDB>(dk, a.scale, epi + w * 32 * RB, dk_dst, ldkv, nrows);
+    store_rows_via_lds<NDB>(dv, 1.f, epi + (4 + w) * 32 * RB, dv_dst, ldkv, nrows);
+    if (has_nxt) {
+      wait_vmem();
+      settle_kv();
+      if (lo <= hi) store_rows(0);
+      __syncthreads();
+    }
+    iv_cur = iv_n1;
+    iv_n1 = iv_n2;
   }
+  (void)iv_cur;
 }
 
 }  // namespace swa
