@@ -237,6 +237,18 @@ swa_status swa_debug_tile_schedule(const int64_t* cu_seqlens_q, const int64_t* c
                                    int32_t* rows_out, int64_t capacity, int64_t* n_rows,
                                    int32_t* block_item, int32_t* block_tile);
 
+/* Device cache of tile schedules.  The library keeps device copies of the
+ * schedules (the tile ranges and work lists its kernels read) of up to 64
+ * recent problems per process, 256 MiB at most, keyed by the device, the
+ * cumulative lengths and every size and mask argument; a call on a cached
+ * problem neither rebuilds nor uploads its schedule.  An entry is written
+ * once, by a synchronous copy, before any kernel reads it; evicting one waits
+ * until its device is idle.  Enabled by default; enable = 0 frees every
+ * entry (waiting for the devices to be idle) and makes calls upload their
+ * schedule into the caller's workspace instead, as swa_backward_noalloc
+ * always does into its scratch. */
+swa_status swa_schedule_cache_enable(int32_t enable);
+
 /* Kernel timing (instrumentation for benchmarks).  While enabled, every
  * kernel the library launches is bracketed by two HIP events recorded on its
  * stream.  swa_profile_read waits for the recorded launches of one kernel

@@ -317,6 +317,26 @@ def test_varlen_equals_separate_calls(dev, dtype):
             1.0, g["dq"][sl].float().abs().max().item())
 
 
+def test_schedule_cache_on_and_off_agree(dev):
+    """Schedules from the library's device cache and schedules uploaded into
+    the workspace on every call give identical results (same tables, two
+    places); problems that alternate keep hitting their own cache entries."""
+    probs = [workloads.make_custom([700, 1500, 300], num_heads=4, head_dim=128, sparse_mode=4,
+                                   pre_tokens=300, next_tokens=40),
+             workloads.make_custom([333, 129], num_heads=2, head_dim=64, sparse_mode=2,
+                                   lengths_kv=[400, 129])]
+    try:
+        swa.swa_schedule_cache_enable(False)
+        off = [run_hip(p, dev) for p in probs]
+        swa.swa_schedule_cache_enable(True)
+        on = [run_hip(p, dev) for p in probs + probs]
+    finally:
+        swa.swa_schedule_cache_enable(True)
+    for i, r in enumerate(on):
+        for n in ("out", "smax", "ssum", "dq", "dk", "dv"):
+            assert torch.equal(r[n], off[i % 2][n]), (i, n)
+
+
 def test_bf16_backward_is_deterministic(dev):
     """The bf16 backward uses no atomics: two calls give identical bits."""
     p = workloads.make_custom([700, 1500, 300], num_heads=4, head_dim=128, sparse_mode=4,

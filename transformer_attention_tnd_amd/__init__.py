@@ -21,7 +21,7 @@ __all__ = [
     "swa_forward_workspace_size", "swa_backward_workspace_size",
     "swa_forward", "swa_backward", "swa_forward_ex", "swa_backward_ex", "swa_backward_noalloc",
     "swa_last_error", "swa_debug_tile_schedule",
-    "swa_profile_enable", "swa_profile_read",
+    "swa_schedule_cache_enable", "swa_profile_enable", "swa_profile_read",
     "forward", "backward", "DTYPE_FP32", "DTYPE_BF16", "DTYPE_FP16",
 ]
 
@@ -62,6 +62,7 @@ _SIGNATURES = {
     "swa_last_error": [],
     "swa_debug_tile_schedule": [_i64p, _i64p, _i64, _i64, _i64, _i64, _i32, _i64, _i64, _i64,
                                 _i32, _i32p, _i64, _i64p, _i32p, _i32p],
+    "swa_schedule_cache_enable": [_i32],
     "swa_profile_enable": [_i32],
     "swa_profile_read": [_i32, ctypes.POINTER(ctypes.c_double), _i64p],
 }
@@ -301,6 +302,11 @@ def swa_debug_tile_schedule(cu_seqlens_q, cu_seqlens_kv, t_q, t_kv, head_dim, dt
                                        ctypes.byref(bt)))
     rows = [tuple(buf[4 * i:4 * i + 4]) for i in range(n.value)]
     return rows, bi.value, bt.value
+
+
+def swa_schedule_cache_enable(enable=True):
+    """Turn the library's device cache of tile schedules on or off (off frees it)."""
+    _check(load_library().swa_schedule_cache_enable(1 if enable else 0))
 
 
 def swa_profile_enable(enable=True):

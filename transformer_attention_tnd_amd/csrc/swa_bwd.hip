@@ -509,6 +509,42 @@ int hip_event_elapsed_ms(float* ms, void* start, void* stop) {
 }
 int hip_event_destroy(void* ev) { return (int)hipEventDestroy(static_cast<hipEvent_t>(ev)); }
 
+int hip_stream_device(void* stream, int* dev) {
+  const hipError_t e = stream ? hipStreamGetDevice(static_cast<hipStream_t>(stream), dev)
+                              : hipGetDevice(dev);
+  return (int)e;
+}
+
+namespace {
+// Run f with `device` current, restoring the caller's device afterwards.
+template <typename F>
+int on_device(int device, F&& f) {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return (int)e;
+  if (cur != device && (e = hipSetDevice(device)) != hipSuccess) return (int)e;
+  e = f();
+  if (cur != device) {
+    const hipError_t r = hipSetDevice(cur);
+    if (e == hipSuccess) e = r;
+  }
+  return (int)e;
+}
+}  // namespace
+
+int hip_device_alloc(int device, void** p, size_t bytes) {
+  return on_device(device, [&] { return hipMalloc(p, bytes); });
+}
+int hip_device_free(int device, void* p) {
+  return on_device(device, [&] {
+    const hipError_t e = hipDeviceSynchronize();
+    return e != hipSuccess ? e : hipFree(p);
+  });
+}
+int hip_memcpy_h2d_sync(int device, void* dst, const void* src, size_t bytes) {
+  return on_device(device, [&] { return hipMemcpy(dst, src, bytes, hipMemcpyHostToDevice); });
+}
+
 int hip_cu_count(void* stream, int* n) {
   static std::atomic<int> cache[64];
   int dev = 0;

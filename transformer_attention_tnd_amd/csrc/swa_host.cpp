@@ -510,6 +510,159 @@ size_t append(std::vector<uint8_t>& blob, const std::vector<T>& v) {
   return at;
 }
 
+// ---- schedules as laid out in device memory
+//
+// A call's schedule is one contiguous blob: per kernel, its items, then
+// (persistent kernels) its work-list codes and offsets.
+struct SchedLayout {
+  size_t bytes = 0;
+  size_t at_items[2] = {0, 0};
+  int32_t n_items[2] = {0, 0};
+  size_t at_code[2] = {0, 0}, at_off[2] = {0, 0};
+  int32_t grid[2] = {0, 0};
+};
+
+void build_forward_schedule(const Problem& p, const std::vector<Seq>& seqs,
+                            std::vector<uint8_t>& blob, SchedLayout& L) {
+  std::vector<Item> items;
+  schedule_forward(p, seqs, items);
+  order_items(items);
+  blob.clear();
+  L = SchedLayout{};
+  L.at_items[0] = append(blob, items);
+  L.n_items[0] = static_cast<int32_t>(items.size());
+  L.bytes = blob.size();
+}
+
+// Backward: kernel 0 = dK/dV (fp32: the one-pass kernel), kernel 1 = dQ (bf16).
+void build_backward_schedule(const Problem& p, const std::vector<Seq>& seqs, int n_cu,
+                             std::vector<uint8_t>& blob, SchedLayout& L) {
+  const bool two_pass = p.dtype == SWA_DTYPE_BF16;
+  std::vector<Item> items, dq_items;
+  schedule_backward(p, seqs, items);
+  order_items(items);
+  WorkList wl_kv, wl_dq;
+  if (two_pass) {
+    schedule_dq(p, seqs, dq_items);
+    order_items(dq_items);
+    build_worklist(items, p.num_kv_heads, n_cu, 1, wl_kv);
+    build_worklist(dq_items, p.num_heads, n_cu, 1, wl_dq);
+  }
+  blob.clear();
+  L = SchedLayout{};
+  L.at_items[0] = append(blob, items);
+  L.at_items[1] = append(blob, dq_items);
+  L.at_code[0] = append(blob, wl_kv.code);
+  L.at_code[1] = append(blob, wl_dq.code);
+  L.at_off[0] = append(blob, wl_kv.off);
+  L.at_off[1] = append(blob, wl_dq.off);
+  L.n_items[0] = static_cast<int32_t>(items.size());
+  L.n_items[1] = static_cast<int32_t>(dq_items.size());
+  L.grid[0] = wl_kv.grid;
+  L.grid[1] = wl_dq.grid;
+  L.bytes = blob.size();
+}
+
+// Library-owned device copies of recent schedules, keyed by everything a
+// schedule depends on, so that repeated calls on the same problem neither
+// rebuild nor upload it.  An entry is written once, by a synchronous copy,
+// before any kernel reads it, and is freed only after its device is idle.
+struct ScheduleCache {
+  struct Entry {
+    std::vector<int64_t> key;
+    int device;
+    void* dev;
+    size_t bytes;
+    SchedLayout layout;
+    uint64_t used;
+  };
+  std::mutex mu;
+  std::vector<Entry> entries;
+  uint64_t tick = 0;
+  size_t total = 0;
+  bool enabled = true;
+};
+ScheduleCache g_cache;
+constexpr size_t kCacheEntries = 64;
+constexpr size_t kCacheBytes = size_t(256) << 20;
+
+std::vector<int64_t> schedule_key(int kind, int device, int n_cu, const Problem& p) {
+  std::vector<int64_t> k = {kind, device, n_cu, p.dtype, p.head_dim, p.num_heads,
+                            p.num_kv_heads, p.sparse_mode, p.pre_tokens, p.next_tokens,
+                            p.t_q, p.t_kv, p.num_seqs};
+  k.insert(k.end(), p.cu_q, p.cu_q + p.num_seqs);
+  k.insert(k.end(), p.cu_kv, p.cu_kv + p.num_seqs);
+  return k;
+}
+
+// Device schedule of this call: the cached copy, a new cached copy, or
+// (cache disabled or full of live entries that cannot be freed, allocation
+// failure, or the entry point that allocates nothing) the blob uploaded into
+// `ws` (noalloc_device >= 0: that device's fixed scratch).
+swa_status place_schedule(int kind, const Problem& p, const std::vector<Seq>& seqs, char* ws,
+                          int noalloc_device, void* stream, const char** dev, SchedLayout* L) {
+  int n_cu = 0, device = 0, e = 0;
+  if (kind == 1 && (e = hip_cu_count(stream, &n_cu)) != 0)
+    return fail(SWA_ERR_HIP, hip_error_string(e));
+  if ((e = hip_stream_device(stream, &device)) != 0) return fail(SWA_ERR_HIP, hip_error_string(e));
+  auto build = [&](std::vector<uint8_t>& blob) {
+    if (kind == 0)
+      build_forward_schedule(p, seqs, blob, *L);
+    else
+      build_backward_schedule(p, seqs, n_cu, blob, *L);
+  };
+  std::vector<uint8_t> blob;
+  if (noalloc_device >= 0) {
+    build(blob);
+    *dev = ws;
+    return upload_noalloc(blob, ws, noalloc_device, stream);
+  }
+  std::vector<int64_t> key;
+  {
+    std::lock_guard<std::mutex> lock(g_cache.mu);
+    if (g_cache.enabled) {
+      key = schedule_key(kind, device, n_cu, p);
+      for (ScheduleCache::Entry& en : g_cache.entries) {
+        if (en.device == device && en.key == key) {
+          en.used = ++g_cache.tick;
+          *dev = static_cast<const char*>(en.dev);
+          *L = en.layout;
+          return SWA_OK;
+        }
+      }
+    }
+  }
+  build(blob);
+  if (!key.empty() && !blob.empty() && blob.size() <= kCacheBytes / 4) {
+    std::lock_guard<std::mutex> lock(g_cache.mu);
+    // make room: least recently used first
+    while (!g_cache.entries.empty() && (g_cache.entries.size() >= kCacheEntries ||
+                                        g_cache.total + blob.size() > kCacheBytes)) {
+      size_t lru = 0;
+      for (size_t i = 1; i < g_cache.entries.size(); ++i)
+        if (g_cache.entries[i].used < g_cache.entries[lru].used) lru = i;
+      ScheduleCache::Entry& en = g_cache.entries[lru];
+      if (hip_device_free(en.device, en.dev) != 0) break;
+      g_cache.total -= en.bytes;
+      g_cache.entries.erase(g_cache.entries.begin() + lru);
+    }
+    void* d = nullptr;
+    if (g_cache.entries.size() < kCacheEntries && g_cache.total + blob.size() <= kCacheBytes &&
+        hip_device_alloc(device, &d, blob.size()) == 0) {
+      if (hip_memcpy_h2d_sync(device, d, blob.data(), blob.size()) == 0) {
+        g_cache.entries.push_back(
+            ScheduleCache::Entry{std::move(key), device, d, blob.size(), *L, ++g_cache.tick});
+        g_cache.total += blob.size();
+        *dev = static_cast<const char*>(d);
+        return SWA_OK;
+      }
+      hip_device_free(device, d);
+    }
+  }
+  *dev = ws;
+  return upload(blob.data(), blob.size(), ws, stream);
+}
+
 Problem make_problem(const int64_t* cu_q, const int64_t* cu_kv, int64_t num_seqs, int64_t t_q,
                      int64_t t_kv, int64_t n, int64_t nkv, int64_t d, int32_t dtype,
                      double scale, int64_t pre, int64_t next, int64_t mode) {
@@ -645,10 +798,10 @@ swa_status swa_forward_ex(const void* q, const void* k, const void* v,
   if (workspace_bytes < need)
     return fail(SWA_ERR_WORKSPACE, "workspace has " + std::to_string(workspace_bytes) +
                                        " bytes, needs " + std::to_string(need));
-  std::vector<Item> items;
-  schedule_forward(p, seqs, items);
-  order_items(items);
-  if ((s = upload(items.data(), sizeof(Item) * items.size(), workspace, stream)) != SWA_OK)
+  const char* sched = nullptr;
+  SchedLayout SL;
+  if ((s = place_schedule(0, p, seqs, static_cast<char*>(workspace), -1, stream, &sched, &SL)) !=
+      SWA_OK)
     return s;
   int e = 0;
   if (end_q < t_q) {
@@ -657,7 +810,7 @@ swa_status swa_forward_ex(const void* q, const void* k, const void* v,
     if ((e = timed_launch(K_FILL, stream, [&] { return launch_fill(f, stream); })) != 0)
       return fail(SWA_ERR_HIP, hip_error_string(e));
   }
-  if (!items.empty()) {
+  if (SL.n_items[0] > 0) {
     FwdArgs a;
     a.q = q;
     a.k = k;
@@ -665,8 +818,8 @@ swa_status swa_forward_ex(const void* q, const void* k, const void* v,
     a.out = out;
     a.smax = softmax_max;
     a.ssum = softmax_sum;
-    a.items = static_cast<const Item*>(workspace);
-    a.n_items = static_cast<int32_t>(items.size());
+    a.items = reinterpret_cast<const Item*>(sched + SL.at_items[0]);
+    a.n_items = SL.n_items[0];
     a.num_heads = static_cast<int32_t>(num_heads);
     a.num_kv_heads = static_cast<int32_t>(num_kv_heads);
     a.scale_log2 = static_cast<float>(scale * 1.4426950408889634);
@@ -721,32 +874,12 @@ swa_status run_backward(const Problem& p, const std::vector<Seq>& seqs, int64_t 
   swa_status s = SWA_OK;
   // bf16: dK/dV kernel + dQ kernel (no atomics); fp32: one pass with a dq accumulator
   const bool two_pass = dtype == SWA_DTYPE_BF16;
-  std::vector<Item> items, dq_items;
-  schedule_backward(p, seqs, items);
-  order_items(items);
-  if (two_pass) {
-    schedule_dq(p, seqs, dq_items);
-    order_items(dq_items);
-  }
-  const size_t n_kv_items = items.size();
-  // persistent bf16 kernels: work lists over one workgroup per compute unit
-  WorkList wl_kv, wl_dq;
+  const char* sched = nullptr;
+  SchedLayout SL;
+  if ((s = place_schedule(1, p, seqs, ws + L.items, noalloc_device, stream, &sched, &SL)) != SWA_OK)
+    return s;
+  const size_t n_kv_items = static_cast<size_t>(SL.n_items[0]);
   int e = 0;
-  if (two_pass) {
-    int n_cu = 0;
-    if ((e = hip_cu_count(stream, &n_cu)) != 0) return fail(SWA_ERR_HIP, hip_error_string(e));
-    build_worklist(items, num_kv_heads, n_cu, 1, wl_kv);
-    build_worklist(dq_items, num_heads, n_cu, 1, wl_dq);
-  }
-  std::vector<uint8_t> blob;
-  append(blob, items);
-  const size_t at_dq_items = append(blob, dq_items);
-  const size_t at_code_kv = append(blob, wl_kv.code), at_code_dq = append(blob, wl_dq.code);
-  const size_t at_off_kv = append(blob, wl_kv.off), at_off_dq = append(blob, wl_dq.off);
-  s = noalloc_device >= 0 ? upload_noalloc(blob, ws + L.items, noalloc_device, stream)
-                          : upload(blob.data(), blob.size(), ws + L.items, stream);
-  if (s != SWA_OK) return s;
-  const char* sched = ws + L.items;
   float* drow = reinterpret_cast<float*>(ws + L.drow);
   float* lse2 = reinterpret_cast<float*>(ws + L.lse2);
   float* dq_acc = two_pass ? nullptr : reinterpret_cast<float*>(ws + L.dq_acc);
@@ -772,11 +905,11 @@ swa_status run_backward(const Problem& p, const std::vector<Seq>& seqs, int64_t 
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  a.items = reinterpret_cast<const Item*>(sched);
-  a.n_items = static_cast<int32_t>(n_kv_items);
-  a.work = reinterpret_cast<const int32_t*>(sched + at_code_kv);
-  a.work_off = reinterpret_cast<const int32_t*>(sched + at_off_kv);
-  a.n_wg = wl_kv.grid;
+  a.items = reinterpret_cast<const Item*>(sched + SL.at_items[0]);
+  a.n_items = SL.n_items[0];
+  a.work = reinterpret_cast<const int32_t*>(sched + SL.at_code[0]);
+  a.work_off = reinterpret_cast<const int32_t*>(sched + SL.at_off[0]);
+  a.n_wg = SL.grid[0];
   a.num_heads = static_cast<int32_t>(num_heads);
   a.num_kv_heads = static_cast<int32_t>(num_kv_heads);
   a.t_q = static_cast<int32_t>(t_q);
@@ -787,13 +920,13 @@ swa_status run_backward(const Problem& p, const std::vector<Seq>& seqs, int64_t 
   // bf16: the dQ kernel first (it also writes D and lse2 of every row of every
   // sequence: one item per block of query rows, even when the block attends
   // no key), then the dK/dV kernel, which reads them
-  if (two_pass && !dq_items.empty()) {
+  if (two_pass && SL.n_items[1] > 0) {
     BwdArgs b = a;
-    b.items = reinterpret_cast<const Item*>(sched + at_dq_items);
-    b.n_items = static_cast<int32_t>(dq_items.size());
-    b.work = reinterpret_cast<const int32_t*>(sched + at_code_dq);
-    b.work_off = reinterpret_cast<const int32_t*>(sched + at_off_dq);
-    b.n_wg = wl_dq.grid;
+    b.items = reinterpret_cast<const Item*>(sched + SL.at_items[1]);
+    b.n_items = SL.n_items[1];
+    b.work = reinterpret_cast<const int32_t*>(sched + SL.at_code[1]);
+    b.work_off = reinterpret_cast<const int32_t*>(sched + SL.at_off[1]);
+    b.n_wg = SL.grid[1];
     if ((e = timed_launch(K_BWD_DQ, stream, [&] {
            return launch_bwd_dq(b, static_cast<int>(head_dim), stream);
          })) != 0)
@@ -985,6 +1118,21 @@ swa_status swa_debug_tile_schedule(const int64_t* cu_seqlens_q, const int64_t* c
     }
   }
   *n_rows = n;
+  return SWA_OK;
+}
+
+swa_status swa_schedule_cache_enable(int32_t enable) {
+  std::lock_guard<std::mutex> lock(g_cache.mu);
+  if (!enable) {
+    while (!g_cache.entries.empty()) {
+      ScheduleCache::Entry& en = g_cache.entries.back();
+      const int e = hip_device_free(en.device, en.dev);
+      if (e != 0) return fail(SWA_ERR_HIP, hip_error_string(e));
+      g_cache.total -= en.bytes;
+      g_cache.entries.pop_back();
+    }
+  }
+  g_cache.enabled = enable != 0;
   return SWA_OK;
 }
 

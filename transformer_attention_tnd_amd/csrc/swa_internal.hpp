@@ -192,5 +192,12 @@ int hip_event_elapsed_ms(float* ms, void* start, void* stop);
 int hip_event_destroy(void* ev);
 // compute units of the device of `stream` (null: the current device), cached per device
 int hip_cu_count(void* stream, int* n);
+// device of `stream` (null: the current device)
+int hip_stream_device(void* stream, int* dev);
+// device memory of `device` (allocated with that device current) and a
+// synchronous host-to-device copy into it
+int hip_device_alloc(int device, void** p, size_t bytes);
+int hip_device_free(int device, void* p);  // waits for the device to be idle first
+int hip_memcpy_h2d_sync(int device, void* dst, const void* src, size_t bytes);
 
 }  // namespace swa
