@@ -113,27 +113,111 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
   char* const kbuf0 = lds;
   char* const vbuf0 = lds + NBUF * TB;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6, g = w >> 2, h = lane >> 5, c = lane & 31;
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int head = L / a.n_items;
-  const Item it = a.items[L - head * a.n_items];
   const int64_t ld = (int64_t)a.num_heads * D;       // q / out row stride
   const int64_t ldkv = (int64_t)a.num_kv_heads * D;  // k / v row stride
+  // Persistent: this workgroup runs the units work[0 .. n_units) (an item of
+  // 2 x HALF query rows and a head each, from the host's work list).
+  const int32_t* work = a.work + a.work_off[blockIdx.x];
+  const int n_units = a.work_off[blockIdx.x + 1] - a.work_off[blockIdx.x];
+  if (n_units <= 0) return;
+  // the bf16 kernels without dropout load a unit's Q rows and first tiles
+  // before the previous unit's epilogue, which then stages its rows in the
+  // last two V buffers (the first tiles take the others)
+  constexpr bool kOverlap = sizeof(T) == 2 && !kDrop;
+  // a kernel tile is visited if one of its scheduler tiles is, and mask-free
+  // only if all of them are (keys of a visited kernel tile that the schedule
+  // skips are outside the band: the mask removes them)
+  auto vis = [](int32_t r, int& l, int& u) {
+    const int l0 = r & 0xffff, u0 = (r >> 16) & 0xffff;
+    l = l0 > u0 ? 1 : l0 / SUB;
+    u = l0 > u0 ? 0 : u0 / SUB;
+  };
+  // the loop range of a unit: the union of its two halves' visited tiles
+  auto loop_range = [&](const Item& u, int& l, int& h) {
+    int lo0, hi0, lo1, hi1;
+    vis(u.tiles[0], lo0, hi0);
+    vis(u.tiles[1], lo1, hi1);
+    if (lo0 > hi0) {
+      l = lo1;
+      h = hi1;
+    } else if (lo1 > hi1) {
+      l = lo0;
+      h = hi0;
+    } else {
+      l = lo0 < lo1 ? lo0 : lo1;
+      h = hi0 > hi1 ? hi0 : hi1;
+    }
+  };
+  // Q fragments: B operand of S^T = K Q^T, lane (column qrow) holds
+  // Q[qrow][KSTEP*t + KPL*h + e].
+  op_t qf[QSTEPS];
+  // A unit's Q rows (into qf) and the copies of its first key / value tiles:
+  // K(lo .. lo + NBUF - 2) and V(lo .. lo + NBUF - 3) into buffers 0, 1, ...
+  auto unit_prologue = [&](const Item& u, int hd) {
+    // lane indices formed here (the empty asm keeps them from being computed
+    // once before the unit loop and held in registers across it)
+    int t_ = threadIdx.x;
+    asm volatile("" : "+v"(t_));
+    const int tid = t_, lane = tid & 63, w = tid >> 6, g = w >> 2, h = lane >> 5, c = lane & 31;
+    (void)lane;
+    const int kh = hd / (a.num_heads / a.num_kv_heads);
+    const int qr = u.block * 2 * HALF + HALF * g + 32 * (w & 3) + c;
+    const bool ok = qr < u.sq;
+    const T* qp = static_cast<const T*>(a.q) + ((int64_t)u.q_base + (ok ? qr : 0)) * ld + hd * D;
+#pragma unroll
+    for (int t = 0; t < QSTEPS; ++t) {
+      qf[t] = M::load(qp + KSTEP * t + KPL * h);
+      if (!ok) qf[t] = op_t{};
+    }
+    int ul, uh;
+    loop_range(u, ul, uh);
+    if (ul <= uh) {
+      const T* kgu = static_cast<const T*>(a.k) + (int64_t)u.kv_base * ldkv + kh * D;
+      const T* vgu = static_cast<const T*>(a.v) + (int64_t)u.kv_base * ldkv + kh * D;
+      for (int j = 0; j <= NBUF - 2; ++j)
+        if (ul + j <= uh)
+          tile_load_lds<T, D, BN, NT>(kgu + (int64_t)(ul + j) * BN * ldkv, ldkv,
+                                      u.skv - (ul + j) * BN, kbuf0 + j * TB, tid);
+      for (int j = 0; j <= NBUF - 3; ++j)
+        if (ul + j <= uh)
+          tile_load_lds<T, D, BN, NT>(vgu + (int64_t)(ul + j) * BN * ldkv, ldkv,
+                                      u.skv - (ul + j) * BN, vbuf0 + j * TB, tid);
+    }
+  };
+  // the Q row loads are complete (the caller waited): an empty use of each
+  // register tells the compiler's wait tracking, so that it does not count
+  // them as outstanding in the loop (where a wait for them would also wait
+  // for the tile copies in flight)
+  auto settle_q = [&]() {
+#pragma unroll
+    for (int t = 0; t < QSTEPS; ++t) asm volatile("" : : "v"(qf[t]));
+  };
+  {
+    const int32_t code0 = work[0];
+    unit_prologue(a.items[code0 & 0xffff], code0 >> 16);
+    wait_vmem();
+    settle_q();
+    __syncthreads();
+  }
+
+  for (int ku = 0; ku < n_units; ++ku) {
+  // lane indices formed again per unit (the empty asm keeps the compiler from
+  // hoisting values derived from them out of the unit loop, where they would
+  // hold registers across it)
+  int tid_u = threadIdx.x;
+  asm volatile("" : "+v"(tid_u));
+  const int tid = tid_u;
+  const int lane = tid & 63, w = tid >> 6, g = w >> 2, h = lane >> 5, c = lane & 31;
+  const int32_t code = work[ku];
+  const int head = code >> 16;
+  const Item it = a.items[code & 0xffff];
   const int kvh = head / (a.num_heads / a.num_kv_heads);  // grouped heads share K / V
   const T* qg = static_cast<const T*>(a.q) + (int64_t)it.q_base * ld + head * D;
   const T* kg = static_cast<const T*>(a.k) + (int64_t)it.kv_base * ldkv + kvh * D;
   const T* vg = static_cast<const T*>(a.v) + (int64_t)it.kv_base * ldkv + kvh * D;
   const int qrow = it.block * 2 * HALF + HALF * g + 32 * (w & 3) + c;  // sequence-local
   // this group's tile range, and the union over both groups (the loop range),
-  // in kernel tiles: a kernel tile is visited if one of its scheduler tiles
-  // is, and mask-free only if all of them are (keys of a visited kernel tile
-  // that the schedule skips are outside the band: the mask removes them)
-  auto vis = [](int32_t r, int& l, int& u) {
-    const int l0 = r & 0xffff, u0 = (r >> 16) & 0xffff;
-    l = l0 > u0 ? 1 : l0 / SUB;
-    u = l0 > u0 ? 0 : u0 / SUB;
-  };
+  // in kernel tiles
   auto full = [](int32_t r, int& l, int& u) {
     const int l0 = r & 0xffff, u0 = (r >> 16) & 0xffff;
     l = l0 > u0 ? 1 : (l0 + SUB - 1) / SUB;
@@ -143,21 +227,7 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
   vis(g ? it.tiles[1] : it.tiles[0], mlo, mhi);
   full(g ? it.full[1] : it.full[0], mflo, mfhi);
   int lo, hi;
-  {
-    int lo0, hi0, lo1, hi1;
-    vis(it.tiles[0], lo0, hi0);
-    vis(it.tiles[1], lo1, hi1);
-    if (lo0 > hi0) {
-      lo = lo1;
-      hi = hi1;
-    } else if (lo1 > hi1) {
-      lo = lo0;
-      hi = hi0;
-    } else {
-      lo = lo0 < lo1 ? lo0 : lo1;
-      hi = hi0 > hi1 ? hi0 : hi1;
-    }
-  }
+  loop_range(it, lo, hi);
   const float cs = kPos ? a.scale_log2 : 1.f;  // raw score -> exp2 units
   // Keys allowed for this lane's row: j in [j_min, j_max] (empty past the
   // end).  Formed where a masked tile needs it (the row index passes an
@@ -168,10 +238,10 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
     asm volatile("" : "+v"(q));
     j_min = 0;
     j_max = it.skv - 1;
-    if (a.mode != 0) {  // 64-bit: pre / next may be near the int range
-      const int64_t lo64 = (int64_t)q - it.band[0], hi64 = (int64_t)q + it.band[1];
-      j_min = lo64 < 0 ? 0 : (lo64 > it.skv ? it.skv : (int)lo64);
-      j_max = hi64 < j_max ? (hi64 < -1 ? -1 : (int)hi64) : j_max;
+    if (a.mode != 0) {  // (the item's band is clamped to +-2^30 and q < 2^20: no overflow)
+      const int lo32 = q - it.band[0], hi32 = q + it.band[1];
+      j_min = lo32 < 0 ? 0 : (lo32 > it.skv ? it.skv : lo32);
+      j_max = hi32 < j_max ? (hi32 < -1 ? -1 : hi32) : j_max;
     }
     if (q >= it.sq) j_max = -1;
   };
@@ -196,19 +266,6 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
         mwn[e] = (qrow < it.sq && w + e < a.drop.n_words) ? a.drop.words[w + e] : 0u;
     }
   };
-
-  // Q fragments: B operand of S^T = K Q^T, lane (column qrow) holds
-  // Q[qrow][KSTEP*t + KPL*h + e].
-  op_t qf[QSTEPS];
-  {
-    const bool ok = qrow < it.sq;
-    const T* qp = qg + (int64_t)(ok ? qrow : 0) * ld;
-#pragma unroll
-    for (int t = 0; t < QSTEPS; ++t) {
-      qf[t] = M::load(qp + KSTEP * t + KPL * h);
-      if (!ok) qf[t] = op_t{};
-    }
-  }
 
   auto load_k = [&](int tile, int b) {
     tile_load_lds<T, D, BN, NT>(kg + (int64_t)tile * BN * ldkv, ldkv, it.skv - tile * BN,
@@ -456,16 +513,11 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
   static_assert(2 * NC <= 15, "copy batch fits the wait immediate");
   static_assert(!kSpread || (NBUF - 2) * Dma::PARTS <= 15, "copies in flight fit the wait immediate");
   if (lo <= hi) {
-    load_k(lo, 0);
-    if (NBUF >= 3) {  // K(lo .. lo + NBUF - 2), V(lo .. lo + NBUF - 3)
-      for (int j = 1; j <= NBUF - 2; ++j)
-        if (lo + j <= hi) load_k(lo + j, j);
-      for (int j = 0; j <= NBUF - 3; ++j)
-        if (lo + j <= hi) load_v(lo + j, j);
+    // (the Q rows and the first tiles were loaded by unit_prologue)
+    if constexpr (kDrop) {
+      load_mask(lo);
+      wait_vmem();
     }
-    if constexpr (kDrop) load_mask(lo);
-    wait_vmem();
-    __syncthreads();
     const int nk = hi - lo + 2;
     for (int k = 0; k < nk; ++k) {
       const int t = lo + k;
@@ -508,7 +560,22 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
       if constexpr (kDrop) asm volatile("" : : "v"(mwn[0]), "v"(mwn[1]), "v"(mwn[2]), "v"(mshn));
       __syncthreads();
     }
-    if constexpr (kSpread) wait_vmem();  // the last step's copies (into free buffers)
+    if constexpr (kSpread) {  // the last step's copies (into free buffers), of every wave
+      wait_vmem();
+      __syncthreads();
+    }
+  }
+
+  // the next unit's Q rows and first tiles go out first (bf16 without
+  // dropout) or after this unit's rows have left the K / V area
+  const bool has_next = ku + 1 < n_units;
+  Item nit;
+  int nhead = 0;
+  if (has_next) {
+    const int32_t ncode = work[ku + 1];
+    nhead = ncode >> 16;
+    nit = a.items[ncode & 0xffff];
+    if constexpr (kOverlap) unit_prologue(nit, nhead);
   }
 
   // epilogue: normalise, store out and the statistics of this lane's row
@@ -518,11 +585,13 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
   if constexpr (sizeof(T) == 2) {
     // the wave's 32 rows as whole rows, through its own 32-row slice of the
     // K / V area (free once every wave has left the loop and the last
-    // copies have landed)
+    // copies have landed): with kOverlap the last two V buffers
     static_assert(8 * 32 * RB <= 2 * NBUF * TB, "the staging slices fit in the K / V area");
+    static_assert(!kOverlap || 8 * 32 * RB <= 2 * TB, "the staging slices fit in two V buffers");
+    char* const stage = kOverlap ? vbuf0 + (NBUF - 2) * TB : lds;
     __syncthreads();
     const int row0 = it.block * 2 * HALF + 32 * w;  // sequence-local row of the wave's slice
-    store_rows_via_lds<NDB>(o, inv, lds + w * 32 * RB,
+    store_rows_via_lds<NDB>(o, inv, stage + w * 32 * RB,
                             static_cast<bf16*>(a.out) + ((int64_t)it.q_base + row0) * ld + head * D, ld,
                             it.sq - row0);
   } else if (qrow < it.sq) {
@@ -550,11 +619,21 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
     *reinterpret_cast<floatx4*>(a.smax + so) = mv;
     *reinterpret_cast<floatx4*>(a.ssum + so) = sv;
   }
+  if (has_next) {
+    if constexpr (!kOverlap) {
+      __syncthreads();  // every wave's rows have left the K / V area
+      unit_prologue(nit, nhead);
+    }
+    wait_vmem();
+    settle_q();
+    __syncthreads();
+  }
+  }  // units
 }
 
 template <typename T, int D, bool kDrop>
 static int launch_fwd_t(const FwdArgs& a, void* stream) {
-  const int64_t nwg = (int64_t)a.n_items * a.num_heads;
+  const int64_t nwg = a.n_wg;  // persistent: one workgroup per compute unit
   if (a.scale_log2 > 0.f)
     hipLaunchKernelGGL((swa_fwd_kernel<T, D, true, kDrop>), dim3((unsigned)nwg), dim3(512), 0,
                        static_cast<hipStream_t>(stream), a);

@@ -176,6 +176,13 @@ int64_t max_items_dq(int64_t num_seqs, int64_t t_q) {
   return ceil_div(t_q, DQ_BM) + num_seqs;
 }
 
+// Forward workspace: the schedule (items, a work-list code per (item, head)
+// unit, the work-list offsets).
+size_t fwd_workspace(int64_t num_seqs, int64_t t_q, int64_t n) {
+  const int64_t n_it = max_items_fwd(num_seqs, t_q);
+  return align256(sizeof(Item) * n_it + sizeof(int32_t) * (n_it * n + kMaxGrid + 1));
+}
+
 // Backward workspace: dK/dV items, then dQ items | D | lse2 | dq accumulator
 // (fp32 inputs only).
 struct BwdLayout {
@@ -522,15 +529,20 @@ struct SchedLayout {
   int32_t grid[2] = {0, 0};
 };
 
-void build_forward_schedule(const Problem& p, const std::vector<Seq>& seqs,
+void build_forward_schedule(const Problem& p, const std::vector<Seq>& seqs, int n_cu,
                             std::vector<uint8_t>& blob, SchedLayout& L) {
   std::vector<Item> items;
   schedule_forward(p, seqs, items);
   order_items(items);
+  WorkList wl;
+  build_worklist(items, p.num_heads, n_cu, 2, wl);
   blob.clear();
   L = SchedLayout{};
   L.at_items[0] = append(blob, items);
+  L.at_code[0] = append(blob, wl.code);
+  L.at_off[0] = append(blob, wl.off);
   L.n_items[0] = static_cast<int32_t>(items.size());
+  L.grid[0] = wl.grid;
   L.bytes = blob.size();
 }
 
@@ -602,12 +614,11 @@ std::vector<int64_t> schedule_key(int kind, int device, int n_cu, const Problem&
 swa_status place_schedule(int kind, const Problem& p, const std::vector<Seq>& seqs, char* ws,
                           int noalloc_device, void* stream, const char** dev, SchedLayout* L) {
   int n_cu = 0, device = 0, e = 0;
-  if (kind == 1 && (e = hip_cu_count(stream, &n_cu)) != 0)
-    return fail(SWA_ERR_HIP, hip_error_string(e));
+  if ((e = hip_cu_count(stream, &n_cu)) != 0) return fail(SWA_ERR_HIP, hip_error_string(e));
   if ((e = hip_stream_device(stream, &device)) != 0) return fail(SWA_ERR_HIP, hip_error_string(e));
   auto build = [&](std::vector<uint8_t>& blob) {
     if (kind == 0)
-      build_forward_schedule(p, seqs, blob, *L);
+      build_forward_schedule(p, seqs, n_cu, blob, *L);
     else
       build_backward_schedule(p, seqs, n_cu, blob, *L);
   };
@@ -760,7 +771,7 @@ swa_status swa_forward_workspace_size(int64_t num_seqs, int64_t t_q, int64_t t_k
   if (!bytes) return fail(SWA_ERR_NULLPTR, "bytes is NULL");
   swa_status s = check_sizes(num_seqs, t_q, t_kv, num_heads, head_dim, dtype);
   if (s != SWA_OK) return s;
-  *bytes = align256(sizeof(Item) * max_items_fwd(num_seqs, t_q));
+  *bytes = fwd_workspace(num_seqs, t_q, num_heads);
   return SWA_OK;
 }
 
@@ -794,7 +805,7 @@ swa_status swa_forward_ex(const void* q, const void* k, const void* v,
   int64_t end_q = 0, end_kv = 0;
   swa_status s = validate(p, seqs, &end_q, &end_kv);
   if (s != SWA_OK) return s;
-  const size_t need = align256(sizeof(Item) * max_items_fwd(num_seqs, t_q));
+  const size_t need = fwd_workspace(num_seqs, t_q, num_heads);
   if (workspace_bytes < need)
     return fail(SWA_ERR_WORKSPACE, "workspace has " + std::to_string(workspace_bytes) +
                                        " bytes, needs " + std::to_string(need));
@@ -820,6 +831,9 @@ swa_status swa_forward_ex(const void* q, const void* k, const void* v,
     a.ssum = softmax_sum;
     a.items = reinterpret_cast<const Item*>(sched + SL.at_items[0]);
     a.n_items = SL.n_items[0];
+    a.work = reinterpret_cast<const int32_t*>(sched + SL.at_code[0]);
+    a.work_off = reinterpret_cast<const int32_t*>(sched + SL.at_off[0]);
+    a.n_wg = SL.grid[0];
     a.num_heads = static_cast<int32_t>(num_heads);
     a.num_kv_heads = static_cast<int32_t>(num_kv_heads);
     a.scale_log2 = static_cast<float>(scale * 1.4426950408889634);

@@ -90,6 +90,11 @@ struct FwdArgs {
   float* ssum;
   const Item* items;
   int32_t n_items;
+  // persistent: workgroup w runs the units work[work_off[w] .. work_off[w + 1])
+  // (codes item | head << 16) in order
+  const int32_t* work;
+  const int32_t* work_off;
+  int32_t n_wg;
   int32_t num_heads;     // query heads (q, out, statistics)
   int32_t num_kv_heads;  // key/value heads; query head n reads head n / (num_heads / num_kv_heads)
   float scale_log2;  // scale * log2(e)
