@@ -45,9 +45,11 @@ KERNEL_SOURCES = {
                  _CSRC + "swa_pipe.hpp") + _HDRS,
     "bwd_dq": (_CSRC + "swa_bwd_dq.hip", _CSRC + "swa_pipe.hpp") + _HDRS,
     "bwd_pre": (_CSRC + "swa_bwd.hip",) + _HDRS,
-    "dq_finalize": (_CSRC + "swa_bwd.hip",) + _HDRS,
 }
-BWD_KERNELS = ("bwd_pre", "backward", "bwd_dq", "dq_finalize")
+# fp32 inputs: the dK/dV and dQ kernels are those of swa_bwd.hip
+KERNEL_SOURCES_FP32 = dict(KERNEL_SOURCES, backward=(_CSRC + "swa_bwd.hip",) + _HDRS,
+                           bwd_dq=(_CSRC + "swa_bwd.hip",) + _HDRS)
+BWD_KERNELS = ("bwd_pre", "backward", "bwd_dq")
 
 
 def allowed_pairs(cu_q, cu_kv, mode, pre, nxt):
@@ -82,14 +84,14 @@ def source_hash(files):
     return h.hexdigest()[:16]
 
 
-def traffic_record(kernel, workload):
+def traffic_record(kernel, workload, sources=KERNEL_SOURCES):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path)).get(workload, {}).get(kernel)
-    if not rec or rec.get("source_sha256_16") != source_hash(KERNEL_SOURCES[kernel]):
+    if not rec or rec.get("source_sha256_16") != source_hash(sources[kernel]):
         return None
     return rec.get("bytes_per_launch")
 
@@ -218,20 +220,15 @@ def main():
     ms_step = total_ms / args.steps
     value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
     elem = q.element_size()
-    two_pass = "bwd_dq" in kern
     # algorithmic work per launch of each kernel
     algo = {
         "forward": ("mfma", f_fwd / 1e12, "TFLOP/s"),
-        # two-pass: the dK/dV kernel does S, dP, dV, dK (8*D per pair), the dQ
-        # kernel adds dQ (2*D; its recomputed S and dP are not counted)
-        "backward": ("mfma", (0.8 if two_pass else 1.0) * f_bwd / 1e12, "TFLOP/s"),
+        # the dK/dV kernel does S, dP, dV, dK (8*D per pair), the dQ kernel
+        # adds dQ (2*D; its recomputed S and dP are not counted)
+        "backward": ("mfma", 0.8 * f_bwd / 1e12, "TFLOP/s"),
         "bwd_dq": ("mfma", 0.2 * f_bwd / 1e12, "TFLOP/s"),
-        # per (token, head): read dY, O and two statistics; write D and lse2
-        # (and zero the fp32 dq accumulator in the one-pass backward)
-        "bwd_pre": ("hbm", T * N * (2 * D * elem + 8 + 8 + (0 if two_pass else 4 * D)) / 1e9,
-                    "GB/s"),
-        # per (token, head): read the fp32 accumulator, write dq
-        "dq_finalize": ("hbm", T * N * (4 * D + elem * D) / 1e9, "GB/s"),
+        # fp32, per (token, head): read dY, O and two statistics; write D and lse2
+        "bwd_pre": ("hbm", T * N * (2 * D * elem + 8 + 8) / 1e9, "GB/s"),
     }
     algo = {kk: vv for kk, vv in algo.items() if kk in kern}
     for kind, (bound, work, unit) in algo.items():
@@ -245,7 +242,9 @@ def main():
     achieved = kern[dominant]["achieved"]
     roofline = {"kernel": dominant, "bound": bound, "achieved": achieved, "peak": peak,
                 "unit": unit, "frac": achieved / peak,
-                "traffic": traffic_record(dominant, name) if drop is None else None,
+                "traffic": (traffic_record(dominant, name, KERNEL_SOURCES if q.dtype == torch.bfloat16
+                                           else KERNEL_SOURCES_FP32)
+                            if drop is None else None),
                 "avg_launch_ms": kern[dominant]["avg_ms"]}
 
     cpu = None

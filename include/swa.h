@@ -105,9 +105,9 @@ swa_status swa_forward_workspace_size(int64_t num_seqs, int64_t t_q, int64_t t_k
                                       int64_t num_heads, int64_t head_dim, int32_t dtype,
                                       size_t* bytes);
 
-/* Device workspace bytes that swa_backward needs: the tile schedules, the
- * row terms D = rowsum(dY * out) (stored negated for bf16) and lse2, and, for
- * fp32 inputs only, the fp32 dq accumulator [t_q, num_heads, head_dim]. */
+/* Device workspace bytes that swa_backward needs: the tile schedules and the
+ * row terms D = rowsum(dY * out) (stored negated for bf16) and lse2, 8 bytes
+ * per (token, head) of the queries beside the schedules. */
 swa_status swa_backward_workspace_size(int64_t num_seqs, int64_t t_q, int64_t t_kv,
                                        int64_t num_heads, int64_t head_dim, int32_t dtype,
                                        size_t* bytes);
@@ -128,15 +128,13 @@ swa_status swa_forward(const void* q, const void* k, const void* v,
  * not recompute them) and writes dq, dk, dv.  The sequence, shape and scalar
  * arguments must be those of the forward call that produced out and the
  * statistics; the library cannot check this.
- * bf16 inputs run the two-pass structure of the PyPTO-Gym
+ * Both input types run the two-pass structure of the PyPTO-Gym
  * FlashAttentionScoreGrad article (两趟循环结构): one kernel for dK/dV over
  * key blocks and one for dQ over query blocks, each recomputing P and dS, with
  * no atomics, so every output is bitwise reproducible (the deterministic mode
- * of the explainer, section 6.1); the dQ kernel runs first and also forms the
- * row terms D and lse2 that the dK/dV kernel reads.  fp32 inputs run a
- * preprocess kernel for those terms, then one pass that accumulates dq
- * with fp32 atomics, so its last bits may differ from run to run (the pages'
- * default, explainer section 6.1). */
+ * of the explainer, section 6.1).  bf16: the dQ kernel runs first and also
+ * forms the row terms D and lse2 that the dK/dV kernel reads.  fp32: a
+ * preprocess kernel forms the row terms, then the dK/dV and dQ kernels run. */
 swa_status swa_backward(const void* q, const void* k, const void* v, const void* dy,
                         const void* out, const float* softmax_max, const float* softmax_sum,
                         const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,
@@ -222,8 +220,7 @@ const char* swa_last_error(void);
 /* Host-only: the tile schedule the kernels would run, for checking the
  * skip pattern.  direction 0 = forward (items are query blocks, tiles are
  * key blocks), 1 = backward dK/dV (items are key blocks, tiles are query
- * blocks), 2 = backward dQ of bf16 inputs (items are query blocks, tiles are
- * key blocks).
+ * blocks), 2 = backward dQ (items are query blocks, tiles are key blocks).
  * Writes rows of 4 int32 {sequence, item block, tile, kind} in schedule
  * order, kind 1 = partial (element mask applied), 2 = full (no mask); an
  * item with no visited tile contributes one row {sequence, block, -1, 0}.
@@ -253,9 +250,8 @@ swa_status swa_schedule_cache_enable(int32_t enable);
  * kernel the library launches is bracketed by two HIP events recorded on its
  * stream.  swa_profile_read waits for the recorded launches of one kernel
  * kind, returns their summed duration (ms) and count, and forgets them.
- * Kernel kinds: 0 forward, 1 backward preprocess (fp32), 2 backward main
- * (dK/dV for bf16, one pass for fp32), 3 dq finalize (fp32), 4 zero fill,
- * 5 backward dQ with the row terms (bf16).  Not thread-safe across concurrent streams
+ * Kernel kinds: 0 forward, 1 backward preprocess (fp32), 2 backward dK/dV,
+ * 3 unused, 4 zero fill, 5 backward dQ (for bf16 with the row terms).  Not thread-safe across concurrent streams
  * (launches from all threads are pooled). */
 swa_status swa_profile_enable(int32_t enable);
 swa_status swa_profile_read(int32_t kernel, double* total_ms, int64_t* launches);

@@ -135,14 +135,13 @@ def test_causal_modes_accept_unequal_lengths_and_ignore_pre_next(mode):
     assert a[0] and a == b
 
 
-def test_workspace_sizes_monotone_and_backward_holds_dq_accumulator():
+def test_workspace_sizes_monotone_and_backward_holds_only_schedules_and_row_terms():
     f = swa.swa_forward_workspace_size(1, 16384, 16384, 16, 128, 1)
     b = swa.swa_backward_workspace_size(1, 16384, 16384, 16, 128, 1)
-    # bf16: the schedules and the row terms D and lse2 (fp32 per row and head)
+    # the schedules and the row terms D and lse2 (fp32 per row and head); no
+    # gradient accumulator (the backward has no atomics for either type)
     assert f > 0 and 2 * 16384 * 16 * 4 <= b < 16384 * 16 * 128 * 4
-    # fp32 also holds the fp32 dq accumulator
-    b32 = swa.swa_backward_workspace_size(1, 16384, 16384, 16, 128, 0)
-    assert b32 >= b + 16384 * 16 * 128 * 4
+    assert swa.swa_backward_workspace_size(1, 16384, 16384, 16, 128, 0) == b
     assert swa.swa_backward_workspace_size(4, 16384, 16384, 16, 128, 1) >= b
     with pytest.raises(ValueError):
         swa.swa_forward_workspace_size(1, 16, 16, 2, 80, 1)
@@ -166,7 +165,7 @@ def compare_schedule(cu_q, cu_kv, mode, pre, nxt, direction):
     assert len(order) == len(got)
     for v in got.values():
         assert [t for t, _ in v] == sorted(t for t, _ in v)
-    # directions 0 (forward) and 2 (bf16 backward dQ) walk query blocks over
+    # directions 0 (forward) and 2 (backward dQ) walk query blocks over
     # key tiles, direction 1 (backward dK/dV) key blocks over query tiles
     expect = oracle.enumerate_tiles(cu_q, cu_kv, mode, pre, nxt, bi, bt,
                                     "bwd" if direction == 1 else "fwd")

@@ -67,7 +67,7 @@ _SIGNATURES = {
     "swa_profile_read": [_i32, ctypes.POINTER(ctypes.c_double), _i64p],
 }
 
-KERNEL_KINDS = {"forward": 0, "bwd_pre": 1, "backward": 2, "dq_finalize": 3, "fill": 4, "bwd_dq": 5}
+KERNEL_KINDS = {"forward": 0, "bwd_pre": 1, "backward": 2, "fill": 4, "bwd_dq": 5}
 
 
 class SwaError(RuntimeError):

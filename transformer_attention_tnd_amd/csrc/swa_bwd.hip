@@ -9,26 +9,31 @@
 // in the explainer's stage order (section 8.3): recompute p, dp, ds, then the
 // three products.
 //
-// swa_bwd_pre_kernel: D and the per-row log2-domain normaliser
-//   lse2 = softmax_max * log2(e) + log2(softmax_sum), so that P = exp2(s*c - lse2)
-//   with c = scale * log2(e); for fp32 it also zeroes the dq accumulator.
-// bf16: swa_bwd_kv_kernel (dK, dV, in swa_bwd_kv.hip) and swa_bwd_dq_kernel
-//   (dQ, in swa_bwd_dq.hip), the two-pass structure with no atomics.
-// fp32: swa_bwd_kernel, one pass: one workgroup per (block of 128 keys,
-//   head); each of its 4 waves owns 32 keys and keeps its dK, dV
-//   accumulators in registers while it walks the query tiles of the band.
-//   Scores are formed as S = Q K^T (queries as rows, the wave's keys as
-//   columns), so P and dS come out of the accumulators in the operand layout
-//   of dV^T += dY^T P and dK^T += Q^T dS.  Q and dY tiles go from HBM
-//   straight into swizzled row-major LDS tiles (double-buffered, rows past
-//   the sequence read as zero).  dS is written to LDS and each wave forms dQ
-//   for one 32-wide head-dim block over all 128 keys, added to the fp32
-//   accumulator with atomics (non-deterministic summation order, as the
-//   explainer section 6.1 describes for the default backward);
-//   swa_dq_finalize_kernel then writes dq = scale * dq_acc in the output type.
-//   With grouped heads the workgroup of a key/value head walks the query
-//   heads of its group in turn; with dropout the keep bits of each query tile
-//   are staged in LDS next to lse2 and D.
+// Both input types run the two-pass structure of the PyPTO-Gym article
+// (两趟循环结构): a KV-outer pass for dK, dV and a Q-outer pass for dQ, P and
+// dS recomputed in both, with no atomics, so every output is bitwise
+// reproducible (the deterministic mode of the explainer, section 6.1).
+// bf16: swa_bwd_dq_kernel (dQ; it also forms D and lse2, in swa_bwd_dq.hip),
+//   then swa_bwd_kv_kernel (dK, dV, in swa_bwd_kv.hip).
+// fp32 (this file):
+//   swa_bwd_pre_kernel: D and the per-row log2-domain normaliser
+//     lse2 = softmax_max * log2(e) + log2(softmax_sum), so that
+//     P = exp2(s*c - lse2) with c = scale * log2(e);
+//   swa_bwd_kv_f32_kernel: one workgroup per (block of 128 keys, head); each
+//     of its 4 waves owns 32 keys, keeps their K and V rows and its dK, dV
+//     accumulators in registers and walks the query tiles of the band.
+//     Scores are formed as S = Q K^T (queries as rows, the wave's keys as
+//     columns), so P and dS come out of the accumulators in the operand
+//     layout of dV^T += dY^T P and dK^T += Q^T dS.  Q and dY tiles go from
+//     HBM straight into swizzled row-major LDS tiles (double-buffered, rows
+//     past the sequence read as zero).  With grouped heads the workgroup of a
+//     key/value head walks the query heads of its group in turn; with
+//     dropout the keep bits of each query tile are staged in LDS next to
+//     lse2 and D;
+//   swa_bwd_dq_f32_kernel: one workgroup per (block of 128 query rows,
+//     head); a lane owns one query row (its Q and dY rows in registers as B
+//     operands of S^T = K Q^T and dP^T = V dY^T, its lse2 and D as scalars)
+//     and its column of dQ^T += K^T dS^T, over the key tiles of the band.
 
 #include <hip/hip_runtime.h>
 
@@ -42,6 +47,7 @@ namespace swa {
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void swa_bwd_pre_kernel(BwdPreArgs a) {
+  static_assert(sizeof(T) == 4, "fp32 inputs (bf16 forms D in its dQ kernel)");
   constexpr int EPV = 16 / sizeof(T);
   constexpr int TPR = D / EPV;   // threads per row
   constexpr int RPB = 256 / TPR; // rows per workgroup
@@ -56,11 +62,6 @@ __global__ __launch_bounds__(256) void swa_bwd_pre_kernel(BwdPreArgs a) {
   for (int e = 0; e < EPV; ++e) acc += to_f32(vec_elem<T>(vy, e)) * to_f32(vec_elem<T>(vo, e));
 #pragma unroll
   for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-  if (a.dq_acc) {
-    float* z = a.dq_acc + row * D + ch * EPV;
-#pragma unroll
-    for (int e = 0; e < EPV; e += 4) *reinterpret_cast<floatx4*>(z + e) = floatx4{0.f, 0.f, 0.f, 0.f};
-  }
   if (ch == 0) {
     const int64_t tok = row / a.num_heads, head = row - tok * a.num_heads;
     const int64_t at = head * a.t_q + tok;  // head-major so that a tile's rows are contiguous
@@ -70,41 +71,30 @@ __global__ __launch_bounds__(256) void swa_bwd_pre_kernel(BwdPreArgs a) {
   }
 }
 
-template <typename T, int D, int BM, bool kDrop>
-__global__ __launch_bounds__(256, 1) void swa_bwd_kernel(BwdArgs a) {
+template <int D, int BM, bool kDrop>
+__global__ __launch_bounds__(256, 1) void swa_bwd_kv_f32_kernel(BwdArgs a) {
+  using T = float;
   using M = Mfma<T>;
   using op_t = typename M::op_t;
   constexpr int KPL = M::KPL, KSTEP = M::KSTEP;
   constexpr int BN = BWD_BN;
   constexpr int ES = (int)sizeof(T);
-  constexpr int RB = D * ES;              // Q / dY / K tile row bytes
+  constexpr int RB = D * ES;              // Q / dY tile row bytes
   constexpr int QTB = BM * RB;            // Q or dY tile bytes
-  constexpr int KTB = BN * RB;            // K block bytes
-  constexpr int SRB = BN * ES;            // dS tile row bytes
-  constexpr int STB = BM * SRB;           // dS tile bytes
   constexpr int NDB = D / 32;             // head-dim blocks
   constexpr int QB = BM / 32;             // 32-row query blocks per tile
   constexpr int DSTEPS = D / KSTEP;       // contraction steps over d
   constexpr int QSTEPS = 32 / KSTEP;      // contraction steps per 32 query rows
-  constexpr int KSTEPS = BN / KSTEP;      // contraction steps over the 128 keys
-  constexpr int WPD = 4 / NDB;            // waves sharing one head-dim block in dQ
-  constexpr int TASKS = QB * NDB / 4;     // dQ output blocks per wave
   static_assert(BN == 128 && (BM == 64 || BM == 32), "4 waves x 32 keys; 32/64-row tiles");
-  static_assert(NDB <= 4 && 4 % NDB == 0 && TASKS >= 1 && QB * NDB % 4 == 0, "dQ split");
 
-  // bf16 reads the B operands of S and dP (K and V rows) from LDS; fp32
-  // (one element per lane and step) keeps them in registers instead.
-  constexpr bool kKVlds = sizeof(T) == 2;
-  __shared__ __attribute__((aligned(1024))) char lds[4 * QTB + (kKVlds ? 2 : 1) * KTB + STB];
+  __shared__ __attribute__((aligned(1024))) char lds[4 * QTB];
   __shared__ __attribute__((aligned(16))) float lse_s[2][BM];
   __shared__ __attribute__((aligned(16))) float drow_s[2][BM];
   // dropout keep bits of the tile: [slot][key word kw / 32 of the block][row]
   __shared__ __attribute__((aligned(16))) uint32_t mask_s[kDrop ? 2 * 4 * BM : 1];
-  char* const qbuf = lds;               // Q tiles [2]
-  char* const ybuf = lds + 2 * QTB;     // dY tiles [2]
-  char* const kblk = lds + 4 * QTB;     // K block (operand of S and of dQ)
-  char* const vblk = kblk + KTB;        // V block (operand of dP)
-  char* const sbuf = kKVlds ? vblk + KTB : vblk;  // dS tile
+  // slot b: the Q tile at lds + 2 QTB b, its dY tile right after it
+  char* const qbuf = lds;
+  char* const ybuf = lds + QTB;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, h = lane >> 5, c = lane & 31;
@@ -113,20 +103,18 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kernel(BwdArgs a) {
   const Item it = a.items[L - kvh * a.n_items];
   const int N = a.num_heads;
   const int G = N / a.num_kv_heads;                  // query heads sharing this K / V
-  const int64_t ld = (int64_t)N * D;                 // q / dy / dq row stride
+  const int64_t ld = (int64_t)N * D;                 // q / dy row stride
   const int64_t ldkv = (int64_t)a.num_kv_heads * D;  // k / v / dk / dv row stride
   const T* kg = static_cast<const T*>(a.k) + (int64_t)it.kv_base * ldkv + kvh * D;
   const T* vg = static_cast<const T*>(a.v) + (int64_t)it.kv_base * ldkv + kvh * D;
   // the query head being processed (the group's heads run one after another,
   // accumulating into the same dK / dV) and its tensors
-  int head = kvh * G;
   const T* qg = nullptr;
   const T* dyg = nullptr;
   const float* lse_g = nullptr;
   const float* drow_g = nullptr;
   int64_t drop_head = 0;  // first dropout-mask bit of (sequence, query head)
   auto set_head = [&](int hq) {
-    head = hq;
     drop_head = it.drop_base + (int64_t)hq * it.sq * it.skv;
     qg = static_cast<const T*>(a.q) + (int64_t)it.q_base * ld + hq * D;
     dyg = static_cast<const T*>(a.dy) + (int64_t)it.q_base * ld + hq * D;
@@ -138,13 +126,10 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kernel(BwdArgs a) {
   const int lo = it.tiles[0] & 0xffff, hi = (it.tiles[0] >> 16) & 0xffff;
   const int flo = it.full[0] & 0xffff, fhi = (it.full[0] >> 16) & 0xffff;
   const float c2 = a.scale_log2;
-  const int wd = w % NDB;                 // head-dim block of this wave's dQ
-  const int ld4 = (int)(ld * 4);          // dq_acc row stride in bytes
-  const int dq_lane_off = (4 * h * (int)ld + 32 * wd + c) * 4;
 
-  // fp32: K, V fragments in registers, lane (column kw) holds K[kw][KSTEP*t + h].
-  op_t kf[kKVlds ? 1 : DSTEPS], vf[kKVlds ? 1 : DSTEPS];
-  if constexpr (!kKVlds) {
+  // K, V fragments in registers, lane (column kw) holds K[kw][KSTEP*t + h].
+  op_t kf[DSTEPS], vf[DSTEPS];
+  {
     const bool ok = kw < it.skv;
     const int64_t off = (int64_t)(ok ? kw : 0) * ldkv;
 #pragma unroll
@@ -168,8 +153,8 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kernel(BwdArgs a) {
   uint32_t mreg[2] = {0u, 0u}, msh = 0;
   auto load_qtile = [&](int tile, int b) {
     const int nvalid = it.sq - tile * BM;
-    tile_load_lds<T, D, BM>(qg + (int64_t)tile * BM * ld, ld, nvalid, qbuf + b * QTB, tid);
-    tile_load_lds<T, D, BM>(dyg + (int64_t)tile * BM * ld, ld, nvalid, ybuf + b * QTB, tid);
+    tile_load_lds<T, D, BM>(qg + (int64_t)tile * BM * ld, ld, nvalid, qbuf + 2 * b * QTB, tid);
+    tile_load_lds<T, D, BM>(dyg + (int64_t)tile * BM * ld, ld, nvalid, ybuf + 2 * b * QTB, tid);
     if (tid < 2 * BM) {
       const int row = tid & (BM - 1), i = tile * BM + row;
       if (tid < BM)
@@ -200,31 +185,27 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kernel(BwdArgs a) {
     }
   };
 
-  // Phase A for one query tile: P, dS, dV^T += dY^T P, dK^T += Q^T dS, dS -> LDS.
-  auto phase_a = [&](auto mask_tag, int tile, int b) {
+  // One query tile: P, dS, dV^T += dY^T P, dK^T += Q^T dS.
+  auto tile_step = [&](auto mask_tag, int tile, int b) {
     constexpr bool kMask = decltype(mask_tag)::value;
-    const char* qt = qbuf + b * QTB;
-    const char* yt = ybuf + b * QTB;
+    const char* qt = qbuf + 2 * b * QTB;
+    const char* yt = ybuf + 2 * b * QTB;
 #pragma unroll 1
     for (int qb = 0; qb < QB; ++qb) {
+      // lane indices formed here, per block (an empty asm keeps the compiler
+      // from hoisting the many LDS offsets below out of the loops, which
+      // would keep them all live in registers)
+      int ln = tid;
+      asm volatile("" : "+v"(ln));
+      const int h = (ln >> 5) & 1, c = ln & 31;
       floatx16 s = floatx16{}, dp = floatx16{};
 #pragma unroll
       for (int t = 0; t < DSTEPS; ++t) {
-        // A: query rows of Q / dY; B: this lane's key row of K / V (all in LDS)
+        // A: query rows of Q / dY (LDS); B: this lane's key row of K / V (registers)
         const int off = tile_off<RB>(32 * qb + c, (KSTEP * t + KPL * h) * ES);
-        op_t kb, vb;
-        if constexpr (kKVlds) {
-          const int koff = tile_off<RB>(32 * w + c, (KSTEP * t + KPL * h) * ES);
-          kb = M::load(reinterpret_cast<const T*>(kblk + koff));
-          vb = M::load(reinterpret_cast<const T*>(vblk + koff));
-        } else {
-          kb = kf[t];
-          vb = vf[t];
-        }
-        s = M::mma(M::load(reinterpret_cast<const T*>(qt + off)), kb, s);
-        dp = M::mma(M::load(reinterpret_cast<const T*>(yt + off)), vb, dp);
+        s = M::mma(M::load(reinterpret_cast<const T*>(qt + off)), kf[t], s);
+        dp = M::mma(M::load(reinterpret_cast<const T*>(yt + off)), vf[t], dp);
       }
-      if constexpr (kKVlds) interleave_lds_mfma<2 * DSTEPS, 2, 2>();
       // rows of this lane: 32*qb + c_row(r, h); P = exp2(s*c - lse2), dS = P (dP - D)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -260,41 +241,11 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kernel(BwdArgs a) {
         const op_t sb = M::pack(dp, t2);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          op_t ya, qa;
-          if constexpr (sizeof(T) == 2) {
-            ya = tr_operand<RB, true>(yt, 32 * qb + KSTEP * t2, db, lane);
-            qa = tr_operand<RB, true>(qt, 32 * qb + KSTEP * t2, db, lane);
-          } else {
-            const int row = 32 * qb + row_of_slot<T>(KSTEP * t2 + KPL * h);
-            const int off = tile_off<RB>(row, (32 * db + c) * ES);
-            ya = *reinterpret_cast<const T*>(yt + off);
-            qa = *reinterpret_cast<const T*>(qt + off);
-          }
-          dv[db] = M::mma(ya, pb, dv[db]);
-          dk[db] = M::mma(qa, sb, dk[db]);
+          const int row = 32 * qb + row_of_slot<T>(KSTEP * t2 + KPL * h);
+          const int off = tile_off<RB>(row, (32 * db + c) * ES);
+          dv[db] = M::mma(*reinterpret_cast<const T*>(yt + off), pb, dv[db]);
+          dk[db] = M::mma(*reinterpret_cast<const T*>(qt + off), sb, dk[db]);
         }
-      }
-      // dS (rounded to the input type) for the dQ product
-      if constexpr (sizeof(T) == 2) {
-        // Adjacent lanes hold adjacent keys of the same rows: swap one value
-        // with the neighbour lane so that each lane stores a pair of keys of
-        // one row as a single 32-bit word (even lanes rows r, odd lanes r+1).
-        const bool odd = c & 1;
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const uint32_t mine_r = __builtin_bit_cast(uint16_t, static_cast<T>(dp[r]));
-          const uint32_t mine_r1 = __builtin_bit_cast(uint16_t, static_cast<T>(dp[r + 1]));
-          const uint32_t give = odd ? mine_r : mine_r1;
-          const uint32_t got = __builtin_amdgcn_mov_dpp((int)give, 0xB1, 0xF, 0xF, false);
-          const uint32_t word = odd ? (got | (mine_r1 << 16)) : (mine_r | (got << 16));
-          const int row = 32 * qb + c_row(odd ? r + 1 : r, h);
-          *reinterpret_cast<uint32_t*>(sbuf + tile_off<SRB>(row, (32 * w + (c & ~1)) * ES)) = word;
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          *reinterpret_cast<T*>(sbuf + tile_off<SRB>(32 * qb + c_row(r, h), (32 * w + c) * ES)) =
-              static_cast<T>(dp[r]);
       }
     }
   };
@@ -302,11 +253,6 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kernel(BwdArgs a) {
   for (int gi = 0; gi < G; ++gi) {
     set_head(kvh * G + gi);
     if (lo <= hi) {
-      if (gi == 0) {
-        tile_load_lds<T, D, BN>(kg + (int64_t)kb0 * ldkv, ldkv, it.skv - kb0, kblk, tid);
-        if constexpr (kKVlds)
-          tile_load_lds<T, D, BN>(vg + (int64_t)kb0 * ldkv, ldkv, it.skv - kb0, vblk, tid);
-      }
       load_qtile(lo, 0);
       store_rows(0);
       wait_vmem();
@@ -316,46 +262,13 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kernel(BwdArgs a) {
       const int b = (tile - lo) & 1;
       if (tile < hi) load_qtile(tile + 1, b ^ 1);
       if (tile < flo || tile > fhi)
-        phase_a(std::true_type{}, tile, b);
+        tile_step(std::true_type{}, tile, b);
       else
-        phase_a(std::false_type{}, tile, b);
-      __syncthreads();
-
-      // dQ[32 rows x 32 d] = dS[rows, 128 keys] K[128 keys, d-block wd]
-      const int nrows = it.sq - tile * BM < BM ? it.sq - tile * BM : BM;
-      const bool full_rows = nrows == BM;
-      const __amdgpu_buffer_rsrc_t dq_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-          a.dq_acc + ((int64_t)it.q_base + tile * BM) * ld + head * D, (short)0,
-          (int)(((int64_t)(nrows - 1) * ld + D) * 4), 0x00020000);
-  #pragma unroll
-      for (int k = 0; k < TASKS; ++k) {
-        const int qb = w / NDB + k * WPD;
-        floatx16 acc = floatx16{};
-  #pragma unroll
-        for (int t = 0; t < KSTEPS; ++t) {
-          const op_t sa = M::load(reinterpret_cast<const T*>(
-              sbuf + tile_off<SRB>(32 * qb + c, (KSTEP * t + KPL * h) * ES)));
-          op_t kb;
-          if constexpr (sizeof(T) == 2)
-            kb = tr_operand<RB, false>(kblk, KSTEP * t, wd, lane);
-          else
-            kb = *reinterpret_cast<const T*>(kblk + tile_off<RB>(KSTEP * t + h, (32 * wd + c) * ES));
-          acc = M::mma(sa, kb, acc);
-        }
-        // buffer atomics: wave-uniform row offset in an SGPR, one lane offset
-  #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int i = tile * BM + 32 * qb + c_row(r, h);
-          const int soff = (32 * qb + 8 * (r >> 2) + (r & 3)) * ld4;
-          if (full_rows || i < it.sq)
-            __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[r], dq_rsrc, dq_lane_off, soff, 0);
-        }
-      }
+        tile_step(std::false_type{}, tile, b);
       if (tile < hi) store_rows(b ^ 1);
       wait_vmem();
       __syncthreads();
     }
-
   }  // query heads of the group
 
   // epilogue: this lane's key column of dK^T / dV^T
@@ -368,48 +281,163 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kernel(BwdArgs a) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d0 = 32 * db + 8 * g + 4 * h;
-        if constexpr (sizeof(T) == 2) {
-          bf16x4 k4, v4;
+        floatx4 k4, v4;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            k4[e] = static_cast<bf16>(dk[db][4 * g + e] * a.scale);
-            v4[e] = static_cast<bf16>(dv[db][4 * g + e]);
-          }
-          *reinterpret_cast<bf16x4*>(dkp + d0) = k4;
-          *reinterpret_cast<bf16x4*>(dvp + d0) = v4;
-        } else {
-          floatx4 k4, v4;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            k4[e] = dk[db][4 * g + e] * a.scale;
-            v4[e] = dv[db][4 * g + e];
-          }
-          *reinterpret_cast<floatx4*>(dkp + d0) = k4;
-          *reinterpret_cast<floatx4*>(dvp + d0) = v4;
+        for (int e = 0; e < 4; ++e) {
+          k4[e] = dk[db][4 * g + e] * a.scale;
+          v4[e] = dv[db][4 * g + e];
         }
+        *reinterpret_cast<floatx4*>(dkp + d0) = k4;
+        *reinterpret_cast<floatx4*>(dvp + d0) = v4;
       }
     }
   }
 }
 
-template <typename T>
-__global__ __launch_bounds__(256) void swa_dq_finalize_kernel(FinalizeArgs a) {
-  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
-  if (i >= a.n) return;
-  const floatx4 x0 = *reinterpret_cast<const floatx4*>(a.dq_acc + i);
-  const floatx4 x1 = *reinterpret_cast<const floatx4*>(a.dq_acc + i + 4);
-  T* out = static_cast<T*>(a.dq) + i;
-  if constexpr (sizeof(T) == 2) {
-    bf16x8 v;
+template <int D, bool kDrop>
+__global__ __launch_bounds__(256, 1) void swa_bwd_dq_f32_kernel(BwdArgs a) {
+  using M = Mfma<float>;
+  constexpr int BQ = 128;          // query rows per workgroup
+  constexpr int BN = FWD_BN;       // keys per tile
+  constexpr int RB = D * 4;        // row bytes
+  constexpr int KTB = BN * RB;     // K or V tile bytes
+  constexpr int NDB = D / 32;      // head-dim blocks
+  constexpr int DSTEPS = D / 2;    // contraction steps over d (2 per step)
+  static_assert(BN == 64, "two 32-key blocks per tile");
+  __shared__ __attribute__((aligned(1024))) char lds[4 * KTB];  // K[2] | V[2]
+  char* const kbuf = lds;
+  char* const vbuf = lds + 2 * KTB;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, h = lane >> 5, c = lane & 31;
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int head = L / a.n_items;
+  const Item it = a.items[L - head * a.n_items];
+  const int64_t ld = (int64_t)a.num_heads * D;       // q / dy / dq row stride
+  const int64_t ldkv = (int64_t)a.num_kv_heads * D;  // k / v row stride
+  const int kvh = head / (a.num_heads / a.num_kv_heads);  // grouped heads share K / V
+  const float* kg = static_cast<const float*>(a.k) + (int64_t)it.kv_base * ldkv + kvh * D;
+  const float* vg = static_cast<const float*>(a.v) + (int64_t)it.kv_base * ldkv + kvh * D;
+  const int qrow = it.block * BQ + 32 * w + c;  // this lane's query row (sequence-local)
+  const bool row_ok = qrow < it.sq;
+  const int lo = it.tiles[0] & 0xffff, hi = (it.tiles[0] >> 16) & 0xffff;
+  const float c2 = a.scale_log2;
+
+  // B operands of S^T = K Q^T and dP^T = V dY^T: lane (column qrow) holds
+  // Q[qrow][2t + h], dY likewise; the row's lse2 and D
+  float qf[DSTEPS], yf[DSTEPS];
+  {
+    const int64_t off = ((int64_t)it.q_base + (row_ok ? qrow : 0)) * ld + head * D;
+    const float* qp = static_cast<const float*>(a.q) + off;
+    const float* yp = static_cast<const float*>(a.dy) + off;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      v[e] = static_cast<bf16>(x0[e] * a.scale);
-      v[4 + e] = static_cast<bf16>(x1[e] * a.scale);
+    for (int t4 = 0; t4 < D / 4; ++t4) {
+      const floatx4 q4 = *reinterpret_cast<const floatx4*>(qp + 4 * t4);
+      const floatx4 y4 = *reinterpret_cast<const floatx4*>(yp + 4 * t4);
+      qf[2 * t4] = row_ok ? q4[h] : 0.f;
+      qf[2 * t4 + 1] = row_ok ? q4[2 + h] : 0.f;
+      yf[2 * t4] = row_ok ? y4[h] : 0.f;
+      yf[2 * t4 + 1] = row_ok ? y4[2 + h] : 0.f;
     }
-    *reinterpret_cast<bf16x8*>(out) = v;
-  } else {
-    *reinterpret_cast<floatx4*>(out) = x0 * a.scale;
-    *reinterpret_cast<floatx4*>(out + 4) = x1 * a.scale;
+  }
+  const int64_t at = (int64_t)head * a.t_q + it.q_base + (row_ok ? qrow : 0);
+  const float lse = row_ok ? a.lse2[at] : INFINITY;  // rows past the end: P = 0
+  const float drow = row_ok ? a.drow[at] : 0.f;
+  // keys allowed for this lane's row: j in [j_min, j_max]
+  int j_min = 0, j_max = it.skv - 1;
+  if (a.mode != 0) {  // (the item's band is clamped to +-2^30 and qrow < 2^20: no overflow)
+    const int lo32 = qrow - it.band[0], hi32 = qrow + it.band[1];
+    j_min = lo32 < 0 ? 0 : (lo32 > it.skv ? it.skv : lo32);
+    j_max = hi32 < j_max ? (hi32 < -1 ? -1 : hi32) : j_max;
+  }
+  if (!row_ok) j_max = -1;
+  const int64_t drop_row = kDrop ? it.drop_base + (int64_t)head * it.sq * it.skv +
+                                       (int64_t)(row_ok ? qrow : 0) * it.skv
+                                 : 0;
+
+  auto load_tile = [&](int tile, int b) {
+    tile_load_lds<float, D, BN>(kg + (int64_t)tile * BN * ldkv, ldkv, it.skv - tile * BN,
+                                kbuf + b * KTB, tid);
+    tile_load_lds<float, D, BN>(vg + (int64_t)tile * BN * ldkv, ldkv, it.skv - tile * BN,
+                                vbuf + b * KTB, tid);
+  };
+
+  floatx16 acc[NDB];  // dQ^T: rows = head dim 32 db + c_row(r, h), column = this lane's row
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = floatx16{};
+  if (lo <= hi) {
+    load_tile(lo, 0);
+    wait_vmem();
+    __syncthreads();
+  }
+  for (int tile = lo; tile <= hi; ++tile) {
+    const int b = (tile - lo) & 1;
+    if (tile < hi) load_tile(tile + 1, b ^ 1);
+    const char* kt = kbuf + b * KTB;
+    const char* vt = vbuf + b * KTB;
+    // keep bits of this lane's row for the tile's 64 keys (bit k = key 64 tile + k)
+    uint32_t keep[2] = {0u, 0u};
+    if constexpr (kDrop) {
+      const int64_t bit = drop_row + (int64_t)tile * BN, wd = bit >> 5;
+      uint32_t mw[3];
+#pragma unroll
+      for (int e = 0; e < 3; ++e) mw[e] = (row_ok && wd + e < a.drop.n_words) ? a.drop.words[wd + e] : 0u;
+      const uint32_t sh = (uint32_t)(bit & 31);
+      keep[0] = __builtin_amdgcn_alignbit(mw[1], mw[0], sh);
+      keep[1] = __builtin_amdgcn_alignbit(mw[2], mw[1], sh);
+    }
+#pragma unroll 1
+    for (int jb = 0; jb < 2; ++jb) {
+      // S^T, dP^T of keys 32 jb + c_row(r, h) (rows) and this lane's query (column)
+      floatx16 s = floatx16{}, dp = floatx16{};
+#pragma unroll
+      for (int t = 0; t < DSTEPS; ++t) {
+        const int off = tile_off<RB>(32 * jb + c, (2 * t + h) * 4);
+        s = M::mma(*reinterpret_cast<const float*>(kt + off), qf[t], s);
+        dp = M::mma(*reinterpret_cast<const float*>(vt + off), yf[t], dp);
+      }
+      // P = exp2(s c - lse2), masked; dS = P (dP - D) (with dropout, P (Z dP / kp - D))
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int jt = 32 * jb + c_row(r, h);  // key within the tile
+        const int j = tile * BN + jt;
+        float p = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -lse));
+        p = (j >= j_min && j <= j_max) ? p : 0.f;
+        if constexpr (kDrop) {
+          const bool kept = (keep[jb] >> c_row(r, h)) & 1u;
+          dp[r] = p * ((kept ? dp[r] * a.drop.rkp : 0.f) - drow);
+        } else {
+          dp[r] = p * (dp[r] - drow);
+        }
+      }
+      // dQ^T += K^T dS^T: step t2 takes dS^T register t2, the key c_row(t2, h)
+      // of the block, so the K^T operand of lane l is K[that key][32 db + l % 32]
+#pragma unroll
+      for (int t2 = 0; t2 < 16; ++t2) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const float ka = *reinterpret_cast<const float*>(
+              kt + tile_off<RB>(32 * jb + c_row(t2, h), (32 * db + c) * 4));
+          acc[db] = M::mma(ka, dp[t2], acc[db]);
+        }
+      }
+    }
+    wait_vmem();
+    __syncthreads();
+  }
+  // dq = scale dQ (zero for a row that attends no key)
+  if (row_ok) {
+    float* op = static_cast<float*>(a.dq) + ((int64_t)it.q_base + qrow) * ld + head * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        floatx4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = acc[db][4 * g + e] * a.scale;
+        *reinterpret_cast<floatx4*>(op + 32 * db + 8 * g + 4 * h) = v4;
+      }
+    }
   }
 }
 
@@ -430,27 +458,23 @@ __global__ __launch_bounds__(256) void swa_fill_kernel(FillArgs a) {
   }
 }
 
-template <typename T, int D>
+template <int D>
 static int launch_pre_t(const BwdPreArgs& a, void* stream) {
-  constexpr int RPB = 256 / (D / (16 / sizeof(T)));
+  constexpr int RPB = 256 / (D / 4);
   const int64_t nwg = (a.rows + RPB - 1) / RPB;
-  hipLaunchKernelGGL((swa_bwd_pre_kernel<T, D>), dim3((unsigned)nwg), dim3(256), 0,
+  hipLaunchKernelGGL((swa_bwd_pre_kernel<float, D>), dim3((unsigned)nwg), dim3(256), 0,
                      static_cast<hipStream_t>(stream), a);
   return (int)hipGetLastError();
 }
 
-int launch_bwd_pre(const BwdPreArgs& a, int dtype, int head_dim, void* stream) {
-  if (dtype == 1) return head_dim == 128 ? launch_pre_t<bf16, 128>(a, stream)
-                                         : launch_pre_t<bf16, 64>(a, stream);
-  return head_dim == 128 ? launch_pre_t<float, 128>(a, stream)
-                         : launch_pre_t<float, 64>(a, stream);
+int launch_bwd_pre(const BwdPreArgs& a, int head_dim, void* stream) {
+  return head_dim == 128 ? launch_pre_t<128>(a, stream) : launch_pre_t<64>(a, stream);
 }
 
-template <typename T, int D, bool kDrop>
-static int launch_bwd_t(const BwdArgs& a, void* stream) {
+template <int D, bool kDrop>
+static int launch_kv_f32_t(const BwdArgs& a, void* stream) {
   const int64_t nwg = (int64_t)a.n_items * a.num_kv_heads;  // one workgroup per key block and K/V head
-  constexpr int BM = bwd_block_q(sizeof(T) == 2 ? 1 : 0, D);
-  hipLaunchKernelGGL((swa_bwd_kernel<T, D, BM, kDrop>), dim3((unsigned)nwg), dim3(256), 0,
+  hipLaunchKernelGGL((swa_bwd_kv_f32_kernel<D, BWD_BM, kDrop>), dim3((unsigned)nwg), dim3(256), 0,
                      static_cast<hipStream_t>(stream), a);
   return (int)hipGetLastError();
 }
@@ -458,22 +482,26 @@ static int launch_bwd_t(const BwdArgs& a, void* stream) {
 int launch_backward(const BwdArgs& a, int dtype, int head_dim, void* stream) {
   if (dtype == 1) return launch_bwd_kv(a, head_dim, stream);  // swa_bwd_kv.hip
   if (a.drop.words)
-    return head_dim == 128 ? launch_bwd_t<float, 128, true>(a, stream)
-                           : launch_bwd_t<float, 64, true>(a, stream);
-  return head_dim == 128 ? launch_bwd_t<float, 128, false>(a, stream)
-                         : launch_bwd_t<float, 64, false>(a, stream);
+    return head_dim == 128 ? launch_kv_f32_t<128, true>(a, stream)
+                           : launch_kv_f32_t<64, true>(a, stream);
+  return head_dim == 128 ? launch_kv_f32_t<128, false>(a, stream)
+                         : launch_kv_f32_t<64, false>(a, stream);
 }
 
-int launch_dq_finalize(const FinalizeArgs& a, int dtype, void* stream) {
-  const int64_t nwg = (a.n / 8 + 255) / 256;
-  if (nwg == 0) return 0;
-  if (dtype == 1)
-    hipLaunchKernelGGL((swa_dq_finalize_kernel<bf16>), dim3((unsigned)nwg), dim3(256), 0,
-                       static_cast<hipStream_t>(stream), a);
-  else
-    hipLaunchKernelGGL((swa_dq_finalize_kernel<float>), dim3((unsigned)nwg), dim3(256), 0,
-                       static_cast<hipStream_t>(stream), a);
+template <int D, bool kDrop>
+static int launch_dq_f32_t(const BwdArgs& a, void* stream) {
+  const int64_t nwg = (int64_t)a.n_items * a.num_heads;  // one workgroup per query block and head
+  hipLaunchKernelGGL((swa_bwd_dq_f32_kernel<D, kDrop>), dim3((unsigned)nwg), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), a);
   return (int)hipGetLastError();
+}
+
+int launch_bwd_dq_f32(const BwdArgs& a, int head_dim, void* stream) {
+  if (a.drop.words)
+    return head_dim == 128 ? launch_dq_f32_t<128, true>(a, stream)
+                           : launch_dq_f32_t<64, true>(a, stream);
+  return head_dim == 128 ? launch_dq_f32_t<128, false>(a, stream)
+                         : launch_dq_f32_t<64, false>(a, stream);
 }
 
 int launch_fill(const FillArgs& a, void* stream) {

@@ -183,14 +183,12 @@ size_t fwd_workspace(int64_t num_seqs, int64_t t_q, int64_t n) {
   return align256(sizeof(Item) * n_it + sizeof(int32_t) * (n_it * n + kMaxGrid + 1));
 }
 
-// Backward workspace: dK/dV items, then dQ items | D | lse2 | dq accumulator
-// (fp32 inputs only).
+// Backward workspace: schedule (dK/dV items, then dQ items, work lists) | D | lse2.
 struct BwdLayout {
-  size_t items, drow, lse2, dq_acc, total;
+  size_t items, drow, lse2, total;
 };
 
-BwdLayout bwd_layout(int64_t num_seqs, int64_t t_q, int64_t t_kv, int64_t n, int64_t d,
-                     int32_t dtype) {
+BwdLayout bwd_layout(int64_t num_seqs, int64_t t_q, int64_t t_kv, int64_t n) {
   BwdLayout l;
   l.items = 0;
   // schedule: the items of both kernels, their work lists (a code per
@@ -198,8 +196,7 @@ BwdLayout bwd_layout(int64_t num_seqs, int64_t t_q, int64_t t_kv, int64_t n, int
   const int64_t n_it = max_items_bwd(num_seqs, t_kv) + max_items_dq(num_seqs, t_q);
   l.drow = align256(sizeof(Item) * n_it + sizeof(int32_t) * (n_it * n + 2 * (kMaxGrid + 1)));
   l.lse2 = l.drow + align256(sizeof(float) * t_q * n);
-  l.dq_acc = l.lse2 + align256(sizeof(float) * t_q * n);
-  l.total = l.dq_acc + (dtype == SWA_DTYPE_FP32 ? align256(sizeof(float) * t_q * n * d) : 0);
+  l.total = l.lse2 + align256(sizeof(float) * t_q * n);
   return l;
 }
 
@@ -286,12 +283,12 @@ void schedule_forward(const Problem& p, const std::vector<Seq>& seqs, std::vecto
   }
 }
 
-// Backward schedule: one item per block of BWD_BN keys; query tiles of
-// bwd_block_q(dtype, head_dim) rows.
+// Backward dK/dV schedule: one item per block of BWD_BN keys; query tiles of
+// BWD_BM rows.
 void schedule_backward(const Problem& p, const std::vector<Seq>& seqs,
                        std::vector<Item>& items) {
   items.clear();
-  const int64_t BN = BWD_BN, BM = bwd_block_q(p.dtype, static_cast<int>(p.head_dim));
+  const int64_t BN = BWD_BN, BM = BWD_BM;
   for (const Seq& s : seqs) {
     if (s.skv == 0) continue;
     const Band bd = seq_band(p, s);
@@ -326,7 +323,7 @@ void schedule_backward(const Problem& p, const std::vector<Seq>& seqs,
   }
 }
 
-// dQ schedule (bf16 backward): one item per block of DQ_BM query rows, with
+// dQ schedule: one item per block of DQ_BM query rows, with
 // the key-tile range of forward_range (tiles of FWD_BN).
 void schedule_dq(const Problem& p, const std::vector<Seq>& seqs, std::vector<Item>& items) {
   items.clear();
@@ -546,17 +543,17 @@ void build_forward_schedule(const Problem& p, const std::vector<Seq>& seqs, int 
   L.bytes = blob.size();
 }
 
-// Backward: kernel 0 = dK/dV (fp32: the one-pass kernel), kernel 1 = dQ (bf16).
+// Backward: kernel 0 = dK/dV, kernel 1 = dQ; work lists for the persistent
+// bf16 kernels (the fp32 kernels run one workgroup per unit).
 void build_backward_schedule(const Problem& p, const std::vector<Seq>& seqs, int n_cu,
                              std::vector<uint8_t>& blob, SchedLayout& L) {
-  const bool two_pass = p.dtype == SWA_DTYPE_BF16;
   std::vector<Item> items, dq_items;
   schedule_backward(p, seqs, items);
   order_items(items);
+  schedule_dq(p, seqs, dq_items);
+  order_items(dq_items);
   WorkList wl_kv, wl_dq;
-  if (two_pass) {
-    schedule_dq(p, seqs, dq_items);
-    order_items(dq_items);
+  if (p.dtype == SWA_DTYPE_BF16) {
     build_worklist(items, p.num_kv_heads, n_cu, 1, wl_kv);
     build_worklist(dq_items, p.num_heads, n_cu, 1, wl_dq);
   }
@@ -700,8 +697,7 @@ Problem make_problem(const int64_t* cu_q, const int64_t* cu_kv, int64_t num_seqs
 size_t elem_bytes(int32_t dtype) { return dtype == SWA_DTYPE_FP32 ? 4 : 2; }
 
 // Optional per-kernel timing with HIP events (swa_profile_enable/read).
-enum KernelKind { K_FWD = 0, K_BWD_PRE = 1, K_BWD = 2, K_DQ_FIN = 3, K_FILL = 4, K_BWD_DQ = 5,
-                  K_KINDS = 6 };
+enum KernelKind { K_FWD = 0, K_BWD_PRE = 1, K_BWD = 2, K_FILL = 4, K_BWD_DQ = 5, K_KINDS = 6 };
 struct Profiler {
   std::mutex mu;
   bool on = false;
@@ -781,7 +777,7 @@ swa_status swa_backward_workspace_size(int64_t num_seqs, int64_t t_q, int64_t t_
   if (!bytes) return fail(SWA_ERR_NULLPTR, "bytes is NULL");
   swa_status s = check_sizes(num_seqs, t_q, t_kv, num_heads, head_dim, dtype);
   if (s != SWA_OK) return s;
-  *bytes = bwd_layout(num_seqs, t_q, t_kv, num_heads, head_dim, dtype).total;
+  *bytes = bwd_layout(num_seqs, t_q, t_kv, num_heads).total;
   return SWA_OK;
 }
 
@@ -886,8 +882,9 @@ swa_status run_backward(const Problem& p, const std::vector<Seq>& seqs, int64_t 
   void *dq = B.dq, *dk = B.dk, *dv = B.dv;
   const int64_t sparse_mode = p.sparse_mode;
   swa_status s = SWA_OK;
-  // bf16: dK/dV kernel + dQ kernel (no atomics); fp32: one pass with a dq accumulator
-  const bool two_pass = dtype == SWA_DTYPE_BF16;
+  // bf16: dQ kernel (it also forms D, lse2), then dK/dV kernel;
+  // fp32: preprocess (D, lse2), dK/dV kernel, dQ kernel.  No atomics.
+  const bool bf16 = dtype == SWA_DTYPE_BF16;
   const char* sched = nullptr;
   SchedLayout SL;
   if ((s = place_schedule(1, p, seqs, ws + L.items, noalloc_device, stream, &sched, &SL)) != SWA_OK)
@@ -896,12 +893,11 @@ swa_status run_backward(const Problem& p, const std::vector<Seq>& seqs, int64_t 
   int e = 0;
   float* drow = reinterpret_cast<float*>(ws + L.drow);
   float* lse2 = reinterpret_cast<float*>(ws + L.lse2);
-  float* dq_acc = two_pass ? nullptr : reinterpret_cast<float*>(ws + L.dq_acc);
-  if (!two_pass) {  // fp32: D, lse2 and the zeroed dq accumulator from the preprocess kernel
-    BwdPreArgs pa{dy, out, softmax_max, softmax_sum, drow, lse2, dq_acc, t_q * num_heads,
+  if (!bf16) {
+    BwdPreArgs pa{dy, out, softmax_max, softmax_sum, drow, lse2, t_q * num_heads,
                   static_cast<int32_t>(num_heads), static_cast<int32_t>(t_q)};
     if ((e = timed_launch(K_BWD_PRE, stream, [&] {
-           return launch_bwd_pre(pa, dtype, static_cast<int>(head_dim), stream);
+           return launch_bwd_pre(pa, static_cast<int>(head_dim), stream);
          })) != 0)
       return fail(SWA_ERR_HIP, hip_error_string(e));
   }
@@ -915,7 +911,6 @@ swa_status run_backward(const Problem& p, const std::vector<Seq>& seqs, int64_t 
   a.out = out;
   a.smax = softmax_max;
   a.ssum = softmax_sum;
-  a.dq_acc = dq_acc;
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
@@ -931,16 +926,16 @@ swa_status run_backward(const Problem& p, const std::vector<Seq>& seqs, int64_t 
   a.scale = static_cast<float>(scale);
   a.scale_log2 = static_cast<float>(scale * 1.4426950408889634);
   a.mode = static_cast<int32_t>(sparse_mode);
-  // bf16: the dQ kernel first (it also writes D and lse2 of every row of every
-  // sequence: one item per block of query rows, even when the block attends
-  // no key), then the dK/dV kernel, which reads them
-  if (two_pass && SL.n_items[1] > 0) {
-    BwdArgs b = a;
-    b.items = reinterpret_cast<const Item*>(sched + SL.at_items[1]);
-    b.n_items = SL.n_items[1];
-    b.work = reinterpret_cast<const int32_t*>(sched + SL.at_code[1]);
-    b.work_off = reinterpret_cast<const int32_t*>(sched + SL.at_off[1]);
-    b.n_wg = SL.grid[1];
+  // The dQ schedule has one item per block of query rows of every sequence,
+  // even when the block attends no key (its dq rows are written as zero; the
+  // bf16 dQ kernel also writes their D and lse2, read by its dK/dV kernel).
+  BwdArgs b = a;
+  b.items = reinterpret_cast<const Item*>(sched + SL.at_items[1]);
+  b.n_items = SL.n_items[1];
+  b.work = reinterpret_cast<const int32_t*>(sched + SL.at_code[1]);
+  b.work_off = reinterpret_cast<const int32_t*>(sched + SL.at_off[1]);
+  b.n_wg = SL.grid[1];
+  if (bf16 && SL.n_items[1] > 0) {
     if ((e = timed_launch(K_BWD_DQ, stream, [&] {
            return launch_bwd_dq(b, static_cast<int>(head_dim), stream);
          })) != 0)
@@ -952,16 +947,16 @@ swa_status run_backward(const Problem& p, const std::vector<Seq>& seqs, int64_t 
          })) != 0)
       return fail(SWA_ERR_HIP, hip_error_string(e));
   }
-  if (two_pass) {
-    if (end_q < t_q) {  // tokens after the last sequence
-      FillArgs f{dq, static_cast<int64_t>(elem_bytes(dtype)), num_heads * head_dim, end_q, t_q,
-                 nullptr, nullptr, 0};
-      if ((e = timed_launch(K_FILL, stream, [&] { return launch_fill(f, stream); })) != 0)
-        return fail(SWA_ERR_HIP, hip_error_string(e));
-    }
-  } else {
-    FinalizeArgs fa{dq_acc, dq, static_cast<float>(scale), t_q * num_heads * head_dim};
-    if ((e = timed_launch(K_DQ_FIN, stream, [&] { return launch_dq_finalize(fa, dtype, stream); })) != 0)
+  if (!bf16 && SL.n_items[1] > 0) {
+    if ((e = timed_launch(K_BWD_DQ, stream, [&] {
+           return launch_bwd_dq_f32(b, static_cast<int>(head_dim), stream);
+         })) != 0)
+      return fail(SWA_ERR_HIP, hip_error_string(e));
+  }
+  if (end_q < t_q) {  // tokens after the last sequence
+    FillArgs f{dq, static_cast<int64_t>(elem_bytes(dtype)), num_heads * head_dim, end_q, t_q,
+               nullptr, nullptr, 0};
+    if ((e = timed_launch(K_FILL, stream, [&] { return launch_fill(f, stream); })) != 0)
       return fail(SWA_ERR_HIP, hip_error_string(e));
   }
   if (end_kv < t_kv) {
@@ -1022,7 +1017,7 @@ swa_status swa_backward_ex(const void* q, const void* k, const void* v, const vo
                                   drop_mask, drop_mask_bytes, keep_prob, dq, dk, dv, &p, &seqs,
                                   &end_q, &end_kv, &B);
   if (s != SWA_OK) return s;
-  const BwdLayout L = bwd_layout(num_seqs, t_q, t_kv, num_heads, head_dim, dtype);
+  const BwdLayout L = bwd_layout(num_seqs, t_q, t_kv, num_heads);
   if (workspace_bytes < L.total)
     return fail(SWA_ERR_WORKSPACE, "workspace has " + std::to_string(workspace_bytes) +
                                        " bytes, needs " + std::to_string(L.total));
@@ -1048,7 +1043,7 @@ swa_status swa_backward_noalloc(const void* q, const void* k, const void* v, con
                                   drop_mask, drop_mask_bytes, keep_prob, dq, dk, dv, &p, &seqs,
                                   &end_q, &end_kv, &B);
   if (s != SWA_OK) return s;
-  const BwdLayout L = bwd_layout(num_seqs, t_q, t_kv, num_heads, head_dim, dtype);
+  const BwdLayout L = bwd_layout(num_seqs, t_q, t_kv, num_heads);
   if (L.total > kNoAllocScratchBytes)
     return fail(SWA_ERR_WORKSPACE,
                 "this problem needs " + std::to_string(L.total) + " bytes of scratch; "
@@ -1100,7 +1095,7 @@ swa_status swa_debug_tile_schedule(const int64_t* cu_seqlens_q, const int64_t* c
   } else if (direction == 1) {
     schedule_backward(p, seqs, items);
     *block_item = BWD_BN;
-    *block_tile = bwd_block_q(dtype, static_cast<int>(head_dim));
+    *block_tile = BWD_BM;
   } else {
     schedule_dq(p, seqs, items);
     *block_item = DQ_BM;

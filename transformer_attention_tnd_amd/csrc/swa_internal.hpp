@@ -11,17 +11,16 @@ namespace swa {
 
 // Block sizes.  Forward: a work item is one block of FWD_BM = 2 x FWD_HALF
 // query rows of one sequence (one workgroup per item and head, two wave
-// groups of FWD_HALF rows); it walks key tiles of FWD_BN.  Backward dK/dV
-// (and the fp32 one-pass backward): an item is one block of BWD_BN keys; it
-// walks query tiles of bwd_block_q rows.  Backward dQ (bf16): an item is one
-// block of DQ_BM query rows; it walks key tiles of FWD_BN.
+// groups of FWD_HALF rows); it walks key tiles of FWD_BN.  Backward dK/dV: an
+// item is one block of BWD_BN keys; it walks query tiles of BWD_BM rows.
+// Backward dQ: an item is one block of DQ_BM query rows; it walks key tiles
+// of FWD_BN.
 constexpr int FWD_HALF = 128;
 constexpr int FWD_BM = 2 * FWD_HALF;
 constexpr int FWD_BN = 64;
 constexpr int BWD_BN = 128;
+constexpr int BWD_BM = 64;
 constexpr int DQ_BM = FWD_HALF;
-// query rows per backward tile: 64, or 32 for fp32 with head_dim 128 (LDS)
-constexpr int bwd_block_q(int dtype, int head_dim) { return (dtype == 0 && head_dim == 128) ? 32 : 64; }
 
 // One schedule entry (64 bytes, uploaded to the workspace).
 //   tiles[i] = lo | hi << 16 : visited tile range [lo, hi] (empty if lo > hi)
@@ -109,7 +108,6 @@ struct BwdPreArgs {
   const float* ssum;
   float* drow;   // [N, t_q] rowsum(dY * out)
   float* lse2;   // [N, t_q] softmax_max*log2(e) + log2(softmax_sum), +inf if empty
-  float* dq_acc; // [t_q, N, D] zeroed here (null: nothing to zero)
   int64_t rows;  // t_q * N
   int32_t num_heads;
   int32_t t_q;
@@ -120,16 +118,15 @@ struct BwdArgs {
   const void* k;
   const void* v;
   const void* dy;
-  float* drow;        // [N, t_q]: D = rowsum(dY o O) (fp32 one-pass); -D (bf16
-                      // two-pass: written by the dQ kernel, read by the dK/dV kernel)
+  float* drow;        // [N, t_q]: D = rowsum(dY o O) (fp32: from the preprocess
+                      // kernel); -D (bf16: written by the dQ kernel, read by the dK/dV kernel)
   float* lse2;        // [N, t_q]: softmax_max log2(e) + log2(softmax_sum)
   // bf16 two-pass: the dQ kernel (launched first) computes D and lse2 of its
   // rows from out and the statistics and stores them for the dK/dV kernel
   const void* out;    // [t_q, N, D]
   const float* smax;  // [t_q, N, 8]
   const float* ssum;  // [t_q, N, 8]
-  float* dq_acc;      // fp32 one-pass backward only
-  void* dq;           // bf16 dQ kernel only
+  void* dq;           // dQ kernels only
   void* dk;
   void* dv;
   const Item* items;
@@ -148,13 +145,6 @@ struct BwdArgs {
   DropArgs drop;
 };
 
-struct FinalizeArgs {
-  const float* dq_acc;
-  void* dq;
-  float scale;
-  int64_t n;  // elements
-};
-
 // Zero-fill of rows [row0, row1) of a [rows, N, D] tensor and, if smax is
 // given, softmax_max = -inf / softmax_sum = 0 for those rows.
 struct FillArgs {
@@ -169,8 +159,9 @@ struct FillArgs {
 
 // Launchers (defined in the .hip files).  They return a hipError_t as int.
 int launch_forward(const FwdArgs& a, int dtype, int head_dim, void* stream);
-int launch_bwd_pre(const BwdPreArgs& a, int dtype, int head_dim, void* stream);
-// fp32: the one-pass kernel (dK, dV and the dq accumulator); bf16: the dK/dV kernel
+// fp32 only: D and lse2 of every row
+int launch_bwd_pre(const BwdPreArgs& a, int head_dim, void* stream);
+// the dK/dV kernel of either type over the dK/dV schedule (writes dk, dv)
 int launch_backward(const BwdArgs& a, int dtype, int head_dim, void* stream);
 // bf16 only: the dK/dV kernel over the dK/dV schedule (writes dk, dv);
 // grouped key/value heads go to launch_bwd_kv_grouped
@@ -178,7 +169,9 @@ int launch_bwd_kv(const BwdArgs& a, int head_dim, void* stream);
 int launch_bwd_kv_grouped(const BwdArgs& a, int head_dim, void* stream);
 // bf16 only: the dQ kernel over the dQ schedule (writes dq)
 int launch_bwd_dq(const BwdArgs& a, int head_dim, void* stream);
-int launch_dq_finalize(const FinalizeArgs& a, int dtype, void* stream);
+// fp32 only: the dQ kernel over the dQ schedule (writes dq; reads the D and
+// lse2 of launch_bwd_pre)
+int launch_bwd_dq_f32(const BwdArgs& a, int head_dim, void* stream);
 int launch_fill(const FillArgs& a, void* stream);
 // Size of the fixed device scratch used by swa_backward_noalloc, and the
 // device address of the copy of it on the device of `stream` (null: the
