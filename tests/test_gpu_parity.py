@@ -442,6 +442,8 @@ LARGE = {
         ([(0, 0, 16000, 64), (0, 9, 15000, 32), (0, 15, 10**9, 32)], 4),
     "gqa_swa_bf16_b1_n16kv4_s16384_d128_pre2048_next0":
         ([(0, 0, 0, 64), (0, 6, 5000, 64), (0, 15, 10**9, 64)], 2),
+    "swa_fp32_b1_n16_s16384_d128_pre2048_next0":
+        ([(0, 0, 0, 64), (0, 9, 7000, 64), (0, 15, 10**9, 64)], 2),
 }
 LARGE_CASES = [(n, part) for n, (_, parts) in LARGE.items() for part in range(parts + 1)]
 _large = {}

@@ -53,8 +53,8 @@ class Workload:
 
 
 # Five workloads shaped like the pages' cases (the fourth is the headline
-# sliding-window case: S = 16K, window of 2048 past tokens), then two that
-# measure the other masks and grouped heads at the headline's shape.
+# sliding-window case: S = 16K, window of 2048 past tokens), then three that
+# measure the other masks, grouped heads and fp32 inputs at the headline's shape.
 WORKLOADS = {
     w.name: w
     for w in [
@@ -79,6 +79,9 @@ WORKLOADS = {
         Workload("gqa_swa_bf16_b1_n16kv4_s16384_d128_pre2048_next0", torch.bfloat16, 16, 128, 4,
                  1.0 / math.sqrt(128), pre_tokens=2048, next_tokens=0, std=0.5, batch=1,
                  seqlen=16384, num_kv_heads=4),
+        # the 16K window workload with fp32 inputs (the fp32 kernels at full size)
+        Workload("swa_fp32_b1_n16_s16384_d128_pre2048_next0", torch.float32, 16, 128, 4,
+                 1.0 / math.sqrt(128), pre_tokens=2048, next_tokens=0, batch=1, seqlen=16384),
     ]
 }
 
