@@ -287,7 +287,13 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
 
   // S^T block jb: rows = keys 32*jb + c_row(r, h), column = this lane's query
   // (the two key blocks alternate so that consecutive MFMAs are independent)
+  // (fp32 only; the lane indices are formed inside, behind an empty asm, so
+  // that the compiler does not compute the many swizzled LDS offsets once
+  // and hold them in registers across the tile loop)
   auto scores = [&](const char* kt) __attribute__((always_inline)) {
+    int ln = threadIdx.x;
+    asm volatile("" : "+v"(ln));
+    const int c = ln & 31, h = (ln >> 5) & 1;
 #pragma unroll
     for (int jb = 0; jb < NJB; ++jb) s[jb] = floatx16{};
 #pragma unroll
@@ -300,21 +306,21 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
       }
     }
   };
-  // O^T[db] += V^T P^T with the probabilities of the previous tile
+  // O^T[db] += V^T P^T with the probabilities of the previous tile (fp32
+  // only; lane indices formed inside, as in scores)
   auto pv = [&](const char* vt) __attribute__((always_inline)) {
+    int ln = threadIdx.x;
+    asm volatile("" : "+v"(ln));
+    const int c = ln & 31, h = (ln >> 5) & 1;
 #pragma unroll
     for (int jb = 0; jb < NJB; ++jb) {
 #pragma unroll
       for (int t2 = 0; t2 < PSTEPS; ++t2) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          op_t va;
-          if constexpr (sizeof(T) == 2) {
-            va = tr_operand<RB, true>(vt, 32 * jb + KSTEP * t2, db, lane);
-          } else {
-            const int row = 32 * jb + row_of_slot<T>(KSTEP * t2 + KPL * h);
-            va = *reinterpret_cast<const T*>(vt + tile_off<RB>(row, (32 * db + c) * (int)sizeof(T)));
-          }
+          const int row = 32 * jb + row_of_slot<T>(KSTEP * t2 + KPL * h);
+          const op_t va =
+              *reinterpret_cast<const T*>(vt + tile_off<RB>(row, (32 * db + c) * (int)sizeof(T)));
           o[db] = M::mma(va, pk[jb][t2], o[db]);
         }
       }
