@@ -173,24 +173,25 @@ def test_backward_mask_pattern_16k_window_is_exact(dev):
     assert_equal_counts("dk", dk, SCALE * colc)
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("dt", sorted(DTYPES))
-def test_forward_mask_pattern_with_dropout(dev, dt):
+def test_forward_mask_pattern_with_dropout(dev, dt, D):
     """Forward with dropout, q = 0: softmax_sum is the undropped count of
     allowed keys exactly, softmax_max is 0, and with V_j = e_(j mod D) out is
     zero exactly where no kept allowed key falls in class c."""
-    p = workloads.make_custom([300, 77, 513], num_heads=2, head_dim=64, dtype=DTYPES[dt],
+    p = workloads.make_custom([300, 77, 513], num_heads=2, head_dim=D, dtype=DTYPES[dt],
                               sparse_mode=4, pre_tokens=70, next_tokens=9)
     mask = workloads.make_drop_mask(p, 0.5)
     keep = oracle.unpack_drop_mask(mask, p.cu_seqlens_q, p.cu_seqlens_kv, 2)
     p.q.zero_()
-    p.v.copy_(one_hot_rows(p.v.shape[0], 2, 64, p.cu_seqlens_kv, p.dtype))
+    p.v.copy_(one_hot_rows(p.v.shape[0], 2, D, p.cu_seqlens_kv, p.dtype))
     out, smax, ssum = swa.forward(*(x.to(dev) for x in (p.q, p.k, p.v)), p.cu_seqlens_q,
                                   p.cu_seqlens_kv, p.scale, p.pre_tokens, p.next_tokens,
                                   p.sparse_mode, drop_mask=mask.to(dev), keep_prob=0.5)
     torch.cuda.synchronize()
     out, smax, ssum = out.cpu().float(), smax.cpu(), ssum.cpu()
-    rowc, _ = expected_counts(p, 2, 2, 64, keep, 0.5)
-    count, _ = expected_counts(p, 2, 2, 64)
+    rowc, _ = expected_counts(p, 2, 2, D, keep, 0.5)
+    count, _ = expected_counts(p, 2, 2, D)
     n_allowed = count.sum(2)
     assert torch.equal(ssum[..., 0], n_allowed)
     assert not smax.any()

@@ -145,18 +145,21 @@ def test_dropout_cases_full_parity(dev, case):
     compare_full(p, g, o)
 
 
-def test_dropout_keep_all_equals_no_dropout(dev):
-    """An all-ones mask with keep_prob 1 reproduces the call without dropout up
-    to rounding: the bf16 forward without dropout walks 128-key tiles where the
-    dropout one walks the scheduler's 64-key tiles (another summation order),
-    and without dropout the backward's dP chains start from -D (dS = P (dP - D)
-    in one multiply) where with dropout D is subtracted after the chain."""
-    p = workloads.make_custom([300, 77], num_heads=2, head_dim=128, sparse_mode=4,
-                              pre_tokens=100, next_tokens=0)
+@pytest.mark.parametrize("D", [64, 128])
+def test_dropout_keep_all_equals_no_dropout(dev, D):
+    """An all-ones mask with keep_prob 1 reproduces the call without dropout:
+    the forward bit for bit (the same tiles and order; each probability is
+    multiplied by 1 and masked by all ones), the backward up to rounding
+    (without dropout its dP chains start from -D, dS = P (dP - D) in one
+    multiply, where with dropout D is subtracted after the chain)."""
+    p = workloads.make_custom([300, 77, 700], num_heads=2, head_dim=D, sparse_mode=4,
+                              pre_tokens=300, next_tokens=0)
     mask = workloads.make_drop_mask(p, 1.0)
     a = run_hip(p, dev)
     b = run_hip(p, dev, drop_mask=mask, keep_prob=1.0)
-    for n in ("out", "dq", "dk", "dv"):
+    for n in ("out", "smax", "ssum"):
+        assert torch.equal(a[n], b[n]), n
+    for n in ("dq", "dk", "dv"):
         assert (a[n].float() - b[n].float()).abs().max() <= 1e-2, n
     assert (a["smax"] - b["smax"]).abs().max() <= 1e-5
     assert ((a["ssum"] - b["ssum"]).abs() / b["ssum"].abs().clamp_min(1e-30)).max() <= 1e-4

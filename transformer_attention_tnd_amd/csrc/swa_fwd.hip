@@ -85,10 +85,10 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
   using M = Mfma<T>;
   using op_t = typename M::op_t;
   constexpr int KPL = M::KPL, KSTEP = M::KSTEP;
-  // bf16 without dropout walks 128-key tiles (two of the scheduler's 64-key
-  // tiles per step: half the barriers, rescale checks and lane swaps per
-  // key); the other instantiations walk the scheduler's tiles
-  constexpr bool kWide = sizeof(T) == 2 && !kDrop;
+  // bf16 walks 128-key tiles (two of the scheduler's 64-key tiles per step:
+  // half the barriers, rescale checks and lane swaps per key); fp32 walks
+  // the scheduler's tiles
+  constexpr bool kWide = sizeof(T) == 2;
   constexpr int HALF = FWD_HALF, BN = kWide ? 2 * FWD_BN : FWD_BN, NT = 512;
   constexpr int SUB = BN / FWD_BN;  // scheduler tiles per kernel tile
   constexpr int RB = D * (int)sizeof(T);  // tile row bytes
@@ -104,7 +104,7 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
   // kernels without dropout, whose copies are issued from the matrix phases
   // (the copy of a tile then has two steps to land), else three when they
   // fit (one step), else two
-  constexpr bool kSpreadable = sizeof(T) == 2 && !kDrop;
+  constexpr bool kSpreadable = sizeof(T) == 2;
   constexpr int NBUF = kSpreadable && 8 * TB <= 160 * 1024   ? 4
                       : kSpreadable && 6 * TB <= 160 * 1024 ? 3
                       : 6 * TB <= 160 * 1024 && !kWide      ? 3
@@ -112,6 +112,14 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds[2 * NBUF * TB];  // K[NBUF] V[NBUF]
   char* const kbuf0 = lds;
   char* const vbuf0 = lds + NBUF * TB;
+  // bf16 dropout: the keep words of a tile for every row of the block (KW
+  // words a row: the 128 keys of the tile span 5 words at any bit offset),
+  // two tiles in turn
+  constexpr bool kDropLds = kDrop && sizeof(T) == 2;
+  constexpr int KW = 6;
+  constexpr int KEEP_TILE = 2 * HALF * KW;  // words of one tile
+  static_assert(!kDropLds || (BN == 128 && 32 * KW == 3 * 64), "three 64-lane copies per wave");
+  __shared__ __attribute__((aligned(16))) uint32_t keep_lds[kDropLds ? 2 * KEEP_TILE : 1];
 
   const int64_t ld = (int64_t)a.num_heads * D;       // q / out row stride
   const int64_t ldkv = (int64_t)a.num_kv_heads * D;  // k / v row stride
@@ -123,7 +131,7 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
   // the bf16 kernels without dropout load a unit's Q rows and first tiles
   // before the previous unit's epilogue, which then stages its rows in the
   // last two V buffers (the first tiles take the others)
-  constexpr bool kOverlap = sizeof(T) == 2 && !kDrop;
+  constexpr bool kOverlap = sizeof(T) == 2;
   // a kernel tile is visited if one of its scheduler tiles is, and mask-free
   // only if all of them are (keys of a visited kernel tile that the schedule
   // skips are outside the band: the mask removes them)
@@ -246,18 +254,53 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
     if (q >= it.sq) j_max = -1;
   };
 
-  // Dropout keep bits of this lane's row for the 64 keys of a tile: three
-  // 32-bit words, funnel-shifted into the window in the tile's softmax (bit
-  // k = key 64 t + k).  The words of tile t + 1 are loaded (into mwn) in the
-  // matrix phase of tile t and move into mw at the start of the next matrix
-  // phase, so a load has a full step to land.
+  // Dropout keep bits of this lane's row for the keys of a tile (bit k = key
+  // BN t + k), funnel-shifted into the window in the tile's softmax.
+  // fp32 (64-key tiles): three 32-bit words per lane; the words of tile t + 1
+  // are loaded (into mwn) in the matrix phase of tile t and move into mw at
+  // the start of the next matrix phase, so a load has a full step to land.
   uint32_t mw[3] = {0u, 0u, 0u}, mwn[3] = {0u, 0u, 0u};
   uint32_t msh = 0, mshn = 0;
-  const int64_t drop_row = kDrop ? it.drop_base + (int64_t)head * it.sq * it.skv +
-                                       (int64_t)(qrow < it.sq ? qrow : 0) * it.skv
-                                 : 0;
+  const int64_t drop_row = (kDrop && !kDropLds) ? it.drop_base + (int64_t)head * it.sq * it.skv +
+                                                      (int64_t)(qrow < it.sq ? qrow : 0) * it.skv
+                                                : 0;
+  // bf16 (128-key tiles): the matrix phase of tile t copies the words of
+  // tile t + 1 for the wave's 32 rows into keep_lds[(t + 1) % 2] (a row's
+  // words are those of its clamped row: rows past the sequence attend
+  // nothing), by three 4-byte global -> LDS copies per lane.  Bits are
+  // addressed relative to X, the first bit of the wave's first (clamped) row:
+  // row X + d skv starts in word (X % 32 + d skv) / 32 after word X / 32.
+  // the wave's index and first row (wave-uniform: scalar registers)
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int row0w = it.block * 2 * HALF + 32 * wu;
+  auto keep_x = [&]() -> int64_t {
+    return it.drop_base + (int64_t)head * it.sq * it.skv +
+           (int64_t)(row0w < it.sq ? row0w : it.sq - 1) * it.skv;
+  };
+  auto load_keep = [&](int tile) {
+    if constexpr (kDropLds) {
+      int ln = threadIdx.x;
+      asm volatile("" : "+v"(ln));
+      ln &= 63;
+      const int64_t X = keep_x();
+      const int64_t wb = X >> 5;
+      const int64_t left = (a.drop.n_words - wb) * 4;
+      const u32x4 rs = buffer_rsrc(a.drop.words + wb, (uint32_t)(left < 0 ? 0 : (left > 0x7ffffffc ? 0x7ffffffc : left)));
+      const uint32_t x5 = (uint32_t)(X & 31);
+      const int rc0 = row0w < it.sq ? row0w : it.sq - 1;
+      const uint32_t dst = lds_addr(keep_lds + (tile & 1) * KEEP_TILE + wu * 32 * KW);
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        const int slot = 64 * i + ln, r = slot / KW, e = slot - KW * (slot / KW);
+        const int rr = row0w + r;
+        const uint32_t d = (uint32_t)((rr < it.sq ? rr : it.sq - 1) - rc0);
+        const uint32_t word = ((x5 + d * (uint32_t)it.skv) >> 5) + 4u * (uint32_t)tile + (uint32_t)e;
+        dma4(rs, 4u * word, __builtin_amdgcn_readfirstlane(dst + 256 * i));
+      }
+    }
+  };
   auto load_mask = [&](int tile) {
-    if constexpr (kDrop) {
+    if constexpr (kDrop && !kDropLds) {
       const int64_t bit = drop_row + (int64_t)tile * BN;
       const int64_t w = bit >> 5;
       mshn = (uint32_t)(bit & 31);
@@ -367,7 +410,20 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
     const float moff = m_ref == -INFINITY ? 0.f : -m_ref * cs;
     // keep bits of this lane's keys: block jb, register r -> key 32 jb + c_row(r, h)
     uint32_t keep[NJB] = {};
-    if constexpr (kDrop) {
+    if constexpr (kDropLds) {
+      // this lane's row: words from keep_lds, shift (X + d skv) % 32
+      const uint32_t* kr = keep_lds + (tile & 1) * KEEP_TILE + (wu * 32 + c) * KW;
+      const uint2 w01 = *reinterpret_cast<const uint2*>(kr);
+      const uint2 w23 = *reinterpret_cast<const uint2*>(kr + 2);
+      const uint32_t w4 = kr[4];
+      const int rc0 = row0w < it.sq ? row0w : it.sq - 1;
+      const uint32_t d = (uint32_t)((qrow < it.sq ? qrow : it.sq - 1) - rc0);
+      const uint32_t sh = ((uint32_t)(keep_x() & 31) + d * (uint32_t)it.skv) & 31u;
+      keep[0] = __builtin_amdgcn_alignbit(w01.y, w01.x, sh) >> (4 * h);
+      keep[1] = __builtin_amdgcn_alignbit(w23.x, w01.y, sh) >> (4 * h);
+      keep[2] = __builtin_amdgcn_alignbit(w23.y, w23.x, sh) >> (4 * h);
+      keep[3] = __builtin_amdgcn_alignbit(w4, w23.y, sh) >> (4 * h);
+    } else if constexpr (kDrop) {
       keep[0] = __builtin_amdgcn_alignbit(mw[1], mw[0], msh) >> (4 * h);
       keep[1] = __builtin_amdgcn_alignbit(mw[2], mw[1], msh) >> (4 * h);
     }
@@ -379,7 +435,11 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
         const float p = __builtin_amdgcn_exp2f(fmaf(s[jb][r], cs, moff));
         ls[r & 3] += p;  // the row sum is that of the undropped softmax
         if constexpr (kDrop)
-          s[jb][r] = ((keep[jb] >> (8 * (r >> 2) + (r & 3))) & 1u) ? p * a.drop.rkp : 0.f;
+          // (the signed one-bit field extract is 0 or all ones: a mask of p;
+          // the factor 1 / keep_prob of the kept terms is applied to the row
+          // at the end)
+          s[jb][r] = __uint_as_float(__float_as_uint(p) &
+                                     (uint32_t)__builtin_amdgcn_sbfe((int)keep[jb], 8 * (r >> 2) + (r & 3), 1));
         else
           s[jb][r] = p;
       }
@@ -470,7 +530,9 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
   auto m_phase = [&](int t, int k) __attribute__((always_inline)) {
     const bool do_pv = t - 1 >= mlo && t - 1 <= mhi;
     const bool do_s = t >= mlo && t <= mhi;
-    if constexpr (kDrop) {  // this tile's words in, the next tile's requested
+    if constexpr (kDropLds) {  // the next tile's words, ahead of this step's tile copies
+      if (t + 1 > mlo && t + 1 <= mhi) load_keep(t + 1);
+    } else if constexpr (kDrop) {  // this tile's words in, the next tile's requested
 #pragma unroll
       for (int e = 0; e < 3; ++e) mw[e] = mwn[e];
       msh = mshn;
@@ -520,7 +582,10 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
   static_assert(!kSpread || (NBUF - 2) * Dma::PARTS <= 15, "copies in flight fit the wait immediate");
   if (lo <= hi) {
     // (the Q rows and the first tiles were loaded by unit_prologue)
-    if constexpr (kDrop) {
+    if constexpr (kDropLds) {
+      if (mlo <= mhi) load_keep(mlo);
+      wait_vmem();
+    } else if constexpr (kDrop) {
       load_mask(lo);
       wait_vmem();
     }
@@ -555,15 +620,16 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
         m_phase(t, k);
       // the tiles of the next step have landed (with three buffers, the
       // copies issued in this step may still be in flight)
-      if constexpr (kSpread)  // the copies of the last NBUF - 2 steps (one tile per wave each) stay in flight
-        __builtin_amdgcn_s_waitcnt(0x0F70 | ((NBUF - 2) * Dma::PARTS));
+      if constexpr (kSpread)  // the copies of the last NBUF - 2 steps (one tile per wave each) stay
+        // in flight (with dropout only this step's, issued after the keep words)
+        __builtin_amdgcn_s_waitcnt(0x0F70 | ((kDropLds && NBUF > 3 ? 1 : NBUF - 2) * Dma::PARTS));
       else if (NBUF == 2 || (!ck && !cv) || kDrop)  // dropout: the next tile's keep words too
         wait_vmem();
       else if (ck && cv)
         __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * NC));
       else
         __builtin_amdgcn_s_waitcnt(0x0F70 | NC);
-      if constexpr (kDrop) asm volatile("" : : "v"(mwn[0]), "v"(mwn[1]), "v"(mwn[2]), "v"(mshn));
+      if constexpr (kDrop && !kDropLds) asm volatile("" : : "v"(mwn[0]), "v"(mwn[1]), "v"(mwn[2]), "v"(mshn));
       __syncthreads();
     }
     if constexpr (kSpread) {  // the last step's copies (into free buffers), of every wave
@@ -586,7 +652,8 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
 
   // epilogue: normalise, store out and the statistics of this lane's row
   const float l_ref = pair_sum(l_run);
-  const float inv = l_ref > 0.f ? 1.f / l_ref : 0.f;
+  // (dropout: times 1 / keep_prob, the factor of every kept term)
+  const float inv = l_ref > 0.f ? (kDrop ? a.drop.rkp : 1.f) / l_ref : 0.f;
   const int64_t tok = (int64_t)it.q_base + qrow;
   if constexpr (sizeof(T) == 2) {
     // the wave's 32 rows as whole rows, through its own 32-row slice of the
