@@ -457,19 +457,29 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
   // scheduling fences keep the order.
   constexpr int PVN = NJB * PSTEPS * NDB, SN = QSTEPS * NJB;
   constexpr int AHEAD = SWA_FWD_AHEAD, RING = AHEAD + 1;
-  int ok_[QSTEPS];   // 128-bit read of key row c, chunk 2t + h
-  int otr[NDB][2];   // transposing reads of the V tile, head-dim block db
-  if constexpr (sizeof(T) == 2) {
+  // LDS offsets of the operand reads: ok_[t], the 128-bit read of key row c,
+  // chunk 2t + h; otr[db], the transposing reads of the V tile, head-dim
+  // block db.  Formed once per unit, except with dropout, whose extra state
+  // leaves no room to hold them across the tile loop: there each matrix
+  // phase forms them again from a lane index behind an empty asm.
+  int ok_[QSTEPS];
+  int otr[NDB][2];
+  auto operand_offsets = [&](int ln) __attribute__((always_inline)) {
+    if constexpr (sizeof(T) == 2) {
+      ln &= 63;
+      const int cc = ln & 31, hh = ln >> 5;
 #pragma unroll
-    for (int t = 0; t < QSTEPS; ++t) ok_[t] = tile_off<RB>(c, (KSTEP * t + KPL * h) * 2);
+      for (int t = 0; t < QSTEPS; ++t) ok_[t] = tile_off<RB>(cc, (KSTEP * t + KPL * hh) * 2);
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const int s16 = lane & 15;
-      const int col2 = 2 * (32 * db + 16 * ((lane >> 4) & 1) + 4 * (s16 & 3));
-      otr[db][0] = tile_off<RB>(4 * h + (s16 >> 2), col2);
-      otr[db][1] = tile_off<RB>(4 * h + (s16 >> 2) + 8, col2);
+      for (int db = 0; db < NDB; ++db) {
+        const int s16 = ln & 15;
+        const int col2 = 2 * (32 * db + 16 * ((ln >> 4) & 1) + 4 * (s16 & 3));
+        otr[db][0] = tile_off<RB>(4 * hh + (s16 >> 2), col2);
+        otr[db][1] = tile_off<RB>(4 * hh + (s16 >> 2) + 8, col2);
+      }
     }
-  }
+  };
+  if constexpr (!kDropLds) operand_offsets(lane);
   // bf16 without dropout: each group copies one tile per step, part by part
   // from the slots of its matrix phase (a burst of copy instructions holds
   // the issuing waves while the address unit drains it): group 0 the K tile
@@ -488,6 +498,11 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
     static_assert(!kSpread || COPY_EVERY * (Dma::PARTS - 1) + 1 < LAST - FIRST + AHEAD,
                   "every copy has a slot");
     op_t ring[RING];
+    if constexpr (kDropLds) {
+      int ln = threadIdx.x;
+      asm volatile("" : "+v"(ln));
+      operand_offsets(ln);
+    }
     auto read = [&](auto ic) {
       constexpr int i = decltype(ic)::value;
       if constexpr (sizeof(T) != 2) {
