@@ -434,14 +434,17 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
       for (int r = 0; r < 16; ++r) {
         const float p = __builtin_amdgcn_exp2f(fmaf(s[jb][r], cs, moff));
         ls[r & 3] += p;  // the row sum is that of the undropped softmax
-        if constexpr (kDrop)
-          // (the signed one-bit field extract is 0 or all ones: a mask of p;
-          // the factor 1 / keep_prob of the kept terms is applied to the row
-          // at the end)
-          s[jb][r] = __uint_as_float(__float_as_uint(p) &
-                                     (uint32_t)__builtin_amdgcn_sbfe((int)keep[jb], 8 * (r >> 2) + (r & 3), 1));
-        else
+        if constexpr (kDrop) {
+          // the signed one-bit field extract is 0 or all ones: a mask of p
+          // (written as asm: the builtin is turned into an and, a compare and
+          // a select, one instruction more); the factor 1 / keep_prob of the
+          // kept terms is applied to the row at the end
+          uint32_t m;
+          asm("v_bfe_i32 %0, %1, %2, 1" : "=v"(m) : "v"(keep[jb]), "n"(8 * (r >> 2) + (r & 3)));
+          s[jb][r] = __uint_as_float(__float_as_uint(p) & m);
+        } else {
           s[jb][r] = p;
+        }
       }
 #pragma unroll
       for (int t2 = 0; t2 < PSTEPS; ++t2) pk[jb][t2] = M::pack(s[jb], t2);
