@@ -91,11 +91,15 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_dq_kernel(BwdArgs a) {
   int qrow = 0, q_sq = 0;              // this lane's query row (sequence-local), Sq
   // B operands of S^T and dP^T: lane (column qrow) holds Q[qrow][16t + 8h + e], dY likewise
   op_t qf[DSTEPS], yf[DSTEPS];
-  float lse = INFINITY, drow = 0.f;  // this row's lse2 and D (rows past the end: P = 0)
+  // this row's lse2 and D (rows past the end: P = 0); with dropout lse2 +
+  // log2(kp) and D kp
+  float lse = INFINITY, drow = 0.f;
   int j_min = 0, j_max = -1;         // keys allowed for this lane's row
   // dP^T chains start from -D instead of zero, so the accumulator ends as
-  // dP - D and dS = P (dP - D) is one multiply (with dropout, dS = P (Z dP / kp
-  // - D) needs dP alone: the chains start from zero)
+  // dP - D and dS = P (dP - D) is one multiply.  With dropout (keep bit Z,
+  // probability kp) the chains start from -D kp and P is formed as P / kp:
+  // dS = P (Z dP / kp - D) = (P / kp) (Z ? dP - D kp : -D kp), a select and
+  // one multiply.
   floatx16 ndrow;
   floatx16 acc[NDB];  // dQ^T: rows = head dim 32 db + c_row(r, h), column = this lane's row
 
@@ -227,14 +231,18 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_dq_kernel(BwdArgs a) {
     if (row_ok) {
       drow = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
       lse = (ssm > 0.f && smx > -INFINITY) ? smx * 1.4426950408889634f + log2f(ssm) : INFINITY;
+      if constexpr (kDrop) {
+        drow *= 1.f / a.drop.rkp;
+        lse += a.drop.log2kp;
+      }
       if (h == 0) {
         const int64_t at = (int64_t)u.head * a.t_q + u.q_base + qrow;
-        a.drow[at] = -drow;  // the dK/dV kernel starts its dP chains from -D
+        a.drow[at] = -drow;  // the dK/dV kernel starts its dP chains from it
         a.lse2[at] = lse;
       }
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) ndrow[r] = kDrop ? 0.f : -drow;
+    for (int r = 0; r < 16; ++r) ndrow[r] = -drow;
     j_min = 0;
     j_max = u.skv - 1;
     if (a.mode != 0) {  // 64-bit: pre / next may be near the int range
@@ -294,7 +302,7 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_dq_kernel(BwdArgs a) {
         if constexpr (i % 2 == 0)
           s[jb] = M::mma(x, qf[t], t == 0 ? floatx16{} : s[jb]);
         else
-          dp[jb] = M::mma(x, yf[t], t == 0 ? ndrow : dp[jb]);  // ndrow: -D (no dropout) or 0
+          dp[jb] = M::mma(x, yf[t], t == 0 ? ndrow : dp[jb]);  // ndrow: -D (with dropout -D kp)
       } else {
         constexpr int j = i - G_Q0, jb = j / NQ, t2 = (j % NQ) / NDB, db = j % NDB;
         acc[db] = M::mma(x, sk[jb][t2], acc[db]);
@@ -314,8 +322,12 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_dq_kernel(BwdArgs a) {
     };
     auto soft_b = [&](int jb, int r) {
       if constexpr (kDrop) {
-        const bool kept = (keep[jb] >> (8 * (r >> 2) + (r & 3))) & 1u;
-        dp[jb][r] = s[jb][r] * ((kept ? dp[jb][r] * a.drop.rkp : 0.f) - drow);
+        // keep bit as a mask (signed one-bit field extract: 0 or all ones),
+        // then (P / kp) (Z ? dP - D kp : -D kp)
+        uint32_t m, sel;
+        asm("v_bfe_i32 %0, %1, %2, 1" : "=v"(m) : "v"(keep[jb]), "n"(8 * (r >> 2) + (r & 3)));
+        asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(sel) : "v"(m), "v"(dp[jb][r]), "v"(-drow));
+        dp[jb][r] = s[jb][r] * __uint_as_float(sel);
       } else {
         dp[jb][r] = s[jb][r] * dp[jb][r];
       }

@@ -227,12 +227,17 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
     if constexpr (kMask) rg = lane_range(i_min - tile * BM - 4 * h, i_max - tile * BM - 4 * h, BM);
     op_t ring[RING];
     floatx16 s[2], dp[2];
-    floatx4 lv[2][4], dv4[2][4];  // lse2 and -D of 4 rows (dv4: dropout only)
-    floatx16 nd[2];  // -D of the rows of accumulator registers 0..15 of block qb
-    // Without dropout (and with one query head per workgroup: the grouped
-    // build keeps its accumulators apart) the dP chain starts from -D, so
-    // that the accumulator ends as dP - D and dS = P (dP - D) is one multiply
-    constexpr bool kNegD = !kDrop && !kGroups;
+    // lse2 and the stored row term -D of 4 rows (with dropout lse2 + log2(kp)
+    // and -D kp, so that exp2(s c - lse2) = P / kp); dv4 is loaded when the
+    // softmax needs it (grouped heads, dropout)
+    floatx4 lv[2][4], dv4[2][4];
+    floatx16 nd[2];  // the row term of the rows of accumulator registers 0..15 of block qb
+    // With one query head per workgroup (the grouped build keeps its
+    // accumulators apart) the dP chain starts from the row term, so that the
+    // accumulator ends as dP - D (dropout: dP - D kp) and dS = P (dP - D) is
+    // one multiply; with dropout dS = P (Z dP / kp - D) = (P / kp) (Z ? dP - D kp
+    // : -D kp), a select and one multiply, and dV takes P Z / kp.
+    constexpr bool kNegD = !kGroups;
     uint32_t mk[2][4][4];  // keep words of rows 32 qb + 8 g + 4 h + e (this wave's keys)
     op_t pk[2][2], sk[2][2];
 
@@ -282,10 +287,18 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
     };
     auto soft_b = [&](int qb, int r) {
       if constexpr (kDrop) {
-        // dV takes P Z / kp, dS = P (Z dP / kp - D)
-        const bool kept = (mk[qb][r >> 2][r & 3] >> c) & 1u;
-        dp[qb][r] = s[qb][r] * ((kept ? dp[qb][r] * a.drop.rkp : 0.f) + dv4[qb][r >> 2][r & 3]);
-        s[qb][r] = kept ? s[qb][r] * a.drop.rkp : 0.f;
+        // keep bit of (row, this lane's key) as a mask: 0 or all ones
+        uint32_t m;
+        asm("v_bfe_i32 %0, %1, %2, 1" : "=v"(m) : "v"(mk[qb][r >> 2][r & 3]), "v"(c));
+        const float nd4 = dv4[qb][r >> 2][r & 3];  // -D kp
+        if constexpr (kNegD) {  // the accumulator holds dP - D kp
+          uint32_t sel;
+          asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(sel) : "v"(m), "v"(dp[qb][r]), "v"(nd4));
+          dp[qb][r] = s[qb][r] * __uint_as_float(sel);
+        } else {
+          dp[qb][r] = s[qb][r] * (__uint_as_float(__float_as_uint(dp[qb][r]) & m) + nd4);
+        }
+        s[qb][r] = __uint_as_float(__float_as_uint(s[qb][r]) & m);
       } else if constexpr (kNegD) {
         dp[qb][r] = s[qb][r] * dp[qb][r];
       } else {
@@ -309,7 +322,7 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
           if (m == kv_soft_slot(qb, 4 * g) - 2) {
             const int off = olr + (32 * qb + 8 * g) * 4;
             lv[qb][g] = *reinterpret_cast<const floatx4*>(reinterpret_cast<const char*>(lse_s) + off);
-            if constexpr (!kNegD)
+            if constexpr (!kNegD || kDrop)
               dv4[qb][g] = *reinterpret_cast<const floatx4*>(reinterpret_cast<const char*>(drow_s) + off);
             if constexpr (kDrop) {
               typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));

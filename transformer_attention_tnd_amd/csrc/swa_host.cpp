@@ -748,7 +748,8 @@ int timed_launch(int kind, void* stream, F&& fn) {
 // Kernel operands of the dropout mask (words null: no dropout).
 DropArgs drop_args(const Problem& p) {
   DropArgs d{static_cast<const uint32_t*>(p.drop_mask),
-             static_cast<int64_t>(p.drop_mask_bytes / 4), static_cast<float>(1.0 / p.keep_prob)};
+             static_cast<int64_t>(p.drop_mask_bytes / 4), static_cast<float>(1.0 / p.keep_prob),
+             static_cast<float>(std::log2(p.keep_prob))};
   return d;
 }
 

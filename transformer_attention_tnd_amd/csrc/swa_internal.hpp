@@ -72,11 +72,12 @@ inline int32_t work_code(int64_t item, int64_t head) {
 }
 
 // Dropout operands of the kernels: the packed keep bits as 32-bit words
-// (null: no dropout), their count, and 1 / keep_prob.
+// (null: no dropout), their count, 1 / keep_prob and log2(keep_prob).
 struct DropArgs {
   const uint32_t* words;
   int64_t n_words;
   float rkp;
+  float log2kp;
 };
 
 // Kernel arguments.  Element pointers are typeless; the kernels cast.
@@ -119,8 +120,10 @@ struct BwdArgs {
   const void* v;
   const void* dy;
   float* drow;        // [N, t_q]: D = rowsum(dY o O) (fp32: from the preprocess
-                      // kernel); -D (bf16: written by the dQ kernel, read by the dK/dV kernel)
-  float* lse2;        // [N, t_q]: softmax_max log2(e) + log2(softmax_sum)
+                      // kernel); -D, with dropout -D keep_prob (bf16: written by the dQ
+                      // kernel, read by the dK/dV kernel)
+  float* lse2;        // [N, t_q]: softmax_max log2(e) + log2(softmax_sum) (bf16 with
+                      // dropout: + log2(keep_prob), so that exp2(s c - lse2) = P / keep_prob)
   // bf16 two-pass: the dQ kernel (launched first) computes D and lse2 of its
   // rows from out and the statistics and stores them for the dK/dV kernel
   const void* out;    // [t_q, N, D]
