@@ -20,7 +20,9 @@ SOURCES = {
     # matrix-core results in ordinary vector registers: the softmax of the
     # bf16 backward kernels then reads them without accumulator-register copies
     "swa_bwd_kv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
-    "swa_bwd_kv_gqa.hip": [],
+    "swa_bwd_kv_gqa.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    # (the grouped build with dropout spills with that register form)
+    "swa_bwd_kv_gqa_drop.hip": [],
     "swa_bwd_dq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "swa_noalloc.hip": [],
 }

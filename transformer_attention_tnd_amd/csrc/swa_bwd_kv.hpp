@@ -232,12 +232,13 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
     // softmax needs it (grouped heads, dropout)
     floatx4 lv[2][4], dv4[2][4];
     floatx16 nd[2];  // the row term of the rows of accumulator registers 0..15 of block qb
-    // With one query head per workgroup (the grouped build keeps its
-    // accumulators apart) the dP chain starts from the row term, so that the
-    // accumulator ends as dP - D (dropout: dP - D kp) and dS = P (dP - D) is
-    // one multiply; with dropout dS = P (Z dP / kp - D) = (P / kp) (Z ? dP - D kp
-    // : -D kp), a select and one multiply, and dV takes P Z / kp.
-    constexpr bool kNegD = !kGroups;
+    // The dP chain starts from the row term, so that the accumulator ends as
+    // dP - D (dropout: dP - D kp) and dS = P (dP - D) is one multiply; with
+    // dropout dS = P (Z dP / kp - D) = (P / kp) (Z ? dP - D kp : -D kp), a
+    // select and one multiply, and dV takes P Z / kp.  Not in the grouped
+    // build with dropout, compiled with the default register assignment,
+    // where the chain start costs accumulator-register copies.
+    constexpr bool kNegD = !kGroups || !kDrop;
     uint32_t mk[2][4][4];  // keep words of rows 32 qb + 8 g + 4 h + e (this wave's keys)
     op_t pk[2][2], sk[2][2];
 

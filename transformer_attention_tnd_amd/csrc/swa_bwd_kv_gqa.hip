@@ -1,6 +1,8 @@
 // Launch of the bf16 dK/dV kernel for grouped key/value heads (each
-// workgroup runs the query heads of its group one after another).  Compiled
-// with the default register assignment.
+// workgroup runs the query heads of its group one after another).  Compiled,
+// like swa_bwd_kv.hip, with the matrix-core results in ordinary vector
+// registers; the instantiation with dropout is in swa_bwd_kv_gqa_drop.hip
+// (with that register form it spills).
 
 #include "swa_bwd_kv.hpp"
 
@@ -19,7 +21,7 @@ static int launch_bwd_kv_grouped_t(const BwdArgs& a, int head_dim, void* stream)
 }
 
 int launch_bwd_kv_grouped(const BwdArgs& a, int head_dim, void* stream) {
-  return a.drop.words ? launch_bwd_kv_grouped_t<true>(a, head_dim, stream)
+  return a.drop.words ? launch_bwd_kv_grouped_drop(a, head_dim, stream)
                       : launch_bwd_kv_grouped_t<false>(a, head_dim, stream);
 }
 

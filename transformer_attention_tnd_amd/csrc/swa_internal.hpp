@@ -170,6 +170,7 @@ int launch_backward(const BwdArgs& a, int dtype, int head_dim, void* stream);
 // grouped key/value heads go to launch_bwd_kv_grouped
 int launch_bwd_kv(const BwdArgs& a, int head_dim, void* stream);
 int launch_bwd_kv_grouped(const BwdArgs& a, int head_dim, void* stream);
+int launch_bwd_kv_grouped_drop(const BwdArgs& a, int head_dim, void* stream);
 // bf16 only: the dQ kernel over the dQ schedule (writes dq)
 int launch_bwd_dq(const BwdArgs& a, int head_dim, void* stream);
 // fp32 only: the dQ kernel over the dQ schedule (writes dq; reads the D and
