@@ -188,22 +188,69 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
   // zero: the tiles that hold such rows are masked tiles, where their P is
   // zero whatever lse2 holds), waited for with the tile copies; with dropout
   // the keep bits of the rows go through registers (store_rows)
-  auto load_rows = [&](int tile, int b) {
+  // (of a unit with query length sq, key length skv, key block kb, whose
+  // head's lse2 / -D rows start at lse_b / drow_b and keep bits at dh)
+  auto load_rows_of = [&](const float* lse_b, const float* drow_b, int sq, int skv, int kb,
+                          int64_t dh, int tile, int b) {
     if (w < 2) {
-      const int nv = it.sq - tile * BM;
+      const int nv = sq - tile * BM;
       const uint32_t nrec = nv <= 0 ? 0u : (uint32_t)(nv < BM ? nv : BM) * 4u;
-      const float* src = (w == 0 ? lse_g : drow_g) + (int64_t)tile * BM;
+      const float* src = (w == 0 ? lse_b : drow_b) + (int64_t)tile * BM;
       const uint32_t dst = lds_addr(w == 0 ? (const void*)lse_s[b] : (const void*)drow_s[b]);
       dma4(buffer_rsrc(src, nrec), (uint32_t)lane * 4u, __builtin_amdgcn_readfirstlane(dst));
     }
     if constexpr (kDrop) {
       const int row = tid & (BM - 1), i = tile * BM + row;
-      const int64_t bit = drop_head + (int64_t)i * it.skv + it.block * BN + 32 * (tid / BM);
+      const int64_t bit = dh + (int64_t)i * skv + kb * BN + 32 * (tid / BM);
       const int64_t wd = bit >> 5;
       msh = (uint32_t)(bit & 31);
-      mreg[0] = (i < it.sq && wd < a.drop.n_words) ? a.drop.words[wd] : 0u;
-      mreg[1] = (i < it.sq && wd + 1 < a.drop.n_words) ? a.drop.words[wd + 1] : 0u;
+      mreg[0] = (i < sq && wd < a.drop.n_words) ? a.drop.words[wd] : 0u;
+      mreg[1] = (i < sq && wd + 1 < a.drop.n_words) ? a.drop.words[wd + 1] : 0u;
     }
+  };
+  auto load_rows = [&](int tile, int b) {
+    load_rows_of(lse_g, drow_g, it.sq, it.skv, it.block, drop_head, tile, b);
+  };
+  // The next unit, prefetched by the pipeline of this unit's last tile (when
+  // that tile is masked): its first query tile and rows into the free slab,
+  // and its K / V rows into the epilogue area (read into registers at the
+  // switch, before this unit's dK / dV pass through that area).
+  using KvDma = TileDma<bf16, D, BN>;
+  KvDma kv_st;     // K rows of the next unit (lane offsets, destination)
+  u32x4 kv_v_rsrc;  // its V rows (same offsets, 32 rows x RB further on)
+  struct Next {
+    const float* lse_b;
+    const float* drow_b;
+    int sq, skv, block, lo;
+    int64_t dh;
+  } nx;
+  auto prefetch_select = [&](const UnitInfo& n, int b) {
+    const int hq = n.head * G;
+    const int nlo = n.tiles0 & 0xffff, nhi = (n.tiles0 >> 16) & 0xffff;
+    const bf16* q0 = static_cast<const bf16*>(a.q) + (int64_t)n.q_base * ld + hq * D;
+    const bf16* y0 = static_cast<const bf16*>(a.dy) + (int64_t)n.q_base * ld + hq * D;
+    const int nvalid = nlo <= nhi ? n.sq - nlo * BM : 0;
+    char* slab = lds + b * SLAB;
+    cp_q.init(q0 + (int64_t)nlo * BM * ld, ld, nvalid, slab, tid);
+    cp_dy.init(y0 + (int64_t)nlo * BM * ld, ld, nvalid, slab + QTB, tid);
+    nx.lse_b = a.lse2 + (int64_t)hq * a.t_q + n.q_base;
+    nx.drow_b = a.drow + (int64_t)hq * a.t_q + n.q_base;
+    nx.sq = n.sq;
+    nx.skv = n.skv;
+    nx.block = n.block;
+    nx.lo = nlo;
+    nx.dh = n.drop_base + (int64_t)hq * n.sq * n.skv;
+    const int64_t ko = ((int64_t)n.kv_base + n.block * BN) * ldkv + n.head * D;
+    kv_st.init(static_cast<const bf16*>(a.k) + ko, ldkv, n.skv - n.block * BN, epi, tid);
+    kv_v_rsrc = buffer_rsrc(static_cast<const bf16*>(a.v) + ko, kv_st.rsrc[2]);
+  };
+  auto kv_stage_issue = [&](auto pc) {
+    constexpr int pt = decltype(pc)::value;  // K parts, then V parts
+    if constexpr (pt < KvDma::PARTS)
+      kv_st.template issue<pt>();
+    else
+      dma16(kv_v_rsrc, kv_st.voff + (pt - KvDma::PARTS) * kv_st.vstep,
+            kv_st.dst + BN * RB + (pt - KvDma::PARTS) * 256 * 16);
   };
   auto copy_all = [&]() {
     static_for<Dma::PARTS>([&](auto pc) {
@@ -220,8 +267,10 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
 
   // One query tile: S, dP, P, dS, dV^T += dY^T P, dK^T += Q^T dS.
   // One query tile (slab b): also issues the copies of tile + 1 into slab b ^ 1
-  auto step = [&](auto mask_tag, int tile, int b) {
+  auto step = [&](auto mask_tag, int tile, int b, auto next_tag) __attribute__((always_inline)) {
     constexpr bool kMask = decltype(mask_tag)::value;
+    // kNext: the last tile of the unit, which prefetches the next one
+    constexpr bool kNext = decltype(next_tag)::value;
     // row 32 qb + 8 g + 4 h + e is allowed iff 32 qb + 8 g + e lies in the lane's range rg
     LaneRange rg{0, 0u};
     if constexpr (kMask) rg = lane_range(i_min - tile * BM - 4 * h, i_max - tile * BM - 4 * h, BM);
@@ -345,11 +394,20 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
       }
     };
 
-    start_copy(tile + 1, b ^ 1);
+    if constexpr (!kNext) start_copy(tile + 1, b ^ 1);
     static_assert(COPY_EVERY * (2 * Dma::PARTS - 1) + 1 < NOPS + AHEAD, "every copy has a slot");
+    static_assert(COPY_EVERY * (2 * KvDma::PARTS - 1) + 3 < NOPS + AHEAD, "every K / V copy has a slot");
     static_for<NOPS + AHEAD>([&](auto sc) {
       constexpr int sl = decltype(sc)::value;
-      if constexpr (sl == 0) load_rows(tile + 1, b ^ 1);
+      if constexpr (sl == 0) {
+        if constexpr (kNext)
+          load_rows_of(nx.lse_b, nx.drow_b, nx.sq, nx.skv, nx.block, nx.dh, nx.lo, b ^ 1);
+        else
+          load_rows(tile + 1, b ^ 1);
+      }
+      // the next unit's K / V rows, one copy every COPY_EVERY slots from slot 3
+      if constexpr (kNext && sl % COPY_EVERY == 3 && sl / COPY_EVERY < 2 * KvDma::PARTS)
+        kv_stage_issue(std::integral_constant<int, sl / COPY_EVERY>{});
       // -D of block qb's rows, three slots before its first dP product
       // (product NS qb + 1, issued at slot NS qb + 1 + AHEAD)
       if constexpr (kNegD && (sl == AHEAD - 2 || sl == NS + AHEAD - 2)) {
@@ -399,24 +457,25 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
       asm volatile("" : "+v"(omk));
     }
   };
+  int cur = 0;  // slab of the current tile; a head or unit starts where the last one ended
   // tiles [from, to] in order, each body branch-free (masked or not)
-  auto run = [&](auto mask_tag, int from, int to) {
+  auto run = [&](auto mask_tag, int from, int to) __attribute__((always_inline)) {
     for (int tile = from; tile <= to; ++tile) {
-      const int b = (tile - lo) & 1;
-      step(mask_tag, tile, b);
-      if (tile < hi) store_rows(b ^ 1);
+      step(mask_tag, tile, cur, std::false_type{});
+      if (tile < hi) store_rows(cur ^ 1);
       wait_vmem();
       __syncthreads();
-      flip(b);
+      flip(cur);
+      cur ^= 1;
     }
   };
-  // the first query tile of head hq of the current unit into slab 0, with
+  // the first query tile of head hq of the current unit into slab cur, with
   // its lse2 / -D rows (and keep bits); waited for by the caller
   auto copy_first = [&]() {
     if (lo <= hi) {
-      start_copy(lo, 0);
+      start_copy(lo, cur);
       copy_all();
-      load_rows(lo, 0);
+      load_rows(lo, cur);
     }
   };
   // the K / V row loads are complete (the caller waited): an empty use of
@@ -434,6 +493,8 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
   uint32_t iv_cur = load_unit(a.items, __builtin_amdgcn_readfirstlane(load_code(work, 0)), lane);
   uint32_t iv_n1 = 0u;
   if (n_units > 1) iv_n1 = load_unit(a.items, __builtin_amdgcn_readfirstlane(load_code(work, 1)), lane);
+  int32_t code_n2 = 0;  // code of the unit after the next (loaded a unit ahead of its item)
+  if (n_units > 2) code_n2 = load_code(work, 2);
   {
     const UnitInfo u0 = unit_info(iv_cur);
     set_unit(u0);
@@ -442,34 +503,49 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
     copy_first();
     wait_vmem();
     settle_kv();
-    if (lo <= hi) store_rows(0);
+    if (lo <= hi) store_rows(cur);
     __syncthreads();
   }
 
   for (int k = 0; k < n_units; ++k) {
     const bool has_nxt = k + 1 < n_units;
-    // the item of unit k + 2 lands during this unit
+    // the item of unit k + 2 and the code of unit k + 3 land during this unit
     uint32_t iv_n2 = 0u;
-    if (k + 2 < n_units)
-      iv_n2 = load_unit(a.items, __builtin_amdgcn_readfirstlane(load_code(work, k + 2)), lane);
+    int32_t code_n3 = 0;
+    if (k + 2 < n_units) iv_n2 = load_unit(a.items, __builtin_amdgcn_readfirstlane(code_n2), lane);
+    if (k + 3 < n_units) code_n3 = load_code(work, k + 3);
     key_range();
+    bool pre = false;  // the last tile prefetched the next unit
     for (int gi = 0; gi < G; ++gi) {
       if (gi > 0) {  // the next query head of the group: its first tile
         set_head(kvh * G + gi);
         copy_first();
         wait_vmem();
-        if (lo <= hi) store_rows(0);
+        if (lo <= hi) store_rows(cur);
         __syncthreads();
       }
+      // the unit's last tile, when masked, prefetches the next unit (not
+      // with dropout, whose extra state leaves no registers for it)
+      const bool last_masked = !(flo <= fhi && fhi >= hi);
+      pre = !kDrop && has_nxt && gi == G - 1 && lo <= hi && last_masked;
+      const int last = pre ? hi - 1 : hi;
       if (flo <= fhi) {  // masked tiles before and after the mask-free range
         run(std::true_type{}, lo, flo - 1);
-        run(std::false_type{}, flo, fhi);
-        run(std::true_type{}, fhi + 1, hi);
+        run(std::false_type{}, flo, fhi < last ? fhi : last);
+        run(std::true_type{}, fhi + 1, last);
       } else {
-        run(std::true_type{}, lo, hi);
+        run(std::true_type{}, lo, last);
       }
-      // the next head (or unit) starts on slab 0 again
-      if (lo <= hi && ((hi - lo + 1) & 1)) flip(1);
+      if constexpr (!kDrop) {
+        if (pre) {
+          prefetch_select(unit_info(iv_n1), cur ^ 1);
+          step(std::true_type{}, hi, cur, std::true_type{});
+          wait_vmem();
+          __syncthreads();
+          flip(cur);
+          cur ^= 1;
+        }
+      }
     }
 
     // Switch: the next unit's K / V rows (the registers of this unit's are
@@ -482,22 +558,36 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_kv_kernel(BwdArgs a) {
     const int nrows = it.skv - row0;
     if (has_nxt) {
       const UnitInfo n = unit_info(iv_n1);
-      load_kv_rows(n);
+      if (!kDrop && pre) {
+        // K / V rows from the epilogue area: each wave reads its own 32 keys'
+        // rows, which are exactly the slices its dK / dV take next (LDS
+        // operations of one wave stay in order, so no barrier is needed)
+        const int r = 32 * w + c;
+#pragma unroll
+        for (int t = 0; t < DSTEPS; ++t) {
+          const int off = tile_off<RB>(r, (16 * t + 8 * h) * 2);
+          kr[t] = *reinterpret_cast<const op_t*>(epi + off);
+          vr[t] = *reinterpret_cast<const op_t*>(epi + BN * RB + off);
+        }
+      } else {
+        load_kv_rows(n);
+      }
       set_unit(n);
       set_head(kvh * G);
-      copy_first();
+      if (!pre) copy_first();
     }
-    static_assert(EPI >= 2 * 4 * 32 * RB, "the epilogue slices fit");
+    static_assert(EPI >= 2 * 4 * 32 * RB && EPI >= 2 * BN * RB, "the epilogue slices fit");
     store_rows_via_lds<NDB>(dk, a.scale, epi + w * 32 * RB, dk_dst, ldkv, nrows);
     store_rows_via_lds<NDB>(dv, 1.f, epi + (4 + w) * 32 * RB, dv_dst, ldkv, nrows);
-    if (has_nxt) {
+    if (has_nxt && !pre) {
       wait_vmem();
       settle_kv();
-      if (lo <= hi) store_rows(0);
+      if (lo <= hi) store_rows(cur);
       __syncthreads();
     }
     iv_cur = iv_n1;
     iv_n1 = iv_n2;
+    code_n2 = code_n3;
   }
   (void)iv_cur;
 }

@@ -332,12 +332,24 @@ __device__ __attribute__((always_inline)) inline void store_rows_via_lds(const f
   }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave reads what its other lanes wrote
   constexpr int CPR = RB / 16, RPI = 64 / CPR;           // 16-byte chunks per row, rows per instruction
+  constexpr int NI = 32 / RPI;                           // store instructions
   const int ch = ln % CPR, rr = ln / CPR;
+  // the rows of a batch are all read before its stores: read inside each
+  // row's store condition, each read would be waited for on its own
+  constexpr int NB = NI >= 4 ? 4 : NI;  // rows per batch (registers permitting)
 #pragma unroll
-  for (int i = 0; i < 32 / RPI; ++i) {
-    const int r = RPI * i + rr;
-    const u32x4 val = *reinterpret_cast<const u32x4*>(st + tile_off<RB>(r, 16 * ch));
-    if (r < nrows) *reinterpret_cast<u32x4*>(dst + (int64_t)r * ld + 8 * ch) = val;
+  for (int i0 = 0; i0 < NI; i0 += NB) {
+    u32x4 val[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+      val[i] = *reinterpret_cast<const u32x4*>(st + tile_off<RB>(RPI * (i0 + i) + rr, 16 * ch));
+#pragma unroll
+    for (int i = 0; i < NB; ++i) asm volatile("" : "+v"(val[i]));
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int r = RPI * (i0 + i) + rr;
+      if (r < nrows) *reinterpret_cast<u32x4*>(dst + (int64_t)r * ld + 8 * ch) = val[i];
+    }
   }
   asm volatile("" ::: "memory");  // the reads stay ahead of any later write to st
 }
