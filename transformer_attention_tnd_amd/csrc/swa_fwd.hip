@@ -200,8 +200,33 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int t = 0; t < QSTEPS; ++t) asm volatile("" : : "v"(qf[t]));
   };
+  // Units' codes and items pass through LDS (bf16 with a positive scale; the
+  // other kernels, short of registers, load them where needed): slot u & 1 holds the item of
+  // unit u (words 0-15) and the codes of units u .. u + 3 (words 16-19, zero
+  // past the list).  During unit u, lanes 0-3 of wave 0 copy those of unit
+  // u + 1 into the other slot (copies waited for with the tile copies), so
+  // that neither a unit's start nor its switch waits for a load.
+  constexpr bool kSlots = sizeof(T) == 2 && kPos;
+  __shared__ __attribute__((aligned(16))) int32_t unit_lds[2][20];
+  auto fetch_unit = [&](int u, int32_t code) {  // unit u's item and codes into slot u & 1
+    if (kSlots && threadIdx.x < 64) {
+      span_load_lds(a.items + (code & 0xffff), (uint32_t)sizeof(Item), 64,
+                    reinterpret_cast<char*>(unit_lds[u & 1]), threadIdx.x);
+      span_load_lds(work + u, (uint32_t)(n_units - u) * 4u, 16,
+                    reinterpret_cast<char*>(unit_lds[u & 1] + 16), threadIdx.x);
+    }
+  };
+  auto slot_word = [&](int u, int i) { return __builtin_amdgcn_readfirstlane(unit_lds[u & 1][i]); };
+  auto slot_item = [&](int u) {
+    Item r;
+    int32_t* d = reinterpret_cast<int32_t*>(&r);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) d[i] = slot_word(u, i);
+    return r;
+  };
   {
     const int32_t code0 = work[0];
+    fetch_unit(0, code0);
     unit_prologue(a.items[code0 & 0xffff], code0 >> 16);
     wait_vmem();
     settle_q();
@@ -216,9 +241,11 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
   asm volatile("" : "+v"(tid_u));
   const int tid = tid_u;
   const int lane = tid & 63, w = tid >> 6, g = w >> 2, h = lane >> 5, c = lane & 31;
-  const int32_t code = work[ku];
+  const int w_u = w, h_u = h, c_u = c;
+  const int32_t code = kSlots ? slot_word(ku, 16) : work[ku];
   const int head = code >> 16;
-  const Item it = a.items[code & 0xffff];
+  const Item it = kSlots ? slot_item(ku) : a.items[code & 0xffff];
+  if (kSlots && ku + 1 < n_units) fetch_unit(ku + 1, slot_word(ku, 17));
   const int kvh = head / (a.num_heads / a.num_kv_heads);  // grouped heads share K / V
   const T* qg = static_cast<const T*>(a.q) + (int64_t)it.q_base * ld + head * D;
   const T* kg = static_cast<const T*>(a.k) + (int64_t)it.kv_base * ldkv + kvh * D;
@@ -657,18 +684,36 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
   }
 
   // the next unit's Q rows and first tiles go out first (bf16 without
-  // dropout) or after this unit's rows have left the K / V area
+  // dropout) or after this unit's rows have left the K / V area; its slot
+  // has landed (the tile loop ended with a wait and a barrier; a unit
+  // without tiles waits here)
   const bool has_next = ku + 1 < n_units;
+  if (kSlots && lo > hi) {
+    wait_vmem();
+    __syncthreads();
+  }
   Item nit;
   int nhead = 0;
   if (has_next) {
-    const int32_t ncode = work[ku + 1];
+    const int32_t ncode = kSlots ? slot_word(ku + 1, 16) : work[ku + 1];
     nhead = ncode >> 16;
-    nit = a.items[ncode & 0xffff];
+    nit = kSlots ? slot_item(ku + 1) : a.items[ncode & 0xffff];
     if constexpr (kOverlap) unit_prologue(nit, nhead);
+    // (measured: waiting for these loads before the epilogue's stores is
+    // faster than letting the two overlap)
+    if constexpr (kSlots) wait_vmem();
   }
 
-  // epilogue: normalise, store out and the statistics of this lane's row
+  // epilogue: normalise, store out and the statistics of this lane's row.
+  // (kSlots: its lane indices are formed again here; held from the unit's
+  // start they may come back from scratch, and such reloads would wait
+  // behind the next unit's row loads and tile copies issued above.)
+  {
+  int tid_e = threadIdx.x;
+  if constexpr (kSlots) asm volatile("" : "+v"(tid_e));
+  const int w = kSlots ? __builtin_amdgcn_readfirstlane(tid_e >> 6) : w_u;
+  const int h = kSlots ? (tid_e & 63) >> 5 : h_u, c = kSlots ? tid_e & 31 : c_u;
+  const int qrow = it.block * 2 * HALF + HALF * (w >> 2) + 32 * (w & 3) + c;  // sequence-local
   const float l_ref = pair_sum(l_run);
   // (dropout: times 1 / keep_prob, the factor of every kept term)
   const float inv = l_ref > 0.f ? (kDrop ? a.drop.rkp : 1.f) / l_ref : 0.f;
@@ -709,6 +754,7 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
     const int64_t so = (tok * a.num_heads + head) * 8 + 4 * h;
     *reinterpret_cast<floatx4*>(a.smax + so) = mv;
     *reinterpret_cast<floatx4*>(a.ssum + so) = sv;
+  }
   }
   if (has_next) {
     if constexpr (!kOverlap) {
