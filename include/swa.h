@@ -240,10 +240,12 @@ swa_status swa_debug_tile_schedule(const int64_t* cu_seqlens_q, const int64_t* c
  * cumulative lengths and every size and mask argument; a call on a cached
  * problem neither rebuilds nor uploads its schedule.  An entry is written
  * once, by a synchronous copy, before any kernel reads it; evicting one waits
- * until its device is idle.  Enabled by default; enable = 0 frees every
- * entry (waiting for the devices to be idle) and makes calls upload their
- * schedule into the caller's workspace instead, as swa_backward_noalloc
- * always does into its scratch. */
+ * until its device is idle.  Host threads may call at once: an entry that a
+ * call is using is evicted only after that call has enqueued its kernels.
+ * Enabled by default; enable = 0 frees every entry (waiting for the devices
+ * to be idle; an entry in use by a call on another thread is freed when that
+ * call returns) and makes calls upload their schedule into the caller's
+ * workspace instead, as swa_backward_noalloc always does into its scratch. */
 swa_status swa_schedule_cache_enable(int32_t enable);
 
 /* Kernel timing (instrumentation for benchmarks).  While enabled, every

@@ -337,6 +337,92 @@ def test_schedule_cache_on_and_off_agree(dev):
             assert torch.equal(r[n], off[i % 2][n]), (i, n)
 
 
+def test_concurrent_threads_and_streams(dev):
+    """Host threads calling at once, each on a stream of its own (shared
+    schedule cache entries, the pinned staging ring, per-thread error text),
+    get the bits of the same calls made one at a time."""
+    import threading
+    probs = [workloads.make_custom([700, 1500, 300], num_heads=4, head_dim=128, sparse_mode=4,
+                                   pre_tokens=300, next_tokens=40),
+             workloads.make_custom([333, 129], num_heads=2, head_dim=64, sparse_mode=2,
+                                   lengths_kv=[400, 129]),
+             workloads.make_custom([520, 77], num_heads=2, head_dim=128, dtype=torch.float32)]
+    ref = [run_hip(p, dev) for p in probs]
+    n_threads, reps = 6, 3
+    got = [[None] * reps for _ in range(n_threads)]
+    errors = []
+    bad = probs[0]
+
+    def work(i):
+        try:
+            stream = torch.cuda.Stream(device=dev)
+            with torch.cuda.stream(stream):
+                for r in range(reps):
+                    if i % 2 == 0:  # a rejected call between the good ones: its own error text
+                        q = bad.q.to(dev)
+                        try:
+                            swa.forward(q, q, q, bad.cu_seqlens_q, bad.cu_seqlens_kv, bad.scale,
+                                        bad.pre_tokens, bad.next_tokens, 1)
+                            errors.append((i, "sparse_mode 1 accepted"))
+                        except ValueError as e:  # (invalid arguments raise ValueError)
+                            if "sparse_mode" not in str(e):
+                                errors.append((i, f"error text of another call: {e}"))
+                    got[i][r] = run_hip(probs[i % len(probs)], dev)
+        except BaseException as e:  # reported by the main thread
+            errors.append((i, repr(e)))
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(n_threads)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in threads), "a worker thread did not finish"
+    assert not errors, errors
+    for i in range(n_threads):
+        for r in range(reps):
+            for n in ("out", "smax", "ssum", "dq", "dk", "dv"):
+                assert torch.equal(got[i][r][n], ref[i % len(probs)][n]), (i, r, n)
+
+
+def test_concurrent_calls_with_cache_eviction(dev):
+    """More distinct problems than the schedule cache holds (64), called from
+    four threads on their own streams: entries are evicted while other calls
+    use theirs, and every result keeps the bits of the uncached call."""
+    import threading
+    probs = [workloads.make_custom([60 + 7 * i, 33], num_heads=2, head_dim=64, sparse_mode=4,
+                                   pre_tokens=40, next_tokens=9) for i in range(72)]
+    try:
+        swa.swa_schedule_cache_enable(False)
+        ref = [run_hip(p, dev) for p in probs]
+    finally:
+        swa.swa_schedule_cache_enable(True)
+    n_threads = 4
+    got = {}
+    errors = []
+
+    def work(i):
+        try:
+            stream = torch.cuda.Stream(device=dev)
+            with torch.cuda.stream(stream):
+                for rep in range(2):
+                    for j in range(i, len(probs), n_threads):
+                        got[(j, rep)] = run_hip(probs[j], dev)
+        except BaseException as e:  # reported by the main thread
+            errors.append((i, repr(e)))
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(n_threads)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in threads), "a worker thread did not finish"
+    assert not errors, errors
+    assert len(got) == 2 * len(probs)
+    for (j, rep), r in got.items():
+        for n in ("out", "smax", "ssum", "dq", "dk", "dv"):
+            assert torch.equal(r[n], ref[j][n]), (j, rep, n)
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_backward_is_deterministic(dev, dtype):
     """The backward uses no atomics: two calls give identical bits."""

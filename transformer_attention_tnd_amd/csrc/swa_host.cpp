@@ -576,6 +576,10 @@ void build_backward_schedule(const Problem& p, const std::vector<Seq>& seqs, int
 // schedule depends on, so that repeated calls on the same problem neither
 // rebuild nor upload it.  An entry is written once, by a synchronous copy,
 // before any kernel reads it, and is freed only after its device is idle.
+// A call pins the entry it uses from the lookup until its kernels are
+// enqueued: another thread frees only unpinned entries (the wait for the
+// device to be idle then covers every kernel already enqueued on it), and an
+// entry dropped while pinned (cache disabled) is freed by its last unpin.
 struct ScheduleCache {
   struct Entry {
     std::vector<int64_t> key;
@@ -584,14 +588,47 @@ struct ScheduleCache {
     size_t bytes;
     SchedLayout layout;
     uint64_t used;
+    uint64_t id;
+    int pins;
+    bool dropped;  // no longer found by lookups; freed at the last unpin
   };
   std::mutex mu;
   std::vector<Entry> entries;
   uint64_t tick = 0;
+  uint64_t next_id = 0;
   size_t total = 0;
   bool enabled = true;
 };
 ScheduleCache g_cache;
+
+// Frees entry i (its device idle first) and removes it; the lock is held.
+int cache_free_entry(size_t i) {
+  ScheduleCache::Entry& en = g_cache.entries[i];
+  const int e = hip_device_free(en.device, en.dev);
+  if (e != 0) return e;
+  g_cache.total -= en.bytes;
+  g_cache.entries.erase(g_cache.entries.begin() + i);
+  return 0;
+}
+
+// The pin of one call on a cache entry (id 0: none), released when the call
+// returns, after its kernels have been enqueued.
+struct SchedulePin {
+  uint64_t id = 0;
+  SchedulePin() = default;
+  SchedulePin(const SchedulePin&) = delete;
+  SchedulePin& operator=(const SchedulePin&) = delete;
+  ~SchedulePin() {
+    if (!id) return;
+    std::lock_guard<std::mutex> lock(g_cache.mu);
+    for (size_t i = 0; i < g_cache.entries.size(); ++i) {
+      ScheduleCache::Entry& en = g_cache.entries[i];
+      if (en.id != id) continue;
+      if (--en.pins == 0 && en.dropped) cache_free_entry(i);  // (a failure leaves it listed)
+      return;
+    }
+  }
+};
 constexpr size_t kCacheEntries = 64;
 constexpr size_t kCacheBytes = size_t(256) << 20;
 
@@ -609,7 +646,8 @@ std::vector<int64_t> schedule_key(int kind, int device, int n_cu, const Problem&
 // failure, or the entry point that allocates nothing) the blob uploaded into
 // `ws` (noalloc_device >= 0: that device's fixed scratch).
 swa_status place_schedule(int kind, const Problem& p, const std::vector<Seq>& seqs, char* ws,
-                          int noalloc_device, void* stream, const char** dev, SchedLayout* L) {
+                          int noalloc_device, void* stream, const char** dev, SchedLayout* L,
+                          SchedulePin* pin) {
   int n_cu = 0, device = 0, e = 0;
   if ((e = hip_cu_count(stream, &n_cu)) != 0) return fail(SWA_ERR_HIP, hip_error_string(e));
   if ((e = hip_stream_device(stream, &device)) != 0) return fail(SWA_ERR_HIP, hip_error_string(e));
@@ -631,8 +669,10 @@ swa_status place_schedule(int kind, const Problem& p, const std::vector<Seq>& se
     if (g_cache.enabled) {
       key = schedule_key(kind, device, n_cu, p);
       for (ScheduleCache::Entry& en : g_cache.entries) {
-        if (en.device == device && en.key == key) {
+        if (!en.dropped && en.device == device && en.key == key) {
           en.used = ++g_cache.tick;
+          ++en.pins;
+          pin->id = en.id;
           *dev = static_cast<const char*>(en.dev);
           *L = en.layout;
           return SWA_OK;
@@ -643,24 +683,25 @@ swa_status place_schedule(int kind, const Problem& p, const std::vector<Seq>& se
   build(blob);
   if (!key.empty() && !blob.empty() && blob.size() <= kCacheBytes / 4) {
     std::lock_guard<std::mutex> lock(g_cache.mu);
-    // make room: least recently used first
-    while (!g_cache.entries.empty() && (g_cache.entries.size() >= kCacheEntries ||
-                                        g_cache.total + blob.size() > kCacheBytes)) {
-      size_t lru = 0;
-      for (size_t i = 1; i < g_cache.entries.size(); ++i)
-        if (g_cache.entries[i].used < g_cache.entries[lru].used) lru = i;
-      ScheduleCache::Entry& en = g_cache.entries[lru];
-      if (hip_device_free(en.device, en.dev) != 0) break;
-      g_cache.total -= en.bytes;
-      g_cache.entries.erase(g_cache.entries.begin() + lru);
+    // make room: least recently used unpinned entry first
+    while (g_cache.enabled && (g_cache.entries.size() >= kCacheEntries ||
+                               g_cache.total + blob.size() > kCacheBytes)) {
+      size_t lru = g_cache.entries.size();
+      for (size_t i = 0; i < g_cache.entries.size(); ++i)
+        if (g_cache.entries[i].pins == 0 &&
+            (lru == g_cache.entries.size() || g_cache.entries[i].used < g_cache.entries[lru].used))
+          lru = i;
+      if (lru == g_cache.entries.size() || cache_free_entry(lru) != 0) break;
     }
     void* d = nullptr;
-    if (g_cache.entries.size() < kCacheEntries && g_cache.total + blob.size() <= kCacheBytes &&
-        hip_device_alloc(device, &d, blob.size()) == 0) {
+    if (g_cache.enabled && g_cache.entries.size() < kCacheEntries &&
+        g_cache.total + blob.size() <= kCacheBytes && hip_device_alloc(device, &d, blob.size()) == 0) {
       if (hip_memcpy_h2d_sync(device, d, blob.data(), blob.size()) == 0) {
-        g_cache.entries.push_back(
-            ScheduleCache::Entry{std::move(key), device, d, blob.size(), *L, ++g_cache.tick});
+        const uint64_t id = ++g_cache.next_id;
+        g_cache.entries.push_back(ScheduleCache::Entry{std::move(key), device, d, blob.size(), *L,
+                                                       ++g_cache.tick, id, 1, false});
         g_cache.total += blob.size();
+        pin->id = id;
         *dev = static_cast<const char*>(d);
         return SWA_OK;
       }
@@ -808,8 +849,9 @@ swa_status swa_forward_ex(const void* q, const void* k, const void* v,
                                        " bytes, needs " + std::to_string(need));
   const char* sched = nullptr;
   SchedLayout SL;
-  if ((s = place_schedule(0, p, seqs, static_cast<char*>(workspace), -1, stream, &sched, &SL)) !=
-      SWA_OK)
+  SchedulePin pin;  // released on return, after the launches
+  if ((s = place_schedule(0, p, seqs, static_cast<char*>(workspace), -1, stream, &sched, &SL,
+                          &pin)) != SWA_OK)
     return s;
   int e = 0;
   if (end_q < t_q) {
@@ -888,7 +930,9 @@ swa_status run_backward(const Problem& p, const std::vector<Seq>& seqs, int64_t 
   const bool bf16 = dtype == SWA_DTYPE_BF16;
   const char* sched = nullptr;
   SchedLayout SL;
-  if ((s = place_schedule(1, p, seqs, ws + L.items, noalloc_device, stream, &sched, &SL)) != SWA_OK)
+  SchedulePin pin;  // released on return, after the launches
+  if ((s = place_schedule(1, p, seqs, ws + L.items, noalloc_device, stream, &sched, &SL, &pin)) !=
+      SWA_OK)
     return s;
   const size_t n_kv_items = static_cast<size_t>(SL.n_items[0]);
   int e = 0;
@@ -1133,16 +1177,18 @@ swa_status swa_debug_tile_schedule(const int64_t* cu_seqlens_q, const int64_t* c
 
 swa_status swa_schedule_cache_enable(int32_t enable) {
   std::lock_guard<std::mutex> lock(g_cache.mu);
+  g_cache.enabled = enable != 0;
   if (!enable) {
-    while (!g_cache.entries.empty()) {
-      ScheduleCache::Entry& en = g_cache.entries.back();
-      const int e = hip_device_free(en.device, en.dev);
+    // entries in use by a call on another thread are dropped now and freed
+    // when that call has enqueued its kernels
+    for (size_t i = g_cache.entries.size(); i-- > 0;) {
+      ScheduleCache::Entry& en = g_cache.entries[i];
+      en.dropped = true;
+      if (en.pins > 0) continue;
+      const int e = cache_free_entry(i);
       if (e != 0) return fail(SWA_ERR_HIP, hip_error_string(e));
-      g_cache.total -= en.bytes;
-      g_cache.entries.pop_back();
     }
   }
-  g_cache.enabled = enable != 0;
   return SWA_OK;
 }
 
