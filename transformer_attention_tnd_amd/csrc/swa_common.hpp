@@ -118,6 +118,14 @@ __device__ inline uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)((const lds_void*)(p));
 }
 
+// The copies below set m0 (the LDS destination of a buffer load into LDS)
+// themselves and list it as clobbered.  The compiler reserves m0 and sets it
+// right before each of its own instructions that read it, so the clobber
+// entry only documents the write; its warning about a reserved register in
+// a clobber list is silenced here.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+
 // 16 bytes per lane from rsrc + voff into LDS at lds_base + 16 * lane.  The
 // copy is issued as inline assembly so that the compiler does not treat it
 // as an LDS store (it would otherwise wait for it before every later LDS
@@ -146,6 +154,8 @@ __device__ inline void dma4(u32x4 rsrc, uint32_t voff, uint32_t lds_base) {
                : "s"(lds_base), "v"(voff), "s"(rsrc)
                : "memory", "m0");
 }
+
+#pragma clang diagnostic pop
 
 // Copy rows [0, ROWS) of a row-major [rows, ld] slice starting at `base`
 // into a swizzled LDS tile (no registers involved).  Rows >= nvalid read as

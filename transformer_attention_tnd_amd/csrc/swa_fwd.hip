@@ -247,7 +247,6 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
   const Item it = kSlots ? slot_item(ku) : a.items[code & 0xffff];
   if (kSlots && ku + 1 < n_units) fetch_unit(ku + 1, slot_word(ku, 17));
   const int kvh = head / (a.num_heads / a.num_kv_heads);  // grouped heads share K / V
-  const T* qg = static_cast<const T*>(a.q) + (int64_t)it.q_base * ld + head * D;
   const T* kg = static_cast<const T*>(a.k) + (int64_t)it.kv_base * ldkv + kvh * D;
   const T* vg = static_cast<const T*>(a.v) + (int64_t)it.kv_base * ldkv + kvh * D;
   const int qrow = it.block * 2 * HALF + HALF * g + 32 * (w & 3) + c;  // sequence-local
