@@ -460,7 +460,7 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
       for (int r = 0; r < 16; ++r) {
         const float p = __builtin_amdgcn_exp2f(fmaf(s[jb][r], cs, moff));
         ls[r & 3] += p;  // the row sum is that of the undropped softmax
-        if constexpr (kDrop) {
+        if constexpr (kDrop && !kDropLds) {
           // the signed one-bit field extract is 0 or all ones: a mask of p
           // (written as asm: the builtin is turned into an and, a compare and
           // a select, one instruction more); the factor 1 / keep_prob of the
@@ -474,6 +474,30 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
       }
 #pragma unroll
       for (int t2 = 0; t2 < PSTEPS; ++t2) pk[jb][t2] = M::pack(s[jb], t2);
+      if constexpr (kDropLds) {
+        // The keep bits mask the rounded probabilities a pair at a time:
+        // dword i of operand t2 holds registers r = 8 t2 + 2 i and r + 1,
+        // whose bits are b = 8 (r / 4) + r % 4 and b + 1, i.e. b0 = 8 (i / 2)
+        // + 2 (i % 2) and b0 + 1 for t2 = 0, and 16 more for t2 = 1.  With
+        // bit b0 shifted to bit 15 of x and bit b0 + 1 to bit 15 of y (so
+        // bits b0 + 16, b0 + 17 sit at bit 31), v_perm_b32's selectors 8 / 10
+        // (9 / 11) copy the sign bit of byte 1 (byte 3) of x / y into a whole
+        // byte: the two 16-bit halves of the mask, for t2 = 0 (t2 = 1).
+        // The factor 1 / keep_prob of the kept terms is applied to the row
+        // at the end.
+        typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+        u32x4_t d0 = __builtin_bit_cast(u32x4_t, pk[jb][0]);
+        u32x4_t d1 = __builtin_bit_cast(u32x4_t, pk[jb][1]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int b0 = 8 * (i >> 1) + 2 * (i & 1);
+          const uint32_t x = keep[jb] << (15 - b0), y = keep[jb] << (14 - b0);
+          d0[i] &= __builtin_amdgcn_perm(y, x, 0x0A0A0808u);
+          d1[i] &= __builtin_amdgcn_perm(y, x, 0x0B0B0909u);
+        }
+        pk[jb][0] = __builtin_bit_cast(op_t, d0);
+        pk[jb][1] = __builtin_bit_cast(op_t, d1);
+      }
     }
     l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
   };
