@@ -512,19 +512,25 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
   constexpr int AHEAD = SWA_FWD_AHEAD, RING = AHEAD + 1;
   // LDS offsets of the operand reads: ok_[t], the 128-bit read of key row c,
   // chunk 2t + h; otr[db], the transposing reads of the V tile, head-dim
-  // block db.  Formed once per unit, except with dropout, whose extra state
-  // leaves no room to hold them across the tile loop: there each matrix
-  // phase forms them again from a lane index behind an empty asm.
+  // block db.  Formed once per unit, except ok_ with dropout, whose extra
+  // state leaves no room to hold all of them across the tile loop: there
+  // each matrix phase forms ok_ again from a lane index behind an empty asm
+  // (measured: holding otr and forming ok_ per phase is the fastest of the
+  // four ways, with no register spilled; holding both spilled 3 registers,
+  // holding ok_ alone 82).
   int ok_[QSTEPS];
   int otr[NDB][2];
-  auto operand_offsets = [&](int ln) __attribute__((always_inline)) {
+  auto operand_offsets = [&](int ln, auto part) __attribute__((always_inline)) {
+    // part: 1 the 128-bit read offsets, 2 the transposing ones, 3 both
+    constexpr int P = decltype(part)::value;
     if constexpr (sizeof(T) == 2) {
       ln &= 63;
       const int cc = ln & 31, hh = ln >> 5;
 #pragma unroll
-      for (int t = 0; t < QSTEPS; ++t) ok_[t] = tile_off<RB>(cc, (KSTEP * t + KPL * hh) * 2);
+      for (int t = 0; t < QSTEPS; ++t)
+        if constexpr ((P & 1) != 0) ok_[t] = tile_off<RB>(cc, (KSTEP * t + KPL * hh) * 2);
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
+      for (int db = 0; db < NDB && (P & 2) != 0; ++db) {
         const int s16 = ln & 15;
         const int col2 = 2 * (32 * db + 16 * ((ln >> 4) & 1) + 4 * (s16 & 3));
         otr[db][0] = tile_off<RB>(4 * hh + (s16 >> 2), col2);
@@ -532,7 +538,10 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
       }
     }
   };
-  if constexpr (!kDropLds) operand_offsets(lane);
+  // offsets formed per matrix phase (1: the 128-bit read offsets; with
+  // dropout) and once per unit (the others)
+  constexpr int kOffPerPhase = kDropLds ? 1 : 0;
+  operand_offsets(lane, std::integral_constant<int, 3 - kOffPerPhase>{});
   // bf16 without dropout: each group copies one tile per step, part by part
   // from the slots of its matrix phase (a burst of copy instructions holds
   // the issuing waves while the address unit drains it): group 0 the K tile
@@ -551,10 +560,10 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_kernel(FwdArgs a) {
     static_assert(!kSpread || COPY_EVERY * (Dma::PARTS - 1) + 1 < LAST - FIRST + AHEAD,
                   "every copy has a slot");
     op_t ring[RING];
-    if constexpr (kDropLds) {
+    if constexpr (kOffPerPhase != 0) {
       int ln = threadIdx.x;
       asm volatile("" : "+v"(ln));
-      operand_offsets(ln);
+      operand_offsets(ln, std::integral_constant<int, kOffPerPhase>{});
     }
     auto read = [&](auto ic) {
       constexpr int i = decltype(ic)::value;
